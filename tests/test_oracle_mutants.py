@@ -1,0 +1,107 @@
+"""CPU mutation check of the oracle's pins.
+
+Each mutant plants one plausible mistake in a copy of the oracle source (a
+dropped rounding, a flushed subnormal, a missing key RMSNorm, a flipped sign,
+a wrong row ...), builds it into a temporary library and runs the pins: at
+least one pin must fail.  This shows the pins would catch that mistake in the
+oracle.  Mistakes are planted only here, on the CPU.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+from oracle import build as obuild
+
+SRC = open(obuild.SOURCE).read()
+
+# name -> (exact text in the oracle source, replacement)
+MUTANTS = {
+    "inner_rounding_dropped": (
+        "        uint16_t t = add2 ? oracle_bf16_add(add[h], add2[h]) : add[h];\n"
+        "        out_prefix[h] = oracle_bf16_add(prefix[h], t);",
+        "        volatile float s3 = bf16_to_f32(prefix[h]) + (bf16_to_f32(add[h]) +\n"
+        "                            (add2 ? bf16_to_f32(add2[h]) : 0.0f));\n"
+        "        out_prefix[h] = oracle_round_bf16((double)s3);"),
+    "addends_reassociated": (
+        "        uint16_t t = add2 ? oracle_bf16_add(add[h], add2[h]) : add[h];\n"
+        "        out_prefix[h] = oracle_bf16_add(prefix[h], t);",
+        "        uint16_t t = oracle_bf16_add(prefix[h], add[h]);\n"
+        "        out_prefix[h] = add2 ? oracle_bf16_add(t, add2[h]) : t;"),
+    "flush_to_zero": (
+        "    volatile float s = bf16_to_f32(a) + bf16_to_f32(b); /* binary32 RN add */",
+        "    volatile float s = bf16_to_f32(a) + bf16_to_f32(b);\n"
+        "    if (fabsf(s) < 0x1p-126f) s = 0.0f;"),
+    "denormals_are_zero": (
+        "static float bf16_to_f32(uint16_t b)\n{\n    uint32_t u = (uint32_t)b << 16;",
+        "static float bf16_to_f32(uint16_t b)\n{\n"
+        "    uint32_t u = (b & 0x7F80u) ? (uint32_t)b << 16 : (uint32_t)(b & 0x8000u) << 16;"),
+    "ties_away_from_zero": (
+        "    double n = nearbyint(a / quantum);",
+        "    double n = round(a / quantum);"),
+    "no_key_rmsnorm": (
+        "        z[s] = rstd * qdot;",
+        "        z[s] = qdot; (void)rstd;"),
+    "key_norm_sum_not_mean": (
+        "        double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n        z[s]",
+        "        double rstd = 1.0 / sqrt(sumsq + eps);\n        z[s]"),
+    "softmax_sign_flipped": (
+        "        z[s] = exp(z[s] - zmax);",
+        "        z[s] = exp(zmax - z[s]);"),
+    "no_max_subtraction": (
+        "        z[s] = exp(z[s] - zmax);",
+        "        z[s] = exp(z[s]); (void)zmax;"),
+    "normalised_values_mixed": (
+        "        z[s] = rstd * qdot;",
+        "        z[s] = rstd * qdot;\n"
+        "        for (int64_t hh = 0; hh < H; ++hh) ((double*)ks)[hh] *= rstd;"),
+    "unrounded_prefix_mixed": (
+        "        k[(int64_t)N * H + h] = oracle_bf16_to_f64(out_prefix[h]);",
+        "    {   uint16_t t2 = add2 ? oracle_bf16_add(add[h], add2[h]) : add[h];\n"
+        "        k[(int64_t)N * H + h] = (double)(bf16_to_f32(prefix[h]) + bf16_to_f32(t2)); }"),
+    "prefix_left_out_of_mix": (
+        "    for (int s = 0; s < S; ++s) {\n        z[s] = z[s] / denom;",
+        "    z[N] = 0.0; denom = 0.0; for (int s = 0; s < N; ++s) denom += z[s];\n"
+        "    if (N == 0) { z[0] = 1.0; denom = 1.0; }\n"
+        "    for (int s = 0; s < S; ++s) {\n        z[s] = z[s] / denom;"),
+    "final_eps_outside_sqrt": (
+        "    double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n    for",
+        "    double rstd = 1.0 / (sqrt(sumsq / (double)H) + eps);\n    for"),
+    "final_sqrt_missing": (
+        "    double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n    for",
+        "    double rstd = 1.0 / (sumsq / (double)H + eps);\n    for"),
+    "gamma_dropped": (
+        "* rstd * oracle_bf16_to_f64(gamma[h]);",
+        "* rstd;"),
+    "gamma_as_offset": (
+        "* rstd * oracle_bf16_to_f64(gamma[h]);",
+        "* rstd * (1.0 + oracle_bf16_to_f64(gamma[h]));"),
+    "snapshot_row_not_offset": (
+        "            rows[s] = snapshots[s] + off;",
+        "            rows[s] = snapshots[s];"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, "mutation anchor for %s not unique/present" % name
+    src = os.path.join(str(mutant_dir), name + ".c")
+    with open(src, "w") as fh:
+        fh.write(SRC.replace(old, new))
+    lib = obuild.build(source=src, output=os.path.join(str(mutant_dir), "lib%s.so" % name))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for check in pins.QUICK + [pins.check_round_vs_fractions]:
+        try:
+            check(orc)
+        except (AssertionError, RuntimeError, FloatingPointError) as exc:
+            caught.append((check.__name__, str(exc)[:200]))
+            break
+    assert caught, "mutant %s passed every pin" % name
