@@ -1,0 +1,129 @@
+// Device helpers for the gfx950 AttnRes + RMSNorm kernels: bf16 <-> binary32,
+// wave-wide sums on DPP, and the per-token barrier of the split-hidden kernel.
+//
+// Arithmetic conventions (the whole library is built with -ffp-contract=off and
+// IEEE binary32 denormals, so every a*b+c below is written as an explicit fma
+// or as two rounded operations on purpose):
+//   * widening bf16 -> binary32 is exact (a 16-bit shift);
+//   * narrowing binary32 -> bf16 rounds to nearest, ties to even, keeps
+//     subnormals, overflows to +-Inf and keeps NaN quiet.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+// ---- bf16 <-> binary32 --------------------------------------------------
+
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e (0..7) of eight packed bf16 values, widened exactly.
+__device__ __forceinline__ float elem(const uint4& v, int e)
+{
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return (e & 1) ? hi_f32(w) : lo_f32(w);
+}
+
+// Nearest bf16, ties to even.  Adding 0x7fff plus the kept pattern's lowest bit
+// carries into the kept half exactly when the dropped half is above one half,
+// or equal to it with an odd kept half; a carry out of the mantissa moves to the
+// next binade or to Inf, as rounding requires.  NaN is kept quiet.
+__device__ __forceinline__ uint32_t round_bf16(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return round_bf16(lo) | (round_bf16(hi) << 16);
+}
+
+// Two bf16 tensor additions' worth of one packed pair: bf16(a + b) per half,
+// each a binary32 round-to-nearest add of exactly widened operands.
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
+{
+    return pack_bf16(lo_f32(a) + lo_f32(b), hi_f32(a) + hi_f32(b));
+}
+
+__device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b)
+{
+    return make_uint4(add_bf16x2(a.x, b.x), add_bf16x2(a.y, b.y), add_bf16x2(a.z, b.z),
+                      add_bf16x2(a.w, b.w));
+}
+
+// ---- wave-wide sums -------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
+// lane.  Four DPP butterflies give every lane the sum of its 16-lane row
+// (lane i and its partner add the same two values, so both get the same bits);
+// the four row sums are then read as scalars and added in a fixed order.
+// All 64 lanes must be active.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = v + dpp<0xb1>(v);  // quad_perm [1,0,3,2]
+    v = v + dpp<0x4e>(v);  // quad_perm [2,3,0,1]
+    v = v + dpp<0x141>(v); // row_half_mirror: pairs quads 0-1, 2-3
+    v = v + dpp<0x140>(v); // row_mirror: pairs the two halves of a row
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// ---- device-scope loads/stores and the per-token barrier -----------------
+
+__device__ __forceinline__ void store_agent(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier among the `parties` workgroups that share one token.  Words:
+// sync[0] = arrivals in the current episode, sync[1] = episode number.  The
+// last arriver resets the arrival count and then publishes the next episode
+// with a release; the others spin (acquire) until the episode changes.  Every
+// episode leaves sync[0] == 0, so the words never need clearing between calls
+// (HIP-graph replay included).  The spin is bounded: after `spin_limit`
+// polls the workgroup gives up and bumps *timeouts (a counter the host can
+// read), so a broken launch cannot hang the device.
+__device__ __forceinline__ void token_barrier(unsigned* sync, unsigned parties, unsigned spin_limit,
+                                              unsigned* timeouts)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned episode = __hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned arrived =
+            __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (arrived == parties - 1) {
+            __hip_atomic_store(&sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            unsigned polls = 0;
+            while (__hip_atomic_load(&sync[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == episode) {
+                if (++polls >= spin_limit) {
+                    __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+} // namespace attnres

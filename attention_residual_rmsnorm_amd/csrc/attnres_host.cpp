@@ -1,0 +1,162 @@
+// Host-side argument validation and dispatch planning (see attnres_host.hpp).
+#include "attnres_host.hpp"
+
+#include "attnres.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace attnres {
+
+static_assert(MAX_SNAP == ATTNRES_MAX_SNAPSHOTS, "snapshot limit mismatch");
+static_assert(MAX_HIDDEN == ATTNRES_MAX_HIDDEN, "hidden limit mismatch");
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+int round_up64(int64_t x) { return (int)((x + 63) / 64 * 64); }
+
+bool plan_wg(int64_t M, int nvec, int vpt, Plan& pl)
+{
+    if (vpt == 0)
+        vpt = nvec <= 512 ? 1 : nvec <= 1024 ? 2 : 4;
+    if (vpt != 1 && vpt != 2 && vpt != 4)
+        return false;
+    const int maxb = vpt == 1 ? 1024 : 512;
+    const int threads = std::max(64, round_up64((nvec + vpt - 1) / vpt));
+    if (threads > maxb)
+        return false;
+    pl.variant = 1;
+    pl.vpt = vpt;
+    pl.threads = threads;
+    pl.chunks = 1;
+    pl.grid = std::min<int64_t>(M, int64_t(1) << 20);
+    return true;
+}
+
+bool plan_split(int64_t M, int nvec, int vpt, Plan& pl)
+{
+    if (vpt == 0)
+        vpt = 1;
+    if (vpt != 1 && vpt != 2)
+        return false;
+    const int chunks = (nvec + 64 * vpt - 1) / (64 * vpt);
+    if (chunks > MAX_CHUNKS || M > MAX_SPLIT_TOKENS)
+        return false;
+    pl.variant = 2;
+    pl.vpt = vpt;
+    pl.threads = 64;
+    pl.chunks = chunks;
+    pl.grid = M * chunks;
+    return true;
+}
+
+} // namespace
+
+int validate_sizes(int64_t M, int n, int64_t H)
+{
+    if (n < 0)
+        return ATTNRES_EINVAL;
+    if (n > MAX_SNAP)
+        return ATTNRES_EUNSUPPORTED;
+    if (M < 0 || M > INT32_MAX || H < 8 || H % 8 != 0 || H > MAX_HIDDEN)
+        return ATTNRES_EINVAL;
+    return ATTNRES_OK;
+}
+
+int validate_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
+                 int n, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
+                 const void* out_prefix, const void* out_norm)
+{
+    int rc = validate_sizes(M, n, H);
+    if (rc != ATTNRES_OK)
+        return rc;
+    if (!(eps >= 0.0f) || std::isinf(eps))
+        return ATTNRES_EINVAL;
+    if (M == 0)
+        return ATTNRES_OK; // empty batch: the [M,H] buffers may be empty (NULL)
+    if (!prefix || !add || !query || !gamma || !out_prefix || !out_norm)
+        return ATTNRES_EINVAL;
+    if (n > 0 && !snapshots)
+        return ATTNRES_EINVAL;
+    for (int s = 0; s < n; ++s)
+        if (!snapshots[s] || !aligned16(snapshots[s]))
+            return ATTNRES_EINVAL;
+    if (!aligned16(prefix) || !aligned16(add) || (add2 && !aligned16(add2)) || !aligned16(query) ||
+        !aligned16(gamma) || !aligned16(out_prefix) || !aligned16(out_norm))
+        return ATTNRES_EINVAL;
+
+    // Every read-only buffer other than prefix: add, add2, query, gamma, snapshots.
+    const size_t row_bytes = (size_t)M * (size_t)H * 2u, vec_bytes = (size_t)H * 2u;
+    const void* ins[4 + MAX_SNAP];
+    size_t sizes[4 + MAX_SNAP];
+    int ni = 0;
+    ins[ni] = add, sizes[ni++] = row_bytes;
+    if (add2)
+        ins[ni] = add2, sizes[ni++] = row_bytes;
+    ins[ni] = query, sizes[ni++] = vec_bytes;
+    ins[ni] = gamma, sizes[ni++] = vec_bytes;
+    for (int s = 0; s < n; ++s)
+        ins[ni] = snapshots[s], sizes[ni++] = row_bytes;
+    // out_prefix: equal to prefix (in place) or disjoint from it; disjoint from all else
+    if (out_prefix != prefix && overlaps(out_prefix, row_bytes, prefix, row_bytes))
+        return ATTNRES_EALIAS;
+    if (overlaps(out_prefix, row_bytes, out_norm, row_bytes))
+        return ATTNRES_EALIAS;
+    if (overlaps(out_norm, row_bytes, prefix, row_bytes))
+        return ATTNRES_EALIAS;
+    for (int i = 0; i < ni; ++i)
+        if (overlaps(out_prefix, row_bytes, ins[i], sizes[i]) ||
+            overlaps(out_norm, row_bytes, ins[i], sizes[i]))
+            return ATTNRES_EALIAS;
+    return ATTNRES_OK;
+}
+
+bool valid_override(int variant, int param)
+{
+    switch (variant) {
+    case 0: return param == 0;
+    case 1: return param == 0 || param == 1 || param == 2 || param == 4;
+    case 2: return param == 0 || param == 1 || param == 2;
+    default: return false;
+    }
+}
+
+int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, Plan& pl)
+{
+    (void)n;
+    const int nvec = (int)(H / 8);
+    if (force_variant == 1)
+        return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    if (force_variant == 2)
+        return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    // automatic: few tokens -> spread each token over many CUs
+    if (M <= 64 && plan_split(M, nvec, 0, pl))
+        return ATTNRES_OK;
+    return plan_wg(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+}
+
+int validate_add(const void* a, const void* b, const void* out, int64_t n)
+{
+    if (n < 0)
+        return ATTNRES_EINVAL;
+    if (n == 0)
+        return ATTNRES_OK; // nothing to add: the pointers are not examined
+    if (!a || !b || !out)
+        return ATTNRES_EINVAL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return ATTNRES_EINVAL;
+    const size_t bytes = (size_t)n * 2u;
+    if ((out != a && overlaps(out, bytes, a, bytes)) || (out != b && overlaps(out, bytes, b, bytes)))
+        return ATTNRES_EALIAS;
+    return ATTNRES_OK;
+}
+
+} // namespace attnres

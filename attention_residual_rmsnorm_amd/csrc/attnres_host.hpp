@@ -1,0 +1,42 @@
+// Host-side argument validation and dispatch planning of libattnres.
+// Plain C++ (no HIP calls, no device code), so it also builds with g++ under
+// address/undefined-behaviour sanitizers for CPU tests.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace attnres {
+
+constexpr int MAX_SNAP = 12;             // == ATTNRES_MAX_SNAPSHOTS
+constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
+constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
+constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
+
+struct Plan {
+    int variant = 0; // 1 = workgroup per token, 2 = split hidden
+    int vpt = 0;     // 16-byte vectors per thread
+    int threads = 0; // threads per workgroup
+    int chunks = 1;  // workgroups per token
+    int64_t grid = 0;
+};
+
+// Full validation of a fused call; returns a status code (ATTNRES_*).
+int validate_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
+                 int n, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
+                 const void* out_prefix, const void* out_norm);
+
+// Size-only validation (what attnres_plan checks).
+int validate_sizes(int64_t M, int n, int64_t H);
+
+// Dispatch for (M, N, H).  Never depends on whether add2 is given.
+// force_variant / force_param: 0 = automatic, else as attnres_set_variant.
+int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, Plan& pl);
+
+// Is (variant, param) an accepted dispatch override?
+bool valid_override(int variant, int param);
+
+// Validation of the standalone add.
+int validate_add(const void* a, const void* b, const void* out, int64_t n);
+
+} // namespace attnres

@@ -1,0 +1,171 @@
+/*
+ * libattnres: the fused attention-residual (AttnRes) combine + RMSNorm of one
+ * decode step, with the MoE-tail additions folded in, for MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; every tensor is bf16 (bit patterns held in
+ * 16-bit words), row-major and contiguous.  Device pointers must be memory the
+ * GPU can read/write (hipMalloc'd or equivalent); host pointers are marked.
+ *
+ * Operation (per token m, all tokens independent):
+ *   1. fold-add     t  = bf16(add + add2)  (t = add when add2 is NULL)
+ *                   p' = bf16(prefix + t)
+ *      Each addition is a binary32 round-to-nearest-even add of the exactly
+ *      widened bf16 values, subnormals kept; the result is rounded to bf16
+ *      (nearest even).  p' is written to out_prefix and is bit-for-bit what
+ *      two separate bf16 tensor additions produce.  Source: page
+ *      "[#20545][perf] Kimi K3: fold the MoE-tail additions into the next
+ *      attention-residual" (TensorRT-LLM #20546), sections "Description" and
+ *      "Op".
+ *   2. mix          sources k_0..k_{N-1} = the N snapshot rows, k_N = p';
+ *                   z_s = sum_h q_h * k_{s,h} / sqrt(mean_h(k_{s,h}^2) + eps)
+ *                   alpha = softmax(z);   x = sum_s alpha_s * k_s
+ *      The page names this step "attention-residual" and notes (section
+ *      "Model") that the capture tap needs the pre-norm mixture x; it prints
+ *      no formula.  The reading implemented: weightless key RMSNorm, no
+ *      temperature, raw (not normalised) sources mixed, p' taken after its
+ *      bf16 rounding.
+ *   3. RMSNorm      out_norm = bf16(x / sqrt(mean_h(x_h^2) + eps) * gamma)
+ *      x stays binary32 (never rounded to bf16 before the norm).
+ *
+ * Accuracy contract: out_prefix is bit-exact; out_norm is within 2 bf16 ulps
+ * (or 1e-2 absolute) of the same formula evaluated in binary64 with one final
+ * rounding.  Results are deterministic: the same inputs and the same dispatch
+ * give the same bits, and the dispatch never depends on whether add2 is given,
+ * so add2 = s yields the same bits as add = bf16(add + s), add2 = NULL.
+ *
+ * Execution: stream-ordered and asynchronous; no host synchronisation and no
+ * printing.  Every argument is validated before any HIP call; an invalid call
+ * launches nothing.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATTNRES_OK 0
+#define ATTNRES_EINVAL (-1)       /* null required pointer, M < 0 or M > INT32_MAX,
+                                     n_snapshots < 0, H not a positive multiple of 8,
+                                     H above ATTNRES_MAX_HIDDEN,
+                                     pointer not 16-byte aligned, eps < 0 or not finite,
+                                     bad variant request */
+#define ATTNRES_EUNSUPPORTED (-2) /* n_snapshots > ATTNRES_MAX_SNAPSHOTS: the caller
+                                     adds the tail first and takes an unfused route
+                                     (the page's fallback for N > 12, section "Model") */
+#define ATTNRES_EALIAS (-3)       /* forbidden overlap between an output and any other
+                                     buffer */
+#define ATTNRES_EHIP (-4)         /* a HIP call failed (launch error, no device,
+                                     out of memory for the scratch) */
+
+#define ATTNRES_MAX_SNAPSHOTS 12 /* the fused window's source limit (section "Model") */
+#define ATTNRES_MAX_HIDDEN 16384
+
+/*
+ * attnres_add_rmsnorm_fwd -- the fused decode step described above.
+ *
+ *   prefix       device bf16 [M,H]  running prefix sum (read)
+ *   add          device bf16 [M,H]  first addend, e.g. routed MoE output (read)
+ *   add2         device bf16 [M,H]  second addend, e.g. shared-expert output, or
+ *                                   NULL for the single-addend form (read)
+ *   snapshots    HOST array of n_snapshots device pointers, each bf16 [M,H]
+ *                (the snapshot bank, read); may be NULL when n_snapshots == 0.
+ *                Entries may repeat.  The array is read during the call only.
+ *   n_snapshots  N, 0 <= N <= 12; N = 0 mixes the updated prefix alone (weight
+ *                1), i.e. plain fold-add + RMSNorm
+ *   query        device bf16 [H]    per-layer query of the mix (read)
+ *   gamma        device bf16 [H]    RMSNorm weight, applied as y = x*rstd*gamma
+ *   eps          finite, >= 0; added to the mean square in both RMSNorms
+ *   M            tokens, >= 0.  M = 0 launches nothing and returns ATTNRES_OK
+ *                once N, H and eps are valid; the pointers are not examined.
+ *   H            hidden size, a multiple of 8, 8 <= H <= ATTNRES_MAX_HIDDEN
+ *   out_prefix   device bf16 [M,H]  updated prefix p' (written).  May equal
+ *                prefix exactly (in place); any other overlap with an input or
+ *                with out_norm is ATTNRES_EALIAS.
+ *   out_norm     device bf16 [M,H]  normalised mixture (written); must not
+ *                overlap any other buffer.
+ *   stream       HIP stream the work is enqueued on (0 = the null stream)
+ *
+ * All device pointers must be 16-byte aligned.  The caller owns every buffer
+ * and must keep it alive until the stream work completes.  The library owns a
+ * per-device scratch buffer used by the split-hidden kernel (partials and
+ * barrier counters, which reset themselves); it is allocated on the first
+ * call on a device, or by attnres_init().  Calls that use it on the same
+ * device must be ordered with respect to each other (same stream, or
+ * synchronised): two overlapping calls on different streams of one device
+ * race on it.
+ *
+ * Returns ATTNRES_OK or one of the negative codes above.
+ */
+int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, const void* add2,
+                            const void* const* snapshots, int n_snapshots,
+                            const void* query, const void* gamma, float eps,
+                            int64_t M, int64_t H, void* out_prefix, void* out_norm,
+                            hipStream_t stream);
+
+/*
+ * attnres_bf16_add -- the unfused MoE-tail addition: out = bf16(a + b)
+ * elementwise (binary32 round-to-nearest add, subnormals kept), n elements.
+ * This is the standalone kernel the fold replaces (page "[#20545][perf] Kimi
+ * K3: fold the MoE-tail additions ...", sections "Description" and
+ * "Performance"); it serves the eager chain and the fused-vs-unfused timing.
+ *   a, b, out    device bf16 [n], 16-byte aligned; out may equal a or b exactly,
+ *                other overlaps are ATTNRES_EALIAS
+ *   n            >= 0 elements (any n; n = 0 launches nothing, returns ATTNRES_OK
+ *                and does not examine the pointers)
+ */
+int attnres_bf16_add(const void* a, const void* b, void* out, int64_t n,
+                     hipStream_t stream);
+
+/*
+ * attnres_init -- allocate the split-hidden scratch on the current device and
+ * clear its counters (synchronously).  Optional: the first fused call on a
+ * device does it too.  Call it before capturing calls into a HIP graph, since
+ * allocation is not allowed during capture.  Returns ATTNRES_OK or
+ * ATTNRES_EHIP.
+ */
+int attnres_init(void);
+
+/*
+ * attnres_plan -- the launch the fused call would make for (M, N, H), without
+ * any HIP call.  *variant: 1 = workgroup per token, 2 = split hidden;
+ * *chunks: workgroups per token; *threads: threads per workgroup.  Any output
+ * pointer may be NULL.  Returns ATTNRES_OK or the status the call would return
+ * for these sizes.
+ */
+int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunks,
+                 int* threads);
+
+/*
+ * attnres_set_variant -- process-wide dispatch override for tests and
+ * benchmarks: variant 0 = automatic, 1 = workgroup per token (vectors per
+ * thread = param: 0 automatic, or 1, 2, 4), 2 = split hidden (vectors per
+ * thread = param: 0 automatic, or 1, 2).  Not thread-safe with concurrent
+ * calls.  Returns ATTNRES_OK or ATTNRES_EINVAL.
+ */
+int attnres_set_variant(int variant, int param);
+
+/*
+ * attnres_debug_timeouts -- diagnostic: *out = number of times a split-hidden
+ * workgroup gave up waiting at a per-token barrier on the current device since
+ * the scratch was created (0 in a correct run).  Synchronous (copies one word
+ * to the host).  Returns ATTNRES_OK, ATTNRES_EINVAL (out NULL) or ATTNRES_EHIP.
+ */
+int attnres_debug_timeouts(unsigned* out);
+
+/* Human-readable name of a status code (static storage). */
+const char* attnres_status_string(int status);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int attnres_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

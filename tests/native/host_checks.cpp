@@ -1,0 +1,90 @@
+// CPU check of libattnres's host-side validation and planning, built with g++
+// under -fsanitize=address,undefined (test code).  It drives every path of the
+// validator with fake, never-dereferenced addresses, at every snapshot count
+// 0..13 with and without the second addend, and checks the status codes.  A
+// stack or heap overrun anywhere in that code aborts the run.
+#include "attnres_host.hpp"
+#include "attnres.h"
+
+#include <cstdio>
+#include <cstdlib>
+
+using namespace attnres;
+
+static int failures = 0;
+
+#define EXPECT(cond)                                                                      \
+    do {                                                                                  \
+        if (!(cond)) {                                                                    \
+            std::fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);          \
+            ++failures;                                                                   \
+        }                                                                                 \
+    } while (0)
+
+static const void* at(uintptr_t a) { return reinterpret_cast<const void*>(a); }
+
+int main()
+{
+    const uintptr_t base = uintptr_t(1) << 40;
+    const int64_t M = 4, H = 7168;
+    const uintptr_t row = uintptr_t(M * H * 2);
+    const void* snaps[13];
+    for (int s = 0; s < 13; ++s)
+        snaps[s] = at(base + (uintptr_t)(10 + s) * row);
+    const void* prefix = at(base);
+    const void* add = at(base + row);
+    const void* add2 = at(base + 2 * row);
+    const void* query = at(base + 3 * row);
+    const void* gamma = at(base + 3 * row + 32768); // query: 14336 bytes at 3*row
+    const void* outp = at(base + 4 * row);
+    const void* outn = at(base + 5 * row);
+
+    for (int with2 = 0; with2 < 2; ++with2) {
+        for (int n = 0; n <= 13; ++n) {
+            const void* a2 = with2 ? add2 : nullptr;
+            const int want = n <= 12 ? ATTNRES_OK : ATTNRES_EUNSUPPORTED;
+            EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn) == want);
+            // in place is allowed
+            EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, prefix, outn) == want);
+            if (n >= 1 && n <= 12) {
+                // out_norm equal to the last snapshot
+                EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp,
+                                    snaps[n - 1]) == ATTNRES_EALIAS);
+                // out_prefix inside the last snapshot
+                EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H,
+                                    at(reinterpret_cast<uintptr_t>(snaps[n - 1]) + 4096), outn) ==
+                       ATTNRES_EALIAS);
+            }
+            Plan pl;
+            for (int fv = 0; fv <= 2; ++fv)
+                for (int fp = 0; fp <= 4; ++fp) {
+                    if (!valid_override(fv, fp))
+                        continue;
+                    for (int64_t m : {int64_t(1), int64_t(8), int64_t(64), int64_t(65), int64_t(512),
+                                      int64_t(513), int64_t(1) << 21})
+                        for (int64_t h : {int64_t(8), int64_t(520), int64_t(7168), int64_t(8192),
+                                          int64_t(16384)}) {
+                            const int rc = make_plan(m, n, h, fv, fp, pl);
+                            if (rc == ATTNRES_OK) {
+                                EXPECT(pl.threads % 64 == 0 && pl.threads >= 64 && pl.threads <= 1024);
+                                EXPECT(pl.grid >= 1);
+                                EXPECT((int64_t)pl.threads * pl.vpt * pl.chunks * 8 >= h);
+                                if (pl.variant == 2)
+                                    EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
+                                           pl.grid == m * pl.chunks);
+                            } else {
+                                EXPECT(fv != 0 || h > 8192); // automatic always finds a plan
+                            }
+                        }
+                }
+        }
+    }
+    EXPECT(validate_fwd(nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr, 1e-6f, 0, H, nullptr,
+                        nullptr) == ATTNRES_OK);
+    EXPECT(validate_add(prefix, add, outp, 1000) == ATTNRES_OK);
+    EXPECT(validate_add(prefix, add, prefix, 1000) == ATTNRES_OK);
+    EXPECT(validate_add(prefix, add, at(base + 16), 1000) == ATTNRES_EALIAS);
+    EXPECT(validate_add(nullptr, nullptr, nullptr, 0) == ATTNRES_OK);
+    std::printf("host checks: %d failures\n", failures);
+    return failures ? 1 : 0;
+}

@@ -1,0 +1,163 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol the
+header declares, and rejects invalid calls with the documented status codes
+before any HIP call (so these run without a GPU and launch nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_residual_rmsnorm_amd as ar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ar.library_path), reason="libattnres.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attnres_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attnres_add_rmsnorm_fwd", "attnres_bf16_add", "attnres_init", "attnres_plan",
+              "attnres_set_variant", "attnres_status_string", "attnres_version", "attnres_debug_timeouts"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ar.library_path)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict(re.findall(r"#define (ATTNRES_E?\w+)\s+\(?(-?\d+)\)?", text))
+    assert int(codes["ATTNRES_OK"]) == ar.ATTNRES_OK
+    assert int(codes["ATTNRES_EINVAL"]) == ar.ATTNRES_EINVAL
+    assert int(codes["ATTNRES_EUNSUPPORTED"]) == ar.ATTNRES_EUNSUPPORTED
+    assert int(codes["ATTNRES_EALIAS"]) == ar.ATTNRES_EALIAS
+    assert int(codes["ATTNRES_EHIP"]) == ar.ATTNRES_EHIP
+    assert int(codes["ATTNRES_MAX_SNAPSHOTS"]) == ar.ATTNRES_MAX_SNAPSHOTS
+    assert int(codes["ATTNRES_MAX_HIDDEN"]) == ar.ATTNRES_MAX_HIDDEN
+    assert ar.attnres_version() >= 100
+    assert "overlap" in ar.attnres_status_string(ar.ATTNRES_EALIAS)
+
+
+# Validation: fake but plausible 16-byte-aligned addresses.  Every call below
+# is invalid, so the library returns before touching HIP.
+A = 1 << 40
+ROW = 7168 * 2 * 4  # bytes of an [M=4, H=7168] tensor
+
+
+def base_args(**kw):
+    d = dict(prefix=A, add=A + 1 * ROW, add2=A + 2 * ROW, snaps=[A + 3 * ROW, A + 4 * ROW],
+             query=A + 5 * ROW, gamma=A + 5 * ROW + 65536, eps=1e-6, M=4, H=7168,
+             out_prefix=A + 7 * ROW, out_norm=A + 8 * ROW)
+    d.update(kw)
+    return d
+
+
+def call(d, n=None):
+    lib = ar.library()
+    snaps = d["snaps"]
+    n = len(snaps) if n is None else n
+    arr = (ctypes.c_void_p * max(len(snaps), 1))(*snaps) if snaps is not None else None
+    return lib.attnres_add_rmsnorm_fwd(d["prefix"], d["add"], d["add2"], arr, n, d["query"], d["gamma"],
+                                       ctypes.c_float(d["eps"]), d["M"], d["H"], d["out_prefix"],
+                                       d["out_norm"], None)
+
+
+@pytest.mark.parametrize("field", ["prefix", "add", "query", "gamma", "out_prefix", "out_norm"])
+def test_null_required_pointer(field):
+    assert call(base_args(**{field: None})) == ar.ATTNRES_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), ar.ATTNRES_EINVAL),
+    (dict(M=1 << 31), ar.ATTNRES_EINVAL),
+    (dict(H=0), ar.ATTNRES_EINVAL),
+    (dict(H=7164), ar.ATTNRES_EINVAL),
+    (dict(H=4), ar.ATTNRES_EINVAL),
+    (dict(H=ar.ATTNRES_MAX_HIDDEN + 8), ar.ATTNRES_EINVAL),
+    (dict(eps=-1e-6), ar.ATTNRES_EINVAL),
+    (dict(eps=float("nan")), ar.ATTNRES_EINVAL),
+    (dict(eps=float("inf")), ar.ATTNRES_EINVAL),
+    (dict(prefix=A + 8), ar.ATTNRES_EINVAL),
+    (dict(add2=A + 2 * ROW + 2), ar.ATTNRES_EINVAL),
+    (dict(out_norm=A + 8 * ROW + 4), ar.ATTNRES_EINVAL),
+    (dict(snaps=[A + 3 * ROW, A + 4 * ROW + 2]), ar.ATTNRES_EINVAL),
+    (dict(snaps=[A + 3 * ROW, None]), ar.ATTNRES_EINVAL),
+])
+def test_invalid_sizes_and_alignment(kw, code):
+    assert call(base_args(**kw)) == code
+
+
+def test_snapshot_count():
+    assert call(base_args(), n=-1) == ar.ATTNRES_EINVAL
+    many = [A + (10 + i) * ROW for i in range(13)]
+    assert call(base_args(snaps=many)) == ar.ATTNRES_EUNSUPPORTED
+    assert call(base_args(snaps=None), n=2) == ar.ATTNRES_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out_prefix=A + 16),                       # partial overlap with prefix
+    dict(out_prefix=A + 1 * ROW),                  # == add
+    dict(out_prefix=A + 2 * ROW + 4096),           # inside add2
+    dict(out_prefix=A + 4 * ROW),                  # == a snapshot
+    dict(out_norm=A),                              # == prefix
+    dict(out_norm=A + 7 * ROW),                    # == out_prefix
+    dict(out_norm=A + 5 * ROW),                    # == query
+    dict(out_norm=A + 5 * ROW + 65536 - 16),       # overlaps gamma
+    dict(out_norm=A + 7 * ROW + 16),               # partial overlap with out_prefix
+])
+def test_aliasing(kw):
+    assert call(base_args(**kw)) == ar.ATTNRES_EALIAS
+
+
+def test_bf16_add_validation():
+    lib = ar.library()
+    assert lib.attnres_bf16_add(None, A, A + ROW, 8, None) == ar.ATTNRES_EINVAL
+    assert lib.attnres_bf16_add(A, A + ROW, A + 2 * ROW, -1, None) == ar.ATTNRES_EINVAL
+    assert lib.attnres_bf16_add(A + 2, A + ROW, A + 2 * ROW, 8, None) == ar.ATTNRES_EINVAL
+    assert lib.attnres_bf16_add(A, A + ROW, A + 16, 64, None) == ar.ATTNRES_EALIAS
+
+
+def test_plan_is_pure_and_sane():
+    # small batches spread tokens over CUs, large ones use a workgroup per token
+    v, c, t = ar.attnres_plan(1, 12, 7168)
+    assert v == 2 and c * t * 8 >= 7168
+    v, c, t = ar.attnres_plan(256, 12, 7168)
+    assert v == 1 and c == 1 and t % 64 == 0
+    with pytest.raises(ar.AttnResError):
+        ar.attnres_plan(1, 13, 7168)
+    with pytest.raises(ar.AttnResError):
+        ar.attnres_plan(1, 4, 7170)
+
+
+def test_set_variant_validation():
+    lib = ar.library()
+    assert lib.attnres_set_variant(3, 0) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(1, 3) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(2, 4) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(0, 1) == ar.ATTNRES_EINVAL
+    try:
+        ar.attnres_set_variant(2, 0)
+        assert ar.attnres_plan(256, 4, 7168)[0] == 2
+        ar.attnres_set_variant(1, 1)
+        assert ar.attnres_plan(1, 4, 7168) == (1, 1, 896)
+    finally:
+        ar.attnres_set_variant(0, 0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from attention_residual_rmsnorm_amd import _binding
+
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "library_path", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        _binding.library()

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+out_prefix must be bit-exact and out_norm within 2 bf16 ulps or 1e-2 (see
+parity.py), for the named workloads, every source count, ragged and extreme
+sizes, both kernels (workgroup per token "W", split hidden "S") and their
+vector widths.  Also: two addends == one pre-summed addend bitwise (page
+"[#20545][perf] Kimi K3: fold the MoE-tail additions ...", section "Test
+Coverage"), the hand-derived subnormal examples, determinism, HIP-graph
+replay, canaries around the outputs, and the standalone add kernel.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import parity as P
+import pins
+from attention_residual_rmsnorm_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+# (variant, vectors per thread); 0 = automatic
+VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2)]
+VID = ["auto", "W1", "W2", "S1", "S2"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_residual_rmsnorm_amd as ar
+
+    ar.library()
+    ar.attnres_init()
+    yield ar
+    ar.attnres_set_variant(0, 0)
+
+
+@pytest.fixture
+def variant(request, ar):
+    v, param = request.param
+    ar.attnres_set_variant(v, param)
+    yield (v, param)
+    ar.attnres_set_variant(0, 0)
+
+
+def supported(ar, M, N, H):
+    try:
+        ar.attnres_plan(M, N, H)
+        return True
+    except ar.AttnResError:
+        return False
+
+
+_case_cache = {}
+
+
+def case_for(key, fn):
+    if key not in _case_cache:
+        _case_cache[key] = fn()
+    return _case_cache[key]
+
+
+# --- the named workloads ------------------------------------------------------
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VID, indirect=True)
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_named_workload(ar, orc, variant, name):
+    case = case_for(name, lambda: W.config_case(name))
+    if not supported(ar, case.M, case.N, case.H):
+        pytest.skip("variant not available for this size")
+    say("case", name, "variant", variant, ar.attnres_plan(case.M, case.N, case.H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, name)
+
+
+def test_named_workload_structure():
+    """The subnormal workload really plants subnormal sums and prefixes."""
+    c = W.config_case("cfg3")
+    sub = lambda b: ((b & 0x7F80) == 0) & ((b & 0x7F) != 0)
+    assert sub(c.prefix).mean() > 0.009
+    t = pins.bits_of(pins.tbf(c.add) + pins.tbf(c.add2))
+    assert sub(t).mean() > 0.009
+
+
+# --- two addends == one pre-summed addend, bitwise, N = 0..12 -----------------
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_add2_equals_presummed(ar, variant, M):
+    for N in range(13):
+        case = case_for(("presum", M, N), lambda: W.make_case(cfg=50, M=M, N=N, add2=True))
+        t = pins.bits_of(pins.tbf(case.add) + pins.tbf(case.add2))
+        a = P.run_gpu(case)
+        import dataclasses
+
+        b = P.run_gpu(dataclasses.replace(case, add=t, add2=None))
+        assert np.array_equal(a[0], b[0]), "M=%d N=%d out_prefix" % (M, N)
+        assert np.array_equal(a[1], b[1]), "M=%d N=%d out_norm" % (M, N)
+        want = pins.torch_prefix(case.prefix, case.add, case.add2)
+        assert np.array_equal(a[0], want), "M=%d N=%d prefix != torch" % (M, N)
+
+
+# --- hand-derived fold-add examples through the kernels ----------------------
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VID, indirect=True)
+def test_golden_fold_add(ar, variant):
+    rows = pins.read_golden_fold()
+    H = 64
+    M = len(rows)
+    prefix = np.array([[r[0]] * H for r in rows], np.uint16)
+    add = np.array([[r[1]] * H for r in rows], np.uint16)
+    add2_rows = [r for r in rows if r[2] is not None]
+    q = np.zeros(H, np.uint16)
+    g = np.full(H, 0x3F80, np.uint16)
+    # rows with add2
+    idx = [i for i, r in enumerate(rows) if r[2] is not None]
+    c = W.Case("golden", len(idx), H, prefix[idx], add[idx], np.array([[r[2]] * H for r in add2_rows], np.uint16),
+               [], q, g)
+    gp, _ = P.run_gpu(c)
+    for k, i in enumerate(idx):
+        assert np.all(gp[k] == rows[i][3]), "row %d: %04x != %04x" % (i, gp[k][0], rows[i][3])
+    idx1 = [i for i, r in enumerate(rows) if r[2] is None]
+    c1 = W.Case("golden1", len(idx1), H, prefix[idx1], add[idx1], None, [], q, g)
+    gp1, _ = P.run_gpu(c1)
+    for k, i in enumerate(idx1):
+        assert np.all(gp1[k] == rows[i][3])
+
+
+# --- ragged, tiny and maximal shapes -----------------------------------------
+
+SHAPES = [
+    (1, 8, 0), (3, 8, 12), (2, 64, 1), (5, 520, 3), (3, 1000, 12), (67, 1000, 5),
+    (4, 4104, 7), (2, 7176, 12), (9, 8192, 12), (2, 8200, 4), (3, 16384, 12), (1, 16384, 0),
+    (65, 7168, 2), (130, 512, 12),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VID, indirect=True)
+@pytest.mark.parametrize("M,H,N", SHAPES)
+def test_shapes(ar, orc, variant, M, H, N):
+    if not supported(ar, M, N, H):
+        pytest.skip("variant not available for this size")
+    case = case_for(("shape", M, H, N), lambda: W.make_case(cfg=60, M=M, H=H, N=N, add2=(N % 2 == 0)))
+    say("shape", M, H, N, "variant", variant, ar.attnres_plan(M, N, H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+
+
+def test_beyond_split_slots_and_grid(ar, orc):
+    """M above the split-hidden token slots (workgroup per token), and M above the
+    W grid cap (grid-stride over tokens), checked on sampled rows."""
+    import torch
+
+    for M, H, N in ((600, 7168, 4), ((1 << 20) + 5, 8, 2)):
+        case = W.make_case(cfg=61, M=M, H=H, N=N, add2=True)
+        say("large M", M, H, N, ar.attnres_plan(M, N, H))
+        gp, gn = P.run_gpu(case)
+        idx = np.unique(np.r_[0, 1, M // 2, M - 2, M - 1, np.random.default_rng(0).integers(0, M, 64)])
+        sub = case.rows(idx)
+        rp, rn = P.run_oracle(orc, sub)
+        P.assert_parity(gp[idx], gn[idx], rp, rn, "M=%d" % M)
+        del gp, gn
+        torch.cuda.empty_cache()
+
+
+def test_empty_batch(ar):
+    import torch
+
+    z = torch.empty((0, 7168), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(7168, dtype=torch.bfloat16, device="cuda")
+    op, on = ar.attnres_add_rmsnorm_fwd(z, z, z, [z, z], v, v, 1e-6)
+    assert op.shape == (0, 7168) and on.shape == (0, 7168)
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+def test_in_place_prefix(ar, orc, variant):
+    case = W.make_case(cfg=62, M=8, N=5, add2=True)
+    prefix = P.dev(case.prefix)
+    d = P.dev
+    op, on = ar.attnres_add_rmsnorm_fwd(prefix, d(case.add), d(case.add2), [d(s) for s in case.snapshots],
+                                        d(case.query), d(case.gamma), case.eps, out_prefix=prefix)
+    assert op.data_ptr() == prefix.data_ptr()
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(P.host(op), P.host(on), rp, rn, "in place")
+
+
+# --- determinism, graphs, canaries ---------------------------------------------
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+def test_deterministic(ar, variant):
+    case = case_for("cfg4", lambda: W.config_case("cfg4"))
+    first = P.run_gpu(case)
+    for _ in range(20):
+        again = P.run_gpu(case)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+def test_graph_replay(ar, variant):
+    """Capture one call into a HIP graph; replay it with fresh inputs copied
+    in between (eager work and synchronisation between replays); every replay
+    must equal the eager call on the same inputs, bit for bit."""
+    import torch
+
+    cases = [W.make_case(cfg=70 + i, M=16, N=8, add2=True) for i in range(4)]
+    c0 = cases[0]
+    d = P.dev
+    ins = dict(prefix=d(c0.prefix), add=d(c0.add), add2=d(c0.add2), snaps=[d(s) for s in c0.snapshots],
+               query=d(c0.query), gamma=d(c0.gamma))
+    outp = torch.empty_like(ins["prefix"])
+    outn = torch.empty_like(ins["prefix"])
+
+    def call():
+        ar.attnres_add_rmsnorm_fwd(ins["prefix"], ins["add"], ins["add2"], ins["snaps"], ins["query"],
+                                   ins["gamma"], c0.eps, out_prefix=outp, out_norm=outn)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(12):
+        c = cases[rep % len(cases)]
+        ins["prefix"].copy_(d(c.prefix))
+        ins["add"].copy_(d(c.add))
+        ins["add2"].copy_(d(c.add2))
+        for t, src in zip(ins["snaps"], c.snapshots):
+            t.copy_(d(src))
+        ins["query"].copy_(d(c.query))
+        ins["gamma"].copy_(d(c.gamma))
+        outp.zero_()
+        outn.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        gp, gn = P.host(outp), P.host(outn)
+        ep, en = P.run_gpu(c)
+        assert np.array_equal(gp, ep) and np.array_equal(gn, en), "replay %d" % rep
+    assert ar.attnres_debug_timeouts() == 0
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+def test_canaries(ar, orc, variant):
+    """Outputs live inside larger buffers filled with a canary pattern: nothing
+    outside [M,H] may change."""
+    import torch
+
+    case = W.make_case(cfg=63, M=7, H=1000, N=3, add2=True)
+    n = case.M * case.H
+    pad = 4096
+    canary = 0x7E57
+    bufp = torch.full((n + 2 * pad,), canary, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    bufn = torch.full((n + 2 * pad,), canary, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    outp = bufp[pad:pad + n].view(case.M, case.H)
+    outn = bufn[pad:pad + n].view(case.M, case.H)
+    gp, gn = P.run_gpu(case, out_prefix=outp, out_norm=outn)
+    for buf in (bufp, bufn):
+        h = P.host(buf)
+        assert np.all(h[:pad] == canary) and np.all(h[pad + n:] == canary)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "canary")
+
+
+def test_no_barrier_timeouts(ar):
+    assert ar.attnres_debug_timeouts() == 0
+
+
+# --- the standalone add ----------------------------------------------------------
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536, 65536 * 3 + 5])
+def test_bf16_add(ar, orc, n):
+    rng = np.random.default_rng(n)
+    a = rng.integers(0, 1 << 16, n).astype(np.uint16)
+    b = rng.integers(0, 1 << 16, n).astype(np.uint16)
+    if n >= 65536:
+        a[:65536] = np.arange(65536, dtype=np.uint16)  # every pattern once
+    out = P.host(ar.attnres_bf16_add(P.dev(a), P.dev(b)))
+    want = orc.add_tensor(a, b)
+    nan = P.is_nan16(want)
+    assert np.array_equal(out[~nan], want[~nan])
+    assert np.all(P.is_nan16(out[nan]))
+
+
+def test_single_hip_runtime(ar):
+    """libattnres binds to the HIP runtime torch already loaded: exactly one
+    libamdhip64 is mapped in the process."""
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = sorted(set(l.split()[-1] for l in maps if "libamdhip64" in l))
+    assert len(libs) == 1, libs
+    assert any("libattnres.so" in l for l in maps)
