@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     attnres_debug_timeouts,
     attnres_init,
     attnres_plan,
+    attnres_selftest_rounding,
     attnres_set_variant,
     attnres_status_string,
     attnres_version,

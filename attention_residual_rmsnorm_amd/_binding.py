@@ -58,6 +58,8 @@ def library():
         lib.attnres_set_variant.restype = ctypes.c_int
         lib.attnres_debug_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint)]
         lib.attnres_debug_timeouts.restype = ctypes.c_int
+        lib.attnres_selftest_rounding.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
+        lib.attnres_selftest_rounding.restype = ctypes.c_int
         lib.attnres_status_string.argtypes = [ctypes.c_int]
         lib.attnres_status_string.restype = ctypes.c_char_p
         lib.attnres_version.argtypes = []
@@ -171,6 +173,14 @@ def attnres_set_variant(variant: int, param: int = 0) -> None:
 def attnres_debug_timeouts() -> int:
     out = ctypes.c_uint()
     _check(library().attnres_debug_timeouts(ctypes.byref(out)), "attnres_debug_timeouts")
+    return out.value
+
+
+def attnres_selftest_rounding() -> int:
+    """Number of binary32 inputs whose device bf16 rounding disagrees with the
+    definition (0 expected); runs on the current device."""
+    out = ctypes.c_ulonglong()
+    _check(library().attnres_selftest_rounding(ctypes.byref(out)), "attnres_selftest_rounding")
     return out.value
 
 

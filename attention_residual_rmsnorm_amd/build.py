@@ -17,7 +17,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "attnres.hip"), os.path.join(PKG, "csrc", "attnres_host.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("attnres.hip", "attnres_selftest.hip", "attnres_host.cpp")]
 HEADERS = [os.path.join(PKG, "csrc", n) for n in ("attnres_device.hpp", "attnres_host.hpp")] + [
     os.path.join(ROOT, "include", "attnres.h")]
 LIBRARY = os.path.join(PKG, "libattnres.so")

@@ -91,29 +91,26 @@ __device__ __forceinline__ void softmax_weights(const float* tot, float inv_h, f
         alpha[s] = alpha[s] * inv;
 }
 
-// Loads of vector v of one token's rows (16 bytes = 8 bf16 each); lanes past
-// the end of the row get zeros, which contribute nothing to any sum.
+// Loads of vector v of one token's rows (16 bytes = 8 bf16 each).  The loads
+// are unconditional: a lane past the end of the row reads the row's last
+// vector again (a valid address).  Its values are never stored, and its
+// shares of the sums are dropped (see source_partials and combine), so no
+// branch or mask sits between the loads: every load of the thread is in
+// flight at once.
 template <int NS, bool ADD2, int S, int VPT>
 __device__ __forceinline__ void load_vectors(const Params& p, int64_t row, int v, bool ok, uint4& a,
                                              uint4& b, uint4& c, uint4 (&k)[S][VPT], int j, uint4& q,
                                              uint4& g)
 {
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    a = b = c = q = g = zero;
+    const int vc = ok ? v : p.nvec - 1;
+    a = p.prefix[row + vc];
+    b = p.add[row + vc];
+    c = ADD2 ? p.add2[row + vc] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        k[s][j] = zero;
-    if (ok) {
-        a = p.prefix[row + v];
-        b = p.add[row + v];
-        if (ADD2)
-            c = p.add2[row + v];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            k[s][j] = p.snap[s][row + v];
-        q = p.query[v];
-        g = p.gamma[v];
-    }
+        k[s][j] = p.snap[s][row + vc];
+    q = p.query[vc];
+    g = p.gamma[vc];
 }
 
 // Register fence: the compiler must assume the packed sources changed, so it
@@ -140,34 +137,89 @@ __device__ __forceinline__ void fold_add(const uint4* a, const uint4* b, const u
     }
 }
 
-// A2 for one thread: per-source sums over its VPT*8 elements, fixed order.
+// A2 for one thread: per-source sums over its VPT*8 elements in a fixed order
+// (vector by vector, pair by pair, on v_dot2_f32_bf16); vectors outside the
+// row (ok[j] false) contribute zero.
 template <int S, int VPT>
-__device__ __forceinline__ void source_partials(const uint4 (&k)[S][VPT], const uint4* q, float* part)
+__device__ __forceinline__ void source_partials(const uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
+                                                float* part)
 {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         float ss = 0.f, qd = 0.f;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = elem(k[s][j], e);
-                ss = __builtin_fmaf(x, x, ss);
-                qd = __builtin_fmaf(elem(q[j], e), x, qd);
-            }
+        for (int j = 0; j < VPT; ++j) {
+            const uint4 x = k[s][j];
+            float ssj = dot2_bf16(x.x, x.x, 0.f);
+            ssj = dot2_bf16(x.y, x.y, ssj);
+            ssj = dot2_bf16(x.z, x.z, ssj);
+            ssj = dot2_bf16(x.w, x.w, ssj);
+            float qdj = dot2_bf16(q[j].x, x.x, 0.f);
+            qdj = dot2_bf16(q[j].y, x.y, qdj);
+            qdj = dot2_bf16(q[j].z, x.z, qdj);
+            qdj = dot2_bf16(q[j].w, x.w, qdj);
+            ss += ok[j] ? ssj : 0.f;
+            qd += ok[j] ? qdj : 0.f;
+        }
         part[2 * s] = ss;
         part[2 * s + 1] = qd;
     }
 }
 
+// Workgroup-wide sums of NV per-thread values; afterwards tot[0..NV-1] (LDS)
+// holds the totals, which every thread reads with identical bits.  Quads are
+// summed first (DPP); one lane per quad stores its NV quad sums as a row of
+// `rows` (NVP floats, zero padded); fixed segments of rows are summed by
+// (value, segment) threads, and the segment sums in segment order.  The order
+// is fixed by (NV, blockDim.x) alone.
+template <int NV, int NVP>
+__device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float* segs, float* tot, int tid,
+                                           int nthreads)
+{
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        part[i] = quad_sum(part[i]);
+    if ((tid & 3) == 0) {
+        float4* r = reinterpret_cast<float4*>(rows + (tid >> 2) * NVP);
+#pragma unroll
+        for (int i = 0; i < NVP / 4; ++i)
+            r[i] = make_float4(4 * i + 0 < NV ? part[(4 * i + 0) % NV] : 0.f,
+                               4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
+                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
+                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
+    }
+    __syncthreads();
+    const int nrows = nthreads >> 2;
+    const int nseg = nthreads / NVP;
+    const int rps = (nrows + nseg - 1) / nseg;
+    if (tid < nseg * NVP) {
+        const int v = tid % NVP, seg = tid / NVP;
+        const int r0 = seg * rps, r1 = min(nrows, r0 + rps);
+        float acc = 0.f;
+        for (int r = r0; r < r1; ++r)
+            acc += rows[r * NVP + v];
+        segs[seg * NVP + v] = acc;
+    }
+    __syncthreads();
+    if (tid < NV) {
+        float acc = segs[tid];
+        for (int sg = 1; sg < nseg; ++sg)
+            acc += segs[sg * NVP + tid];
+        tot[tid] = acc;
+    }
+    __syncthreads();
+}
+
 // A4 for one thread: x = sum_s alpha_s k_s (fixed source order), and the
-// thread's share of sum x^2.
+// thread's share of sum x^2 (vectors outside the row contribute zero).
 template <int S, int VPT>
-__device__ __forceinline__ float combine(const uint4 (&k)[S][VPT], const float* alpha, float (&x)[VPT][8])
+__device__ __forceinline__ float combine(const uint4 (&k)[S][VPT], const float* alpha, const bool* ok,
+                                         float (&x)[VPT][8])
 {
     float sx = 0.f;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j)
+    for (int j = 0; j < VPT; ++j) {
+        float sxj = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float acc = alpha[0] * elem(k[0][j], e);
@@ -175,8 +227,10 @@ __device__ __forceinline__ float combine(const uint4 (&k)[S][VPT], const float* 
             for (int s = 1; s < S; ++s)
                 acc = __builtin_fmaf(alpha[s], elem(k[s][j], e), acc);
             x[j][e] = acc;
-            sx = __builtin_fmaf(acc, acc, sx);
+            sxj = __builtin_fmaf(acc, acc, sxj);
         }
+        sx += ok[j] ? sxj : 0.f;
+    }
     return sx;
 }
 
@@ -198,17 +252,20 @@ __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, cons
 template <int NS, bool ADD2, int VPT, int MAXB>
 __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 {
-    constexpr int S = NS + 1;   // sources: snapshots, then the updated prefix
-    constexpr int NV = 2 * S;   // partials per token
+    constexpr int S = NS + 1;                // sources: snapshots, then the updated prefix
+    constexpr int NV = 2 * S;                // partials per token
+    constexpr int NVP = (NV + 3) / 4 * 4;    // LDS record length
     constexpr int MAXW = MAXB / 64;
-    __shared__ float red[MAXW][NV];
-    __shared__ float tot[NV];
+    __shared__ __align__(16) float rows[(MAXB / 4) * NVP];
+    __shared__ float segs[MAXB];
+    __shared__ __align__(16) float tot[NVP];
     __shared__ float red2[MAXW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nw = blockDim.x >> 6;
+    const int nthreads = blockDim.x;
+    const int nw = nthreads >> 6;
     const int nvec = p.nvec;
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
@@ -217,38 +274,26 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
         bool ok[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int v = tid + j * (int)blockDim.x;
+            const int v = tid + j * nthreads;
             ok[j] = v < nvec;
             load_vectors<NS, ADD2>(p, row, v, ok[j], a[j], b[j], c[j], k, j, q[j], g[j]);
         }
+        // keep every load above this point: nothing that waits on a load may be
+        // scheduled between them
+        __builtin_amdgcn_sched_barrier(0);
 
         // A1
         fold_add<ADD2, VPT>(a, b, c, k[NS]);
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
             if (ok[j])
-                p.out_prefix[row + tid + j * (int)blockDim.x] = k[NS][j];
+                p.out_prefix[row + tid + j * nthreads] = k[NS][j];
 
-        // A2: thread -> wave (DPP) -> workgroup (LDS, waves in order)
+        // A2: per thread, then over the workgroup
         float part[NV];
-        source_partials<S, VPT>(k, q, part);
+        source_partials<S, VPT>(k, q, ok, part);
         fence_sources<S, VPT>(k);
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            part[i] = wave_sum(part[i]);
-        if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                red[wave][i] = part[i];
-        }
-        __syncthreads();
-        if (tid < NV) {
-            float acc = red[0][tid];
-            for (int w = 1; w < nw; ++w)
-                acc += red[w][tid];
-            tot[tid] = acc;
-        }
-        __syncthreads();
+        block_sums<NV, NVP>(part, rows, segs, tot, tid, nthreads);
 
         // A3
         float totr[NV], alpha[S];
@@ -259,7 +304,7 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 
         // A4 + A5
         float x[VPT][8];
-        float sx = wave_sum(combine<S, VPT>(k, alpha, x));
+        const float sx = wave_sum(combine<S, VPT>(k, alpha, ok, x));
         if (lane == 0)
             red2[wave] = sx;
         __syncthreads();
@@ -270,7 +315,7 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
             if (ok[j])
-                p.out_norm[row + tid + j * (int)blockDim.x] = normalise(x[j], rstd, g[j]);
+                p.out_norm[row + tid + j * nthreads] = normalise(x[j], rstd, g[j]);
         __syncthreads(); // LDS reuse by the next token
     }
 }
@@ -300,6 +345,7 @@ __global__ __launch_bounds__(64) void fwd_split(Params p)
         ok[j] = v < nvec;
         load_vectors<NS, ADD2>(p, row, v, ok[j], a[j], b[j], c[j], k, j, q[j], g[j]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // A1
     fold_add<ADD2, VPT>(a, b, c, k[NS]);
@@ -310,7 +356,7 @@ __global__ __launch_bounds__(64) void fwd_split(Params p)
 
     // A2: thread -> wave; lane i publishes partial i of this chunk
     float part[NV];
-    source_partials<S, VPT>(k, q, part);
+    source_partials<S, VPT>(k, q, ok, part);
     fence_sources<S, VPT>(k);
     float mine = 0.f;
 #pragma unroll
@@ -339,7 +385,7 @@ __global__ __launch_bounds__(64) void fwd_split(Params p)
     // A3, A4
     softmax_weights<S>(tot, p.inv_h, p.eps, alpha);
     float x[VPT][8];
-    const float sx = wave_sum(combine<S, VPT>(k, alpha, x));
+    const float sx = wave_sum(combine<S, VPT>(k, alpha, ok, x));
     if (lane == 0)
         store_agent(&p.part2[(size_t)t * C + chunk], sx);
     token_barrier(sync, (unsigned)C, p.spin_limit, p.timeouts);
@@ -365,7 +411,7 @@ __global__ __launch_bounds__(256) void bf16_add_kernel(const uint4* a, const uin
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride)
         out[i] = add_bf16x8(a[i], b[i]);
     if (blockIdx.x == 0 && (int)threadIdx.x < tail)
-        ot[threadIdx.x] = (uint16_t)round_bf16(lo_f32(at[threadIdx.x]) + lo_f32(bt[threadIdx.x]));
+        ot[threadIdx.x] = (uint16_t)(pack_bf16(lo_f32(at[threadIdx.x]) + lo_f32(bt[threadIdx.x]), 0.f) & 0xffffu);
 }
 
 // ---------------------------------------------------------------------------

@@ -4,9 +4,9 @@
 // Arithmetic conventions (the whole library is built with -ffp-contract=off and
 // IEEE binary32 denormals, so every a*b+c below is written as an explicit fma
 // or as two rounded operations on purpose):
-//   * widening bf16 -> binary32 is exact (a 16-bit shift);
+//   * widening bf16 -> binary32 is exact (a 16-bit shift or a mask);
 //   * narrowing binary32 -> bf16 rounds to nearest, ties to even, keeps
-//     subnormals, overflows to +-Inf and keeps NaN quiet.
+//     subnormals, overflows to +-Inf and keeps NaN quiet (pack_bf16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,20 +26,20 @@ __device__ __forceinline__ float elem(const uint4& v, int e)
     return (e & 1) ? hi_f32(w) : lo_f32(w);
 }
 
-// Nearest bf16, ties to even.  Adding 0x7fff plus the kept pattern's lowest bit
-// carries into the kept half exactly when the dropped half is above one half,
-// or equal to it with an odd kept half; a carry out of the mantissa moves to the
-// next binade or to Inf, as rounding requires.  NaN is kept quiet.
-__device__ __forceinline__ uint32_t round_bf16(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
-}
+// Two binary32 values rounded to bf16 and packed (lo in bits 15:0).  The
+// conversion compiles to gfx950's v_cvt_pk_bf16_f32, which rounds to nearest
+// even, keeps subnormals (the kernels run with IEEE binary32 denormals),
+// overflows to +-Inf and returns a quiet NaN for NaN; this equals rounding by
+// definition on every binary32 input (checked exhaustively on the device by
+// attnres_selftest_rounding).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
-    return round_bf16(lo) | (round_bf16(hi) << 16);
+    bf16x2_t r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Two bf16 tensor additions' worth of one packed pair: bf16(a + b) per half,
@@ -55,6 +55,16 @@ __device__ __forceinline__ uint4 add_bf16x8(const uint4& a, const uint4& b)
                       add_bf16x2(a.w, b.w));
 }
 
+// c + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs (v_dot2_f32_bf16).  The
+// bf16 products are exact in binary32; the sum is rounded by the instruction.
+// Used for the per-source partial sums, whose accuracy need only be far below
+// one bf16 ulp of the output.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                           c, false);
+}
+
 // ---- wave-wide sums -------------------------------------------------------
 
 template <int CTRL>
@@ -63,15 +73,23 @@ __device__ __forceinline__ float dpp(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+// Sum over each group of 4 consecutive lanes (a quad), returned in all four
+// lanes with identical bits (both partners of a DPP exchange add the same two
+// values).  All 64 lanes must be active.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v = v + dpp<0xb1>(v); // quad_perm [1,0,3,2]
+    v = v + dpp<0x4e>(v); // quad_perm [2,3,0,1]
+    return v;
+}
+
 // Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
-// lane.  Four DPP butterflies give every lane the sum of its 16-lane row
-// (lane i and its partner add the same two values, so both get the same bits);
+// lane.  Four DPP butterflies give every lane the sum of its 16-lane row;
 // the four row sums are then read as scalars and added in a fixed order.
 // All 64 lanes must be active.
 __device__ __forceinline__ float wave_sum(float v)
 {
-    v = v + dpp<0xb1>(v);  // quad_perm [1,0,3,2]
-    v = v + dpp<0x4e>(v);  // quad_perm [2,3,0,1]
+    v = quad_sum(v);
     v = v + dpp<0x141>(v); // row_half_mirror: pairs quads 0-1, 2-3
     v = v + dpp<0x140>(v); // row_mirror: pairs the two halves of a row
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));

@@ -137,10 +137,12 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     if (force_variant == 2)
         return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
-    // automatic: few tokens -> spread each token over many CUs
-    if (M <= 64 && plan_split(M, nvec, 0, pl))
+    // automatic: one workgroup per token (measured faster than the split-hidden
+    // kernel at every batch size: its cross-workgroup barriers cost more than
+    // spreading a token over CUs saves)
+    if (plan_wg(M, nvec, 0, pl))
         return ATTNRES_OK;
-    return plan_wg(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    return plan_split(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
 }
 
 int validate_add(const void* a, const void* b, const void* out, int64_t n)

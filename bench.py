@@ -1,0 +1,496 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused AttnRes combine + RMSNorm decode step on one MI355X.
+
+Workload (the bandwidth configuration): the 25-layer decoder chain of the fused
+op, 256 tokens, H = 7168, bf16, the snapshot bank growing by one entry every
+two layers up to 12 sources (N = 1,1,2,2,...,11,11,12,12,12), each layer's
+MoE tail (routed, shared) folded into the call.  A step is one pass of the
+whole chain.  To measure HBM and not the 256 MB Infinity Cache, the step runs
+16 independent 256-token chains interleaved layer by layer (16 micro-batches,
+about 6 GB of distinct buffers): between two calls of one chain, more than
+256 MB of other data streams through the caches.
+
+value = algorithmic bytes of the step / step time (GB/s, HIP-graph replay,
+inputs resident in HBM).  Algorithmic bytes of one call with N sources:
+14336 * M * (5 + N) + 28672 (reads prefix, add, add2, N snapshots; writes
+out_prefix, out_norm; plus query and gamma).
+
+Also reported on the same JSON line:
+  roofline      the fused kernel's achieved GB/s: algorithmic bytes per launch
+                / average launch duration, the latter from the HIP events that
+                bracket the timed region (graph replays holding only the fused
+                launches); per-layer times from events around each layer's
+                group of launches (queue pre-filled by a sleep kernel, so the
+                events bracket back-to-back kernels); against 8 TB/s; traffic
+                from the committed rocprofv3 PMC summary when it was taken on
+                the current kernel source
+  cpu_baseline  the CPU oracle on the same chain (all 256 tokens, one
+                micro-batch), parallel over token blocks
+  latency_us    per-call time of the small named calls over 16 rotated buffer
+                sets: graph replay, and eager back-to-back launches
+  fold          the pages' comparison: fused call with add2 vs the unfused
+                route (standalone add, then the fused call without add2)
+
+Every timing follows a parity check against the CPU oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of ~8 TB/s) at M tokens × N sources, H=7168"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attnres_fwd_chain_m256_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_residual_rmsnorm_amd", "csrc", n)
+                  for n in ("attnres.hip", "attnres_device.hpp", "attnres_host.cpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def call_bytes(M, H, N, add2=True):
+    return 2 * H * (M * (4 + int(add2) + N) + 2)
+
+
+def dev(bits):
+    """numpy bf16 bit patterns -> bfloat16 device tensor."""
+    import numpy as np
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def host(t):
+    import numpy as np
+    import torch
+
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def norm_ok(got, want):
+    """out_norm within 2 bf16 ulps (monotone integer distance) or 1e-2 absolute, no NaN."""
+    import numpy as np
+
+    from attention_residual_rmsnorm_amd.workloads import bf16_bits_to_f32
+
+    def ordv(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+    nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    ulps = np.abs(ordv(got) - ordv(want))
+    diff = np.abs(bf16_bits_to_f32(got).astype(np.float64) - bf16_bits_to_f32(want))
+    return bool(np.all(((ulps <= 2) | (diff <= 1e-2)) & ~nan(got) & ~nan(want)))
+
+
+# --------------------------------------------------------------------------
+# raw launches (precomputed ctypes arguments keep host overhead low)
+
+class Launcher:
+    def __init__(self):
+        import attention_residual_rmsnorm_amd as ar
+
+        self.ar = ar
+        self.lib = ar.library()
+        self.fwd = self.lib.attnres_add_rmsnorm_fwd
+        self.add = self.lib.attnres_bf16_add
+        self._keep = []
+
+    def fused_args(self, prefix, add, add2, snaps, query, gamma, eps, out_prefix, out_norm):
+        vp = ctypes.c_void_p
+        n = len(snaps)
+        arr = (vp * max(n, 1))(*[s.data_ptr() for s in snaps])
+        self._keep.append(arr)
+        M, H = prefix.shape
+        return (prefix.data_ptr(), add.data_ptr(), None if add2 is None else add2.data_ptr(),
+                arr if n else None, n, query.data_ptr(), gamma.data_ptr(), ctypes.c_float(eps), M, H,
+                out_prefix.data_ptr(), out_norm.data_ptr())
+
+    def run_fused(self, args, stream):
+        rc = self.fwd(*args, stream)
+        if rc != 0:
+            raise RuntimeError("attnres_add_rmsnorm_fwd -> %d" % rc)
+
+    def run_add(self, a, b, out, stream):
+        rc = self.add(a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(), stream)
+        if rc != 0:
+            raise RuntimeError("attnres_bf16_add -> %d" % rc)
+
+
+# --------------------------------------------------------------------------
+# the chain, R micro-batches on the device
+
+class DeviceChains:
+    """R copies of one 256-token chain, each with its own buffers."""
+
+    def __init__(self, chain, R, launcher):
+        import torch
+
+        self.chain, self.R, self.L = chain, R, launcher
+        self.layers = chain.layers
+        q = [dev(l.query) for l in chain.layers]
+        g = [dev(l.gamma) for l in chain.layers]
+        routed0 = [dev(l.routed) for l in chain.layers]
+        shared0 = [dev(l.shared) for l in chain.layers]
+        emb0, p00 = dev(chain.embedding), dev(chain.prefix0)
+        M, H = chain.M, chain.H
+        self.inst = []
+        for i in range(R):
+            c = dict(
+                emb=emb0.clone(), p0=p00.clone(), zero=torch.zeros_like(p00),
+                routed=[t.clone() for t in routed0], shared=[t.clone() for t in shared0],
+                tail=[torch.empty_like(p00) for _ in chain.layers],
+                out_prefix=[torch.empty((M, H), dtype=torch.bfloat16, device="cuda") for _ in chain.layers],
+                out_norm=[torch.empty((M, H), dtype=torch.bfloat16, device="cuda") for _ in chain.layers])
+            self.inst.append(c)
+        self.q, self.g = q, g
+        # static hand-off plan per (instance, layer): prefix and bank tensors
+        self.fused = []      # [layer][instance] ctypes args, both addends
+        self.unfused = []    # [layer][instance] ctypes args, pre-summed addend
+        for l, layer in enumerate(chain.layers):
+            row_f, row_u = [], []
+            for c in self.inst:
+                bank = [c["emb"]] + [c["out_prefix"][k] for k in range(l) if self.layers[k].push_after]
+                if l == 0:
+                    prefix = c["p0"]
+                elif self.layers[l - 1].push_after:
+                    prefix = c["zero"]
+                else:
+                    prefix = c["out_prefix"][l - 1]
+                assert len(bank) == layer.n_sources
+                row_f.append(launcher.fused_args(prefix, c["routed"][l], c["shared"][l], bank, q[l], g[l],
+                                                 chain.eps, c["out_prefix"][l], c["out_norm"][l]))
+                row_u.append(launcher.fused_args(prefix, c["tail"][l], None, bank, q[l], g[l],
+                                                 chain.eps, c["out_prefix"][l], c["out_norm"][l]))
+            self.fused.append(row_f)
+            self.unfused.append(row_u)
+
+    def step(self, stream, fused=True):
+        L = self.L
+        for l in range(len(self.layers)):
+            for i, c in enumerate(self.inst):
+                if fused:
+                    L.run_fused(self.fused[l][i], stream)
+                else:
+                    L.run_add(c["routed"][l], c["shared"][l], c["tail"][l], stream)
+                    L.run_fused(self.unfused[l][i], stream)
+
+    def launches_per_step(self):
+        return len(self.layers) * self.R
+
+    def bytes_per_step(self):
+        c = self.chain
+        return self.R * sum(call_bytes(c.M, c.H, l.n_sources) for l in self.layers)
+
+
+# --------------------------------------------------------------------------
+
+def graph_time(fn, steps, warmup):
+    """Capture fn(stream) into a HIP graph; replay `warmup` then `steps` times.
+    Returns seconds per replay (events bracketed by synchronisation)."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps, g
+
+
+def event_group_times(groups, sleep_cycles=200_000_000):
+    """GPU time of each group of back-to-back launches (seconds).  A sleep
+    kernel holds the queue while the host enqueues every group, with one HIP
+    event between groups, so the events bracket kernels that run back to back
+    (not host launch gaps).  `groups` is a list of lists of fn(stream_handle)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(groups) + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
+    evs[0].record(stream)
+    for i, grp in enumerate(groups):
+        for fn in grp:
+            fn(h)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(len(groups))]
+
+
+# --------------------------------------------------------------------------
+
+def parity_gate(chain, launcher, orc):
+    """Run one chain on the GPU (fresh buffers) and compare sampled token rows
+    with the CPU oracle chain: bit-exact prefixes, out_norm within 2 ulps."""
+    import numpy as np
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+    ar = launcher.ar
+    d = [(dev(l.query), dev(l.gamma), dev(l.routed), dev(l.shared)) for l in chain.layers]
+    step = lambda l, p, b, L: ar.attnres_add_rmsnorm_fwd(p, d[l][2], d[l][3], b, d[l][0], d[l][1], chain.eps)
+    zero = lambda: torch.zeros((chain.M, chain.H), dtype=torch.bfloat16, device="cuda")
+    outs, _ = W.run_chain(chain, step, zero, embedding=dev(chain.embedding), prefix0=dev(chain.prefix0))
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 63, 128, 200, 255])
+    sub = chain.rows(idx)
+    ref, _ = W.run_chain(sub, lambda l, p, b, L: orc.fwd(p, L.routed, L.shared, b, L.query, L.gamma, sub.eps),
+                         lambda: np.zeros((sub.M, sub.H), np.uint16))
+    for l, ((gp, gn), (rp, rn)) in enumerate(zip(outs, ref)):
+        gp, gn = host(gp)[idx], host(gn)[idx]
+        if not np.array_equal(gp, rp):
+            raise SystemExit("parity gate: layer %d out_prefix differs from the oracle" % l)
+        if not norm_ok(gn, rn):
+            raise SystemExit("parity gate: layer %d out_norm outside 2 ulps of the oracle" % l)
+    log("parity gate: 25 layers, %d sampled tokens: ok" % len(idx))
+
+
+def cpu_baseline(chain, threads, min_cpu_seconds=12.0, max_passes=8):
+    """The CPU oracle (as it stands) on the chain: all 256 tokens, token blocks
+    on `threads` threads (ctypes releases the GIL), repeated until about
+    `min_cpu_seconds` of CPU work (threads x wall) is done."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    orc = oracle.get()
+    blocks = np.array_split(np.arange(chain.M), threads)
+    subs = [chain.rows(idx) for idx in blocks]
+
+    def run_block(sub):
+        W.run_chain(sub, lambda l, p, b, L: orc.fwd(p, L.routed, L.shared, b, L.query, L.gamma, sub.eps),
+                    lambda: np.zeros((sub.M, sub.H), np.uint16))
+
+    passes, wall = 0, 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        while passes < max_passes and (passes == 0 or wall * threads < min_cpu_seconds):
+            t0 = time.perf_counter()
+            list(ex.map(run_block, subs))
+            wall += time.perf_counter() - t0
+            passes += 1
+    nbytes = passes * sum(call_bytes(chain.M, chain.H, l.n_sources) for l in chain.layers)
+    return {"value": round(nbytes / wall / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the full 25-layer chain (256 tokens, H=7168, N=1..12, add2) %d times, oracle in "
+                      "binary64, token blocks over %d threads; %.2f s wall" % (passes, threads, wall)}
+
+
+def read_traffic(src_hash):
+    """HBM bytes per fused launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def latency_suite(launcher, rotate=16, calls=96):
+    """µs per call of the small named workloads, over `rotate` distinct buffer sets."""
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    out = {}
+    for name in ("cfg1", "cfg2", "cfg3", "cfg4", "cfg4b"):
+        case = W.config_case(name)
+        sets = []
+        for r in range(rotate):
+            t = lambda x: None if x is None else dev(x)
+            prefix, add, add2 = t(case.prefix), t(case.add), t(case.add2)
+            snaps = [t(s) for s in case.snapshots]
+            q, g = t(case.query), t(case.gamma)
+            op, on = torch.empty_like(prefix), torch.empty_like(prefix)
+            sets.append(launcher.fused_args(prefix, add, add2, snaps, q, g, case.eps, op, on))
+            sets[-1] = (sets[-1], (prefix, add, add2, snaps, q, g, op, on))
+        args = [s[0] for s in sets]
+
+        def many(stream, args=args):
+            for k in range(calls):
+                launcher.run_fused(args[k % len(args)], stream)
+
+        per_replay, _ = graph_time(many, steps=20, warmup=3)
+        grp = event_group_times([[lambda h, a=args[k % len(args)]: launcher.run_fused(a, h) for k in range(calls)]
+                                 for _ in range(3)], sleep_cycles=50_000_000)
+        eager = min(grp) / calls
+        nbytes = call_bytes(case.M, case.H, case.N, case.add2 is not None)
+        out[name] = {"M": case.M, "N": case.N, "graph_us_per_call": round(per_replay / calls * 1e6, 3),
+                     "eager_us_per_call": round(eager * 1e6, 3),
+                     "GBps_graph": round(nbytes / (per_replay / calls) / 1e9, 1),
+                     "variant": launcher.ar.attnres_plan(case.M, case.N, case.H)[0]}
+        log("latency %s: %s" % (name, out[name]))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--micro-batches", type=int, default=16)
+    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy"], default="full",
+                    help="full: everything; chain: the timed chain only (for kernel-trace "
+                         "profiling); eager: --steps eager steps of the chain, no graph and no "
+                         "timing (for counter collection); copy: a plain 1 GiB device copy, the "
+                         "calibration kernel for the HBM byte counters")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the step is one "
+              "GPU's share; see the design notes for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.mode == "copy":
+        n = 1 << 29  # 2^29 bf16 = 1 GiB
+        a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_copy": 2 * n, "bytes_written_per_copy": 2 * n,
+                          "copies": 5}))
+        return
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    launcher = Launcher()
+    launcher.ar.attnres_init()
+    chain = W.make_chain()
+    log("chain inputs ready: M=%d H=%d layers=%d" % (chain.M, chain.H, len(chain.layers)))
+
+    import oracle
+
+    parity_gate(chain, launcher, oracle.get())
+
+    dc = DeviceChains(chain, args.micro_batches, launcher)
+    log("device buffers: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
+    if args.mode == "eager":
+        for k in range(args.steps):
+            dc.step(torch.cuda.current_stream().cuda_stream, fused=True)
+            torch.cuda.synchronize()
+            log("eager step %d done" % k)
+        print(json.dumps({"mode": "eager", "steps": args.steps, "launches": dc.launches_per_step() * args.steps,
+                          "algorithmic_bytes_per_launch": dc.bytes_per_step() / dc.launches_per_step()}))
+        return
+
+    # timed region: whole steps as HIP-graph replays
+    sec, _ = graph_time(lambda s: dc.step(s, fused=True), args.steps, args.warmup)
+    nbytes = dc.bytes_per_step()
+    value = nbytes / sec / 1e9
+    log("step: %.3f ms, %.1f GB/s" % (sec * 1e3, value))
+
+    # the fused kernel's average launch duration over the timed region (the
+    # replayed graph holds nothing but the step's fused launches)
+    launches = dc.launches_per_step()
+    per_launch_bytes = nbytes / launches
+    avg_kernel = sec / launches
+    achieved = per_launch_bytes / avg_kernel / 1e9
+    # per layer: events around each layer's group of micro-batch launches
+    groups = [[(lambda h, a=dc.fused[l][i]: launcher.run_fused(a, h)) for i in range(dc.R)]
+              for l in range(len(dc.layers))]
+    gt = event_group_times(groups)
+    per_layer = {}
+    for l, layer in enumerate(dc.layers):
+        per_layer.setdefault(layer.n_sources, []).append(gt[l] / dc.R)
+    t12 = sum(per_layer[12]) / len(per_layer[12])
+    b12 = call_bytes(chain.M, chain.H, 12)
+    t1 = sum(per_layer[1]) / len(per_layer[1])
+    b1 = call_bytes(chain.M, chain.H, 1)
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash)
+    plan = launcher.ar.attnres_plan(chain.M, 12, chain.H)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "attnres fused fwd, variant %s (%d threads/workgroup)" % (
+                    "W" if plan[0] == 1 else "S", plan[2]),
+                "avg_kernel_us": round(avg_kernel * 1e6, 3),
+                "algorithmic_bytes_per_launch": round(per_launch_bytes),
+                "n12_layer": {"kernel_us": round(t12 * 1e6, 3), "GBps": round(b12 / t12 / 1e9, 1),
+                              "frac": round(b12 / t12 / 1e9 / HBM_PEAK_GBS, 4)},
+                "n1_layer": {"kernel_us": round(t1 * 1e6, 3), "GBps": round(b1 / t1 / 1e9, 1),
+                             "frac": round(b1 / t1 / 1e9 / HBM_PEAK_GBS, 4)},
+                "kernel_source_sha256_16": src_hash}
+    log("roofline: %s" % roofline)
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "25-layer AttnRes+RMSNorm decode chain, M=256 tokens, H=7168, bf16, "
+                               "N=1..12 snapshot sources, MoE tail folded (add2); %d independent "
+                               "micro-batches interleaved per layer (HBM-cold)" % args.micro_batches,
+                   "tokens": chain.M, "hidden": chain.H, "layers": len(chain.layers),
+                   "micro_batches": args.micro_batches, "calls_per_step": launches,
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": roofline,
+    }
+
+    if args.mode == "full":
+        # the pages' comparison: fold vs standalone add + unfused call
+        sec_u, _ = graph_time(lambda s: dc.step(s, fused=False), max(5, args.steps // 2), args.warmup)
+        result["fold"] = {"fused_ms_per_step": round(sec * 1e3, 4), "unfused_ms_per_step": round(sec_u * 1e3, 4),
+                          "saving_us_per_call": round((sec_u - sec) / launches * 1e6, 3)}
+        log("fold: %s" % result["fold"])
+        result["latency_us"] = latency_suite(launcher)
+        if not args.no_cpu_baseline:
+            threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
+            result["cpu_baseline"] = cpu_baseline(chain, threads)
+            log("cpu baseline: %s" % result["cpu_baseline"])
+    assert launcher.ar.attnres_debug_timeouts() == 0
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

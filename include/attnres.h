@@ -158,6 +158,17 @@ int attnres_set_variant(int variant, int param);
  */
 int attnres_debug_timeouts(unsigned* out);
 
+/*
+ * attnres_selftest_rounding -- diagnostic: checks on the current device that
+ * the packed binary32 -> bf16 conversion the kernels use rounds every one of
+ * the 2^32 binary32 inputs to nearest even exactly as rounding by definition
+ * does (subnormals and overflow included; NaN must stay NaN).
+ * *mismatches = number of inputs that disagree (0 expected).  Synchronous;
+ * allocates and frees 16 bytes of device memory.  Returns ATTNRES_OK,
+ * ATTNRES_EINVAL (NULL) or ATTNRES_EHIP.
+ */
+int attnres_selftest_rounding(unsigned long long* mismatches);
+
 /* Human-readable name of a status code (static storage). */
 const char* attnres_status_string(int status);
 

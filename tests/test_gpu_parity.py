@@ -302,3 +302,9 @@ def test_single_hip_runtime(ar):
     libs = sorted(set(l.split()[-1] for l in maps if "libamdhip64" in l))
     assert len(libs) == 1, libs
     assert any("libattnres.so" in l for l in maps)
+
+
+def test_device_rounding_matches_definition(ar):
+    """The hardware bf16 conversion behind every rounding in the kernels equals
+    rounding by definition on all 2^32 binary32 inputs (NaN stays NaN)."""
+    assert ar.attnres_selftest_rounding() == 0
