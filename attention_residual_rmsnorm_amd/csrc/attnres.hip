@@ -17,11 +17,12 @@
 //      registers (N+1 sources x 8 bf16 x VPT 16-byte vectors per thread), the
 //      2(N+1) partials are reduced wave-wide on DPP and across waves in LDS.
 //      No inter-workgroup communication.  Used when there are many tokens.
-//   S  split hidden: C single-wave workgroups per token, each owning 64*VPT
-//      16-byte vectors of the row.  Partials go through a device scratch
-//      buffer and a per-token barrier (two per call: after A2 and after the
-//      sum of squares of A5).  Spreads a few tokens over many CUs, which is
-//      what the latency-bound small-M calls need.
+//   S  split hidden: C workgroups per token, each owning a contiguous chunk of
+//      the row (one 16-byte vector per thread).  All chunks of a token are
+//      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
+//      chunk's share of sum x^2 are exchanged through tagged 64-bit records
+//      with relaxed device-scope atomics (no fences).  Spreads a few tokens
+//      over many CUs, which is what the latency-bound small-M calls need.
 // Both reduce in a fixed order: the same inputs give the same bits, and the
 // add2 / no-add2 instantiations share every line after A1.
 #include "attnres.h"
@@ -40,8 +41,8 @@
 
 namespace attnres {
 
-constexpr int PART_STRIDE = 32;          // floats per (token, chunk) partial record (>= 2*13)
-constexpr int SYNC_STRIDE = 32;          // barrier words per token: one 128-byte line each
+constexpr int REC_STRIDE = 32;           // records per (token, chunk) of the first exchange (>= 2*13)
+constexpr int STATE_STRIDE = 32;         // epoch word per token: one 128-byte line each
 constexpr unsigned SPIN_LIMIT = 1u << 20;
 
 struct Params {
@@ -58,10 +59,10 @@ struct Params {
     int nvec;           // H / 8 (16-byte vectors per row)
     int chunks;         // split hidden: workgroups per token
     int64_t M;
-    float* part;        // split hidden: [token][chunk][PART_STRIDE] partials of A2
-    float* part2;       // split hidden: [token][chunk] sum of squares of the mixture
-    unsigned* sync;     // split hidden: [token][SYNC_STRIDE] barrier words
-    unsigned* timeouts; // split hidden: barrier polls that gave up
+    unsigned long long* rec1; // split hidden: [token][MAX_CHUNKS][REC_STRIDE] tagged A2 partials
+    unsigned long long* rec2; // split hidden: [token][MAX_CHUNKS] tagged chunk sums of x^2
+    unsigned* state;          // split hidden: [token][STATE_STRIDE] epoch word (index 0)
+    unsigned* timeouts;       // split hidden: exchange waits that gave up
     unsigned spin_limit;
 };
 
@@ -91,6 +92,21 @@ __device__ __forceinline__ void softmax_weights(const float* tot, float inv_h, f
         alpha[s] = alpha[s] * inv;
 }
 
+// A 16-byte load with the non-temporal hint, for the [M,H] streams: a decode
+// step reads each of them once, and between two calls of the op the layer in
+// between streams far more than the caches hold, so keeping these lines would
+// only displace others.  query and gamma, read by every token of the call, are
+// loaded normally.
+__device__ __forceinline__ uint4 load_stream(const uint4* p)
+{
+    uint4 r;
+    r.x = __builtin_nontemporal_load(&p->x);
+    r.y = __builtin_nontemporal_load(&p->y);
+    r.z = __builtin_nontemporal_load(&p->z);
+    r.w = __builtin_nontemporal_load(&p->w);
+    return r;
+}
+
 // Loads of vector v of one token's rows (16 bytes = 8 bf16 each).  The loads
 // are unconditional: a lane past the end of the row reads the row's last
 // vector again (a valid address).  Its values are never stored, and its
@@ -103,12 +119,12 @@ __device__ __forceinline__ void load_vectors(const Params& p, int64_t row, int v
                                              uint4& g)
 {
     const int vc = ok ? v : p.nvec - 1;
-    a = p.prefix[row + vc];
-    b = p.add[row + vc];
-    c = ADD2 ? p.add2[row + vc] : make_uint4(0u, 0u, 0u, 0u);
+    a = load_stream(&p.prefix[row + vc]);
+    b = load_stream(&p.add[row + vc]);
+    c = ADD2 ? load_stream(&p.add2[row + vc]) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        k[s][j] = p.snap[s][row + vc];
+        k[s][j] = load_stream(&p.snap[s][row + vc]);
     q = p.query[vc];
     g = p.gamma[vc];
 }
@@ -167,20 +183,18 @@ __device__ __forceinline__ void source_partials(const uint4 (&k)[S][VPT], const 
 }
 
 // Workgroup-wide sums of NV per-thread values; afterwards tot[0..NV-1] (LDS)
-// holds the totals, which every thread reads with identical bits.  Quads are
-// summed first (DPP); one lane per quad stores its NV quad sums as a row of
-// `rows` (NVP floats, zero padded); fixed segments of rows are summed by
-// (value, segment) threads, and the segment sums in segment order.  The order
-// is fixed by (NV, blockDim.x) alone.
-template <int NV, int NVP>
-__device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float* segs, float* tot, int tid,
-                                           int nthreads)
+// holds the totals, which every thread reads with identical bits.  Each
+// 16-lane row is summed on DPP; lane 0 of the row stores its NV row sums as a
+// row of `rows` (NVP floats, zero padded); thread v < NV then adds the rows in
+// row order.  The order is fixed by blockDim.x alone.  MAXROWS = MAXB / 16.
+template <int NV, int NVP, int MAXROWS>
+__device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float* tot, int tid, int nthreads)
 {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-        part[i] = quad_sum(part[i]);
-    if ((tid & 3) == 0) {
-        float4* r = reinterpret_cast<float4*>(rows + (tid >> 2) * NVP);
+        part[i] = row_sum(part[i]);
+    if ((tid & 15) == 0) {
+        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * NVP);
 #pragma unroll
         for (int i = 0; i < NVP / 4; ++i)
             r[i] = make_float4(4 * i + 0 < NV ? part[(4 * i + 0) % NV] : 0.f,
@@ -189,22 +203,20 @@ __device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float
                                4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
     }
     __syncthreads();
-    const int nrows = nthreads >> 2;
-    const int nseg = nthreads / NVP;
-    const int rps = (nrows + nseg - 1) / nseg;
-    if (tid < nseg * NVP) {
-        const int v = tid % NVP, seg = tid / NVP;
-        const int r0 = seg * rps, r1 = min(nrows, r0 + rps);
-        float acc = 0.f;
-        for (int r = r0; r < r1; ++r)
-            acc += rows[r * NVP + v];
-        segs[seg * NVP + v] = acc;
-    }
-    __syncthreads();
     if (tid < NV) {
-        float acc = segs[tid];
-        for (int sg = 1; sg < nseg; ++sg)
-            acc += segs[sg * NVP + tid];
+        // rows in order, loaded 8 at a time so the loads overlap
+        const int nrows = nthreads >> 4;
+        float acc = rows[tid];
+        for (int r0 = 1; r0 < nrows; r0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                v[r] = r0 + r < nrows ? rows[(r0 + r) * NVP + tid] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r0 + r < nrows)
+                    acc += v[r];
+        }
         tot[tid] = acc;
     }
     __syncthreads();
@@ -256,8 +268,8 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
     constexpr int NV = 2 * S;                // partials per token
     constexpr int NVP = (NV + 3) / 4 * 4;    // LDS record length
     constexpr int MAXW = MAXB / 64;
-    __shared__ __align__(16) float rows[(MAXB / 4) * NVP];
-    __shared__ float segs[MAXB];
+    constexpr int MAXROWS = MAXB / 16;
+    __shared__ __align__(16) float rows[MAXROWS * NVP];
     __shared__ __align__(16) float tot[NVP];
     __shared__ float red2[MAXW];
 
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
         float part[NV];
         source_partials<S, VPT>(k, q, ok, part);
         fence_sources<S, VPT>(k);
-        block_sums<NV, NVP>(part, rows, segs, tot, tid, nthreads);
+        block_sums<NV, NVP, MAXROWS>(part, rows, tot, tid, nthreads);
 
         // A3
         float totr[NV], alpha[S];
@@ -321,83 +333,159 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Kernel S: split hidden.  Workgroup b (one wave) handles token b / C, chunk
-// b % C, i.e. vectors chunk*64*VPT + j*64 + lane.  grid = M * C exactly.
-template <int NS, bool ADD2, int VPT>
-__global__ __launch_bounds__(64) void fwd_split(Params p)
+// Kernel S: split hidden.  blockDim.x threads per workgroup, one 16-byte vector
+// each; C = p.chunks workgroups per token, chunk c owning vectors
+// [c*blockDim.x, (c+1)*blockDim.x).  Workgroup b serves token (b/8/C)*8 + b%8,
+// chunk (b/8)%C, so every chunk of a token has the same b mod 8 (the XCD the
+// dispatcher assigns it to); grid = 8*C*ceil(M/8) and workgroups past the last
+// token exit at once.
+//
+// Exchanges (see attnres_device.hpp): the call's epoch E is read from the
+// token's state word at the start; the A2 partials travel with tag 2E+1, the
+// chunk sums of x^2 with tag 2E+2.  Chunk 0 advances the state word to E+1
+// after it has seen every chunk's second record, i.e. after every workgroup of
+// the token has read E, so all workgroups of one call agree on E, and every
+// call (HIP-graph replays included) uses new tags.
+//
+// Two families: MAXB = 128 (1-2 waves per workgroup, up to 32 chunks) and
+// MAXB = 512 (4-8 waves, at most 8 chunks; capped at 128 VGPRs so that two
+// workgroups share a CU).  MAXC*NV <= K1*MINT sizes the per-thread gather.
+template <int NS, bool ADD2, int MAXB, int MINT, int MAXC, int WPE>
+__global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
 {
     constexpr int S = NS + 1;
     constexpr int NV = 2 * S;
-    constexpr int CV = 64 * VPT;
+    constexpr int NVP = (NV + 3) / 4 * 4;
+    constexpr int MAXROWS = MAXB / 16;
+    constexpr int K1 = (MAXC * NV + MINT - 1) / MINT; // first-exchange records per thread
+    __shared__ __align__(16) float rows[MAXROWS * NVP];
+    __shared__ __align__(16) float tot[NVP];
+    __shared__ float xch[MAXC * NV];
+    __shared__ float red2[MAXB / 64];
+    __shared__ float ssum_sh;
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nthreads = blockDim.x;
+    const int nw = nthreads >> 6;
     const int C = p.chunks;
-    const int64_t t = blockIdx.x / C;
-    const int chunk = (int)(blockIdx.x - t * C);
+    const int b = blockIdx.x;
+    const int ib = b >> 3;
+    const int64_t t = (int64_t)(ib / C) * 8 + (b & 7);
+    const int chunk = ib - (ib / C) * C;
+    if (t >= p.M)
+        return;
+
+    unsigned* state = p.state + (size_t)t * STATE_STRIDE;
+    const unsigned epoch = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tag1 = 2u * epoch + 1u, tag2 = 2u * epoch + 2u;
+
     const int nvec = p.nvec;
     const int64_t row = t * (int64_t)nvec;
-
-    uint4 k[S][VPT], q[VPT], g[VPT], a[VPT], b[VPT], c[VPT];
-    bool ok[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        const int v = chunk * CV + j * 64 + lane;
-        ok[j] = v < nvec;
-        load_vectors<NS, ADD2>(p, row, v, ok[j], a[j], b[j], c[j], k, j, q[j], g[j]);
-    }
+    uint4 k[S][1], q[1], g[1], a[1], bb[1], c[1];
+    bool ok[1];
+    const int v = chunk * nthreads + tid;
+    ok[0] = v < nvec;
+    load_vectors<NS, ADD2>(p, row, v, ok[0], a[0], bb[0], c[0], k, 0, q[0], g[0]);
     __builtin_amdgcn_sched_barrier(0);
 
     // A1
-    fold_add<ADD2, VPT>(a, b, c, k[NS]);
-#pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        if (ok[j])
-            p.out_prefix[row + chunk * CV + j * 64 + lane] = k[NS][j];
+    fold_add<ADD2, 1>(a, bb, c, k[NS]);
+    if (ok[0])
+        p.out_prefix[row + v] = k[NS][0];
 
-    // A2: thread -> wave; lane i publishes partial i of this chunk
+    // A2: this chunk's partials, then the token's totals through the records
     float part[NV];
-    source_partials<S, VPT>(k, q, ok, part);
-    fence_sources<S, VPT>(k);
-    float mine = 0.f;
+    source_partials<S, 1>(k, q, ok, part);
+    fence_sources<S, 1>(k);
+    block_sums<NV, NVP, MAXROWS>(part, rows, tot, tid, nthreads);
+    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
+    if (tid < NV)
+        publish(&rec1[chunk * REC_STRIDE + tid], tag1, tot[tid]);
+    {
+        // records of all chunks, read as [c][v] flattened over v < NV
+        const unsigned long long* src = rec1;
+        float* dst = xch;
+        const int n = C * NV;
+        unsigned long long w[K1];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const float w = wave_sum(part[i]);
-        mine = (lane == i) ? w : mine;
+        for (int kk = 0; kk < K1; ++kk) {
+            const int e = tid + kk * nthreads;
+            w[kk] = e < n ? peek(&src[(e / NV) * REC_STRIDE + e % NV]) : ((unsigned long long)tag1 << 32);
+        }
+        for (unsigned polls = 0;; ++polls) {
+            bool ready = true;
+#pragma unroll
+            for (int kk = 0; kk < K1; ++kk)
+                ready &= tag_of(w[kk]) == tag1;
+            if (ready)
+                break;
+            if (polls >= p.spin_limit) {
+                atomicAdd(p.timeouts, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int kk = 0; kk < K1; ++kk) {
+                const int e = tid + kk * nthreads;
+                if (e < n && tag_of(w[kk]) != tag1)
+                    w[kk] = peek(&src[(e / NV) * REC_STRIDE + e % NV]);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < K1; ++kk) {
+            const int e = tid + kk * nthreads;
+            if (e < n)
+                dst[e] = __uint_as_float((unsigned)w[kk]);
+        }
     }
-    float* rec = p.part + (size_t)t * C * PART_STRIDE;
-    if (lane < NV)
-        store_agent(&rec[chunk * PART_STRIDE + lane], mine);
-    unsigned* sync = p.sync + (size_t)t * SYNC_STRIDE;
-    token_barrier(sync, (unsigned)C, p.spin_limit, p.timeouts);
-
-    // every workgroup of the token sums the chunk records in chunk order
-    float acc = 0.f;
-    if (lane < NV) {
-        acc = load_agent(&rec[lane]);
+    __syncthreads();
+    if (tid < NV) {
+        float acc = xch[tid];
         for (int cc = 1; cc < C; ++cc)
-            acc += load_agent(&rec[cc * PART_STRIDE + lane]);
+            acc += xch[cc * NV + tid];
+        tot[tid] = acc;
     }
-    float tot[NV], alpha[S];
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        tot[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), i));
+    __syncthreads();
 
     // A3, A4
-    softmax_weights<S>(tot, p.inv_h, p.eps, alpha);
-    float x[VPT][8];
-    const float sx = wave_sum(combine<S, VPT>(k, alpha, ok, x));
-    if (lane == 0)
-        store_agent(&p.part2[(size_t)t * C + chunk], sx);
-    token_barrier(sync, (unsigned)C, p.spin_limit, p.timeouts);
-
-    // A5
-    const float h = lane < C ? load_agent(&p.part2[(size_t)t * C + lane]) : 0.f;
-    const float ssum = wave_sum(h);
-    const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
+    float totr[NV], alpha[S];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j)
-        if (ok[j])
-            p.out_norm[row + chunk * CV + j * 64 + lane] = normalise(x[j], rstd, g[j]);
+    for (int i = 0; i < NV; ++i)
+        totr[i] = tot[i];
+    softmax_weights<S>(totr, p.inv_h, p.eps, alpha);
+    float x[1][8];
+    const float sx = wave_sum(combine<S, 1>(k, alpha, ok, x));
+    if (lane == 0)
+        red2[wave] = sx;
+    __syncthreads();
+
+    // A5: the token's sum of x^2 through the second records
+    unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
+    if (tid == 0) {
+        float s = red2[0];
+        for (int w = 1; w < nw; ++w)
+            s += red2[w];
+        publish(&rec2[chunk], tag2, s);
+    }
+    if (wave == 0) {
+        float* dst = xch; // first-exchange values are consumed (tot) before this point
+        gather_tagged<1>(rec2, C, tag2, dst, lane, 64, p.spin_limit, p.timeouts);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float s = xch[0];
+        for (int cc = 1; cc < C; ++cc)
+            s += xch[cc];
+        ssum_sh = s;
+        if (chunk == 0) // every chunk has published its second record: all have read the epoch
+            __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const float rstd = rsqrtf(ssum_sh * p.inv_h + p.eps);
+    if (ok[0])
+        p.out_norm[row + v] = normalise(x[0], rstd, g[0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,10 +513,10 @@ constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I
     return {{&fwd_wg<I, A2, VPT, MAXB>...}};
 }
 
-template <bool A2, int VPT, int... I>
+template <bool A2, int MAXB, int MINT, int MAXC, int WPE, int... I>
 constexpr std::array<Kernel, sizeof...(I)> split_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_split<I, A2, VPT>...}};
+    return {{&fwd_split<I, A2, MAXB, MINT, MAXC, WPE>...}};
 }
 
 using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
@@ -437,14 +525,18 @@ using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
 const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024>(Seq{}), wg_table<true, 1, 1024>(Seq{})};
 const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512>(Seq{}), wg_table<true, 2, 512>(Seq{})};
 const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512>(Seq{}), wg_table<true, 4, 512>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kSp1[2] = {split_table<false, 1>(Seq{}), split_table<true, 1>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kSp2[2] = {split_table<false, 2>(Seq{}), split_table<true, 2>(Seq{})};
+// split hidden, 1-2 waves per workgroup (up to 32 chunks)
+const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, 64, MAX_CHUNKS, 1>(Seq{}),
+                                                      split_table<true, 128, 64, MAX_CHUNKS, 1>(Seq{})};
+// split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
+const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 256, 8, 4>(Seq{}),
+                                                      split_table<true, 512, 256, 8, 4>(Seq{})};
 
 struct Scratch {
     void* base = nullptr;
-    float* part = nullptr;
-    float* part2 = nullptr;
-    unsigned* sync = nullptr;
+    unsigned long long* rec1 = nullptr;
+    unsigned long long* rec2 = nullptr;
+    unsigned* state = nullptr;
     unsigned* timeouts = nullptr;
 };
 
@@ -454,10 +546,10 @@ Scratch g_scratch[MAX_DEVICES];
 int g_force_variant = 0;
 int g_force_param = 0;
 
-constexpr size_t PART_BYTES = sizeof(float) * MAX_SPLIT_TOKENS * MAX_CHUNKS * PART_STRIDE;
-constexpr size_t PART2_BYTES = sizeof(float) * MAX_SPLIT_TOKENS * MAX_CHUNKS;
-constexpr size_t SYNC_BYTES = sizeof(unsigned) * MAX_SPLIT_TOKENS * SYNC_STRIDE;
-constexpr size_t SCRATCH_BYTES = PART_BYTES + PART2_BYTES + SYNC_BYTES + 256;
+constexpr size_t REC1_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS * REC_STRIDE;
+constexpr size_t REC2_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS;
+constexpr size_t STATE_BYTES = sizeof(unsigned) * MAX_SPLIT_TOKENS * STATE_STRIDE;
+constexpr size_t SCRATCH_BYTES = REC1_BYTES + REC2_BYTES + STATE_BYTES + 256;
 
 // The scratch of the current device, allocated and cleared on first use.
 int scratch_for_current_device(Scratch** out)
@@ -476,10 +568,10 @@ int scratch_for_current_device(Scratch** out)
             return ATTNRES_EHIP;
         }
         char* c = static_cast<char*>(base);
-        s.part = reinterpret_cast<float*>(c);
-        s.part2 = reinterpret_cast<float*>(c + PART_BYTES);
-        s.sync = reinterpret_cast<unsigned*>(c + PART_BYTES + PART2_BYTES);
-        s.timeouts = reinterpret_cast<unsigned*>(c + PART_BYTES + PART2_BYTES + SYNC_BYTES);
+        s.rec1 = reinterpret_cast<unsigned long long*>(c);
+        s.rec2 = reinterpret_cast<unsigned long long*>(c + REC1_BYTES);
+        s.state = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES);
+        s.timeouts = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES + STATE_BYTES);
         s.base = base;
     }
     *out = &s;
@@ -531,11 +623,11 @@ extern "C" int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, cons
         rc = scratch_for_current_device(&sc);
         if (rc != ATTNRES_OK)
             return rc;
-        p.part = sc->part;
-        p.part2 = sc->part2;
-        p.sync = sc->sync;
+        p.rec1 = sc->rec1;
+        p.rec2 = sc->rec2;
+        p.state = sc->state;
         p.timeouts = sc->timeouts;
-        fn = (pl.vpt == 1 ? kSp1 : kSp2)[a2][n_snapshots];
+        fn = (pl.threads <= 128 ? kSpSmall : kSpLarge)[a2][n_snapshots];
     } else {
         fn = (pl.vpt == 1 ? kWg1 : pl.vpt == 2 ? kWg2 : kWg4)[a2][n_snapshots];
     }

@@ -83,15 +83,22 @@ __device__ __forceinline__ float quad_sum(float v)
     return v;
 }
 
-// Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
-// lane.  Four DPP butterflies give every lane the sum of its 16-lane row;
-// the four row sums are then read as scalars and added in a fixed order.
+// Sum over each 16-lane DPP row, returned in all 16 lanes with identical bits.
 // All 64 lanes must be active.
-__device__ __forceinline__ float wave_sum(float v)
+__device__ __forceinline__ float row_sum(float v)
 {
     v = quad_sum(v);
     v = v + dpp<0x141>(v); // row_half_mirror: pairs quads 0-1, 2-3
     v = v + dpp<0x140>(v); // row_mirror: pairs the two halves of a row
+    return v;
+}
+
+// Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
+// lane: the four 16-lane row sums are read as scalars and added in a fixed
+// order.  All 64 lanes must be active.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row_sum(v);
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
@@ -99,49 +106,70 @@ __device__ __forceinline__ float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
-// ---- device-scope loads/stores and the per-token barrier -----------------
+// ---- cross-workgroup exchange --------------------------------------------
+//
+// Workgroups that share a token exchange binary32 partial sums through 64-bit
+// records: the upper word is a tag, the lower word the value.  A record is
+// written and read with single relaxed device-scope atomics, so a reader that
+// sees the expected tag also sees that call's value: no fence (and none of the
+// whole-cache writeback/invalidate that device-scope release/acquire costs on
+// gfx950) is needed.  Tags come from a per-token epoch word that advances once
+// per call (see fwd_split), so records left by earlier calls never match.
 
-__device__ __forceinline__ void store_agent(float* p, float v)
+__device__ __forceinline__ void publish(unsigned long long* rec, unsigned tag, float v)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long w = ((unsigned long long)tag << 32) | __float_as_uint(v);
+    __hip_atomic_store(rec, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float load_agent(const float* p)
+__device__ __forceinline__ unsigned long long peek(const unsigned long long* rec)
 {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(const_cast<unsigned long long*>(rec), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Barrier among the `parties` workgroups that share one token.  Words:
-// sync[0] = arrivals in the current episode, sync[1] = episode number.  The
-// last arriver resets the arrival count and then publishes the next episode
-// with a release; the others spin (acquire) until the episode changes.  Every
-// episode leaves sync[0] == 0, so the words never need clearing between calls
-// (HIP-graph replay included).  The spin is bounded: after `spin_limit`
-// polls the workgroup gives up and bumps *timeouts (a counter the host can
-// read), so a broken launch cannot hang the device.
-__device__ __forceinline__ void token_barrier(unsigned* sync, unsigned parties, unsigned spin_limit,
-                                              unsigned* timeouts)
+__device__ __forceinline__ unsigned tag_of(unsigned long long w) { return (unsigned)(w >> 32); }
+
+// Reads the n records rec[0..n) into out[0..n) (LDS) once each carries `tag`.
+// Thread tid takes entries tid, tid + nthreads, ... (at most K of them); all
+// of its loads are issued together and only the entries not yet tagged are
+// read again.  The wait is bounded: after `spin_limit` rounds the thread gives
+// up, bumps *timeouts and stores what it has, so a broken launch cannot hang.
+template <int K>
+__device__ __forceinline__ void gather_tagged(const unsigned long long* rec, int n, unsigned tag, float* out,
+                                              int tid, int nthreads, unsigned spin_limit, unsigned* timeouts)
 {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned episode = __hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned arrived =
-            __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (arrived == parties - 1) {
-            __hip_atomic_store(&sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            unsigned polls = 0;
-            while (__hip_atomic_load(&sync[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == episode) {
-                if (++polls >= spin_limit) {
-                    __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
+    unsigned long long w[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int e = tid + k * nthreads;
+        w[k] = e < n ? peek(&rec[e]) : ((unsigned long long)tag << 32);
+    }
+    for (unsigned polls = 0;; ++polls) {
+        bool ready = true;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            ready &= tag_of(w[k]) == tag;
+        if (ready)
+            break;
+        if (polls >= spin_limit) {
+            atomicAdd(timeouts, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int e = tid + k * nthreads;
+            if (e < n && tag_of(w[k]) != tag)
+                w[k] = peek(&rec[e]);
         }
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int e = tid + k * nthreads;
+        if (e < n)
+            out[e] = __uint_as_float((unsigned)w[k]);
+    }
 }
 
 } // namespace attnres

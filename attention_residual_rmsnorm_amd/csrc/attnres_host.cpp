@@ -41,20 +41,25 @@ bool plan_wg(int64_t M, int nvec, int vpt, Plan& pl)
     return true;
 }
 
-bool plan_split(int64_t M, int nvec, int vpt, Plan& pl)
+// Split hidden: `waves` (1, 2 or 4..8) waves per workgroup, one vector per thread, C chunks
+// per token; grid = 8 * C * ceil(M / 8) (chunks of a token share an XCD).
+bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
 {
-    if (vpt == 0)
-        vpt = 1;
-    if (vpt != 1 && vpt != 2)
+    if (waves == 0)
+        waves = 2;
+    if (waves < 1 || waves > 8)
         return false;
-    const int chunks = (nvec + 64 * vpt - 1) / (64 * vpt);
-    if (chunks > MAX_CHUNKS || M > MAX_SPLIT_TOKENS)
+    if (waves == 3)
+        return false; // 1-2 waves: up to 32 chunks; 4-8 waves: up to 8 chunks
+    const int threads = 64 * waves;
+    const int chunks = (nvec + threads - 1) / threads;
+    if (chunks > (waves <= 2 ? MAX_CHUNKS : 8) || M > MAX_SPLIT_TOKENS)
         return false;
     pl.variant = 2;
-    pl.vpt = vpt;
-    pl.threads = 64;
+    pl.vpt = 1;
+    pl.threads = threads;
     pl.chunks = chunks;
-    pl.grid = M * chunks;
+    pl.grid = 8 * (int64_t)chunks * ((M + 7) / 8);
     return true;
 }
 
@@ -124,7 +129,7 @@ bool valid_override(int variant, int param)
     switch (variant) {
     case 0: return param == 0;
     case 1: return param == 0 || param == 1 || param == 2 || param == 4;
-    case 2: return param == 0 || param == 1 || param == 2;
+    case 2: return param >= 0 && param <= 8 && param != 3;
     default: return false;
     }
 }
@@ -137,9 +142,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     if (force_variant == 2)
         return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
-    // automatic: one workgroup per token (measured faster than the split-hidden
-    // kernel at every batch size: its cross-workgroup barriers cost more than
-    // spreading a token over CUs saves)
+    // automatic, by measurement on MI355X at H = 7168: up to 64 tokens the
+    // call is latency-bound and spreading each token over 4-wave chunks on
+    // several CUs wins; beyond that one workgroup per token (no exchange) wins.
+    if (M <= SPLIT_MAX_AUTO_TOKENS && plan_split(M, nvec, 4, pl))
+        return ATTNRES_OK;
     if (plan_wg(M, nvec, 0, pl))
         return ATTNRES_OK;
     return plan_split(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;

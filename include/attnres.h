@@ -93,9 +93,10 @@ extern "C" {
  *
  * All device pointers must be 16-byte aligned.  The caller owns every buffer
  * and must keep it alive until the stream work completes.  The library owns a
- * per-device scratch buffer used by the split-hidden kernel (partials and
- * barrier counters, which reset themselves); it is allocated on the first
- * call on a device, or by attnres_init().  Calls that use it on the same
+ * per-device scratch buffer used by the split-hidden kernel (tagged partial
+ * records and one epoch word per token slot; nothing needs clearing between
+ * calls, HIP-graph replays included); it is allocated on the first call that
+ * needs it on a device, or by attnres_init().  Calls that use it on the same
  * device must be ordered with respect to each other (same stream, or
  * synchronised): two overlapping calls on different streams of one device
  * race on it.
@@ -143,10 +144,11 @@ int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunk
 
 /*
  * attnres_set_variant -- process-wide dispatch override for tests and
- * benchmarks: variant 0 = automatic, 1 = workgroup per token (vectors per
- * thread = param: 0 automatic, or 1, 2, 4), 2 = split hidden (vectors per
- * thread = param: 0 automatic, or 1, 2).  Not thread-safe with concurrent
- * calls.  Returns ATTNRES_OK or ATTNRES_EINVAL.
+ * benchmarks: variant 0 = automatic (param 0); 1 = workgroup per token, param =
+ * 16-byte vectors per thread (0 automatic, or 1, 2, 4); 2 = split hidden, param
+ * = waves per workgroup (0 automatic, or 1, 2, 4..8).  A size the forced variant
+ * cannot serve makes the fused call return ATTNRES_EINVAL.  Not thread-safe
+ * with concurrent calls.  Returns ATTNRES_OK or ATTNRES_EINVAL.
  */
 int attnres_set_variant(int variant, int param);
 

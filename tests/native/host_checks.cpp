@@ -57,7 +57,7 @@ int main()
             }
             Plan pl;
             for (int fv = 0; fv <= 2; ++fv)
-                for (int fp = 0; fp <= 4; ++fp) {
+                for (int fp = 0; fp <= 9; ++fp) {
                     if (!valid_override(fv, fp))
                         continue;
                     for (int64_t m : {int64_t(1), int64_t(8), int64_t(64), int64_t(65), int64_t(512),
@@ -71,7 +71,9 @@ int main()
                                 EXPECT((int64_t)pl.threads * pl.vpt * pl.chunks * 8 >= h);
                                 if (pl.variant == 2)
                                     EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
-                                           pl.grid == m * pl.chunks);
+                                           pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&
+                                           pl.threads <= 512 &&
+                                           pl.chunks <= (pl.threads <= 128 ? MAX_CHUNKS : 8));
                             } else {
                                 EXPECT(fv != 0 || h > 8192); // automatic always finds a plan
                             }

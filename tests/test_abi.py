@@ -130,7 +130,9 @@ def test_bf16_add_validation():
 
 def test_plan_is_pure_and_sane():
     v, c, t = ar.attnres_plan(1, 12, 7168)
-    assert c * t * 8 * (2 if v == 1 else 1) >= 7168
+    assert (v, c, t) == (2, 4, 256)
+    assert ar.attnres_plan(64, 12, 7168)[0] == 2
+    assert ar.attnres_plan(65, 12, 7168)[0] == 1
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
     with pytest.raises(ar.AttnResError):
@@ -143,11 +145,16 @@ def test_set_variant_validation():
     lib = ar.library()
     assert lib.attnres_set_variant(3, 0) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(1, 3) == ar.ATTNRES_EINVAL
-    assert lib.attnres_set_variant(2, 4) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(2, 9) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(2, 3) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(0, 1) == ar.ATTNRES_EINVAL
     try:
         ar.attnres_set_variant(2, 0)
         assert ar.attnres_plan(256, 4, 7168)[0] == 2
+        ar.attnres_set_variant(2, 7)
+        assert ar.attnres_plan(1, 4, 7168) == (2, 2, 448)
+        ar.attnres_set_variant(2, 1)
+        assert ar.attnres_plan(3, 4, 7168) == (2, 14, 64)
         ar.attnres_set_variant(1, 1)
         assert ar.attnres_plan(1, 4, 7168) == (1, 1, 896)
     finally:

@@ -20,9 +20,10 @@ from attention_residual_rmsnorm_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-# (variant, vectors per thread); 0 = automatic
-VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2)]
-VID = ["auto", "W1", "W2", "S1", "S2"]
+# (variant, param): 0 = automatic; W = workgroup per token with param vectors
+# per thread; S = split hidden with param waves per workgroup
+VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7)]
+VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w"]
 
 
 def say(*a):
