@@ -13,10 +13,12 @@
 //
 // Two kernels, both HBM-bound streaming kernels (no dense contraction, so no
 // MFMA):
-//   W  one workgroup per token: the token's whole row set is held in
-//      registers (N+1 sources x 8 bf16 x VPT 16-byte vectors per thread), the
-//      2(N+1) partials are reduced wave-wide on DPP and across waves in LDS.
-//      No inter-workgroup communication.  Used when there are many tokens.
+//   W  one workgroup per token: all of the token's loads are in flight at
+//      once (N+1 sources x VPT 16-byte vectors per thread, in registers) and
+//      the sources are mixed group by group as they arrive, under a running
+//      softmax maximum and sum; each group's partials are summed on DPP
+//      within rows and by one wave across rows.  No inter-workgroup
+//      communication.  Used when there are many tokens.
 //   S  split hidden: C workgroups per token, each owning a contiguous chunk of
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
@@ -153,32 +155,39 @@ __device__ __forceinline__ void fold_add(const uint4* a, const uint4* b, const u
     }
 }
 
-// A2 for one thread: per-source sums over its VPT*8 elements in a fixed order
-// (vector by vector, pair by pair, on v_dot2_f32_bf16); vectors outside the
-// row (ok[j] false) contribute zero.
+// A2 for one source and one thread: sum k^2 and q.k over the thread's VPT
+// vectors in a fixed order (vector by vector, pair by pair, on
+// v_dot2_f32_bf16); vectors outside the row (ok[j] false) contribute zero.
+template <int VPT>
+__device__ __forceinline__ float2 source_partial(const uint4 (&x)[VPT], const uint4* q, const bool* ok)
+{
+    float ss = 0.f, qd = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        float ssj = dot2_bf16(x[j].x, x[j].x, 0.f);
+        ssj = dot2_bf16(x[j].y, x[j].y, ssj);
+        ssj = dot2_bf16(x[j].z, x[j].z, ssj);
+        ssj = dot2_bf16(x[j].w, x[j].w, ssj);
+        float qdj = dot2_bf16(q[j].x, x[j].x, 0.f);
+        qdj = dot2_bf16(q[j].y, x[j].y, qdj);
+        qdj = dot2_bf16(q[j].z, x[j].z, qdj);
+        qdj = dot2_bf16(q[j].w, x[j].w, qdj);
+        ss += ok[j] ? ssj : 0.f;
+        qd += ok[j] ? qdj : 0.f;
+    }
+    return make_float2(ss, qd);
+}
+
+// A2 for every source: part[2s] = sum k_s^2, part[2s+1] = q.k_s.
 template <int S, int VPT>
 __device__ __forceinline__ void source_partials(const uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
                                                 float* part)
 {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        float ss = 0.f, qd = 0.f;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const uint4 x = k[s][j];
-            float ssj = dot2_bf16(x.x, x.x, 0.f);
-            ssj = dot2_bf16(x.y, x.y, ssj);
-            ssj = dot2_bf16(x.z, x.z, ssj);
-            ssj = dot2_bf16(x.w, x.w, ssj);
-            float qdj = dot2_bf16(q[j].x, x.x, 0.f);
-            qdj = dot2_bf16(q[j].y, x.y, qdj);
-            qdj = dot2_bf16(q[j].z, x.z, qdj);
-            qdj = dot2_bf16(q[j].w, x.w, qdj);
-            ss += ok[j] ? ssj : 0.f;
-            qd += ok[j] ? qdj : 0.f;
-        }
-        part[2 * s] = ss;
-        part[2 * s + 1] = qd;
+        const float2 v = source_partial<VPT>(k[s], q, ok);
+        part[2 * s] = v.x;
+        part[2 * s + 1] = v.y;
     }
 }
 
@@ -222,31 +231,64 @@ __device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float
     __syncthreads();
 }
 
-// A4 for one thread: x = sum_s alpha_s k_s (fixed source order), and the
-// thread's share of sum x^2 (vectors outside the row contribute zero).
+// 32-bit word w (0..3) of a 16-byte vector: elements 2w (low half) and 2w+1.
+__device__ __forceinline__ uint32_t word(const uint4& v, int w)
+{
+    return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
+// A4 for one thread: x = sum_s alpha_s k_s, and the thread's share of sum x^2
+// (vectors outside the row contribute zero).  Sources are taken in pairs
+// (s, s+1): one byte permute puts element e of both into one word, and
+// v_dot2_f32_bf16 adds k_s*a_s + k_s+1*a_s+1 in one instruction.  The
+// weights go in as two bf16 parts each (hi = bf16(a), lo = bf16(a - hi)), so
+// they keep 16 significant bits; the bf16 products are exact in binary32.  An
+// odd last source is added with a binary32 fma.  Fixed order: pairs in
+// source order (hi part, then lo part), then the odd source.
 template <int S, int VPT>
 __device__ __forceinline__ float combine(const uint4 (&k)[S][VPT], const float* alpha, const bool* ok,
                                          float (&x)[VPT][8])
 {
+    constexpr int NP = S / 2;
+    uint32_t wh[NP > 0 ? NP : 1], wl[NP > 0 ? NP : 1];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const float a0 = alpha[2 * p], a1 = alpha[2 * p + 1];
+        wh[p] = pack_bf16(a0, a1);
+        wl[p] = pack_bf16(a0 - lo_f32(wh[p]), a1 - hi_f32(wh[p]));
+    }
     float sx = 0.f;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         float sxj = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float acc = alpha[0] * elem(k[0][j], e);
+        for (int w = 0; w < 4; ++w) {
+            float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-            for (int s = 1; s < S; ++s)
-                acc = __builtin_fmaf(alpha[s], elem(k[s][j], e), acc);
-            x[j][e] = acc;
-            sxj = __builtin_fmaf(acc, acc, sxj);
+            for (int p = 0; p < NP; ++p) {
+                const uint32_t A = word(k[2 * p][j], w), B = word(k[2 * p + 1][j], w);
+                const uint32_t e0 = __builtin_amdgcn_perm(B, A, 0x05040100u); // (A.lo, B.lo)
+                const uint32_t e1 = __builtin_amdgcn_perm(B, A, 0x07060302u); // (A.hi, B.hi)
+                x0 = dot2_bf16(e0, wh[p], x0);
+                x0 = dot2_bf16(e0, wl[p], x0);
+                x1 = dot2_bf16(e1, wh[p], x1);
+                x1 = dot2_bf16(e1, wl[p], x1);
+            }
+            if (S & 1) {
+                const uint32_t A = word(k[S - 1][j], w);
+                x0 = __builtin_fmaf(alpha[S - 1], lo_f32(A), x0);
+                x1 = __builtin_fmaf(alpha[S - 1], hi_f32(A), x1);
+            }
+            x[j][2 * w] = x0;
+            x[j][2 * w + 1] = x1;
+            sxj = __builtin_fmaf(x0, x0, sxj);
+            sxj = __builtin_fmaf(x1, x1, sxj);
         }
         sx += ok[j] ? sxj : 0.f;
     }
     return sx;
 }
 
-// A5 output of one vector: bf16((x * rstd) * gamma).
 __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, const uint4& g)
 {
     float y[8];
@@ -261,16 +303,215 @@ __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, cons
 // Kernel W: one workgroup per token (grid-stride over tokens).  Thread `tid`
 // owns vectors tid + j*blockDim.x, j < VPT, of the row (coalesced 16-byte
 // loads).  blockDim.x is a multiple of 64, at most MAXB.
-template <int NS, bool ADD2, int VPT, int MAXB>
+//
+// All of the token's loads are issued at once, in the order query, gamma,
+// prefix, add, add2, snapshot 0..N-1; the hardware returns them in that
+// order.  The sources are then consumed in that order, p' first, in groups
+// of up to G (the last source alone): A2 for the group, its token-wide sums,
+// its logits, and its share of A4 under a running maximum and running sum of
+// the softmax (what was gathered so far is rescaled when the maximum grows).
+// A group's work runs while later sources are still in flight, so after the
+// last load lands only one source's step and A5 remain.
+
+// Sources in arrival order: k[0] = p', k[1 + s] = snapshot s.
+template <int NS, bool ADD2, int VPT>
+__device__ __forceinline__ void load_token(const Params& p, int64_t row, const int (&vc)[VPT], uint4 (&q)[VPT],
+                                           uint4 (&g)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT], uint4 (&c)[VPT],
+                                           uint4 (&k)[NS + 1][VPT])
+{
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        q[j] = p.query[vc[j]];
+        g[j] = p.gamma[vc[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        a[j] = load_stream(&p.prefix[row + vc[j]]);
+        b[j] = load_stream(&p.add[row + vc[j]]);
+        c[j] = ADD2 ? load_stream(&p.add2[row + vc[j]]) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            k[1 + s][j] = load_stream(&p.snap[s][row + vc[j]]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__device__ __forceinline__ float uniform(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// 1/sqrt(v) on v_rsq_f32 (about 1 ulp) for v >= eps > 0: never a denormal
+// argument, so the library's rescaling around it is not needed.
+__device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v); }
+
+// Workgroup totals of NV <= 8 per-thread values in two levels.  Each 16-lane
+// row is summed on DPP and lane 0 of the row stores its NV sums (row r at
+// rows[8r..8r+7]; the 64 - blockDim.x/16 rows of absent waves hold zeros);
+// after a barrier wave 0 adds the rows: lane l takes value l/8 over rows
+// l%8, l%8 + 8, ..., l%8 + 56 in order, three DPP steps add the 8 lanes of a
+// value, and lane 8v stores tot[v].  After a second barrier every thread
+// reads the same bits.
+template <int NV>
+__device__ __forceinline__ void group_sums(float (&part)[NV], float* rows, float* tot, int tid)
+{
+    static_assert(NV >= 1 && NV <= 8, "at most 8 values per group");
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        part[i] = row_sum(part[i]);
+    if ((tid & 15) == 0) {
+        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * 8);
+        r[0] = make_float4(part[0], 1 < NV ? part[1 % NV] : 0.f, 2 < NV ? part[2 % NV] : 0.f,
+                           3 < NV ? part[3 % NV] : 0.f);
+        if (NV > 4)
+            r[1] = make_float4(4 < NV ? part[4 % NV] : 0.f, 5 < NV ? part[5 % NV] : 0.f,
+                               6 < NV ? part[6 % NV] : 0.f, 7 < NV ? part[7 % NV] : 0.f);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // lanes of values v >= NV add stale entries, but only among themselves
+        const int v = tid >> 3, r0 = tid & 7;
+        const float* base = rows + r0 * 8 + v;
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t[i] = base[64 * i];
+        float acc = t[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            acc += t[i];
+        acc = acc + dpp<0xb1>(acc);  // quad_perm [1,0,3,2]
+        acc = acc + dpp<0x4e>(acc);  // quad_perm [2,3,0,1]
+        acc = acc + dpp<0x141>(acc); // row_half_mirror: the two quads of each 8 lanes
+        if (r0 == 0 && v < NV)
+            tot[v] = acc;
+    }
+    __syncthreads();
+}
+
+// Running softmax state of one token: x = sum_s e^(z_s - m) k_s and
+// den = sum_s e^(z_s - m) over the sources so far, m their largest logit.
+// z, m and den hold the same bits in every lane (uniform branches).
+template <int VPT>
+struct Mix {
+    float x[VPT][8];
+    float m, den;
+};
+
+// A2-A4 for one group of n consecutive sources ks[0..n).
+template <int n, int VPT, bool FIRST>
+__device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q, const bool* ok, Mix<VPT>& mx,
+                                          float* rows, float* tot, const Params& p, int tid)
+{
+    float part[2 * n];
+#pragma unroll
+    for (int s = 0; s < n; ++s) {
+        const float2 v = source_partial<VPT>(ks[s], q, ok);
+        part[2 * s] = v.x;
+        part[2 * s + 1] = v.y;
+    }
+    group_sums<2 * n>(part, rows, tot, tid);
+    float z[n];
+#pragma unroll
+    for (int s = 0; s < n; ++s)
+        z[s] = uniform(rsq(tot[2 * s] * p.inv_h + p.eps) * tot[2 * s + 1]);
+    float zmax = z[0];
+#pragma unroll
+    for (int s = 1; s < n; ++s)
+        zmax = fmaxf(zmax, z[s]);
+    if (FIRST) {
+        mx.m = zmax;
+        mx.den = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx.x[j][e] = 0.f;
+    } else if (zmax > mx.m) {
+        const float r = __expf(mx.m - zmax);
+        mx.den = mx.den * r;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx.x[j][e] = mx.x[j][e] * r;
+        mx.m = zmax;
+    }
+    float w[n];
+#pragma unroll
+    for (int s = 0; s < n; ++s) {
+        w[s] = __expf(z[s] - mx.m);
+        mx.den = mx.den + w[s];
+    }
+    // x += sum_s w_s k_s: sources in pairs on v_dot2_f32_bf16 with each weight
+    // split into two bf16 parts (hi = bf16(w), lo = bf16(w - hi), 16
+    // significant bits; bf16 products are exact in binary32), an odd last
+    // source by binary32 fma.  Fixed order.
+    constexpr int NP = n / 2;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+        const uint32_t wh = pack_bf16(w[2 * pp], w[2 * pp + 1]);
+        const uint32_t wl = pack_bf16(w[2 * pp] - lo_f32(wh), w[2 * pp + 1] - hi_f32(wh));
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) {
+                const uint32_t A = word(ks[2 * pp][j], ww), B = word(ks[2 * pp + 1][j], ww);
+                const uint32_t e0 = __builtin_amdgcn_perm(B, A, 0x05040100u); // (A.lo, B.lo)
+                const uint32_t e1 = __builtin_amdgcn_perm(B, A, 0x07060302u); // (A.hi, B.hi)
+                float x0 = mx.x[j][2 * ww], x1 = mx.x[j][2 * ww + 1];
+                x0 = dot2_bf16(e0, wh, x0);
+                x0 = dot2_bf16(e0, wl, x0);
+                x1 = dot2_bf16(e1, wh, x1);
+                x1 = dot2_bf16(e1, wl, x1);
+                mx.x[j][2 * ww] = x0;
+                mx.x[j][2 * ww + 1] = x1;
+            }
+    }
+    if (n & 1) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                mx.x[j][e] = __builtin_fmaf(w[n - 1], elem(ks[n - 1][j], e), mx.x[j][e]);
+    }
+    // materialise x here: otherwise the compiler sinks this work past the next
+    // group's wait, out of the window in which loads are in flight
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        asm volatile("" : "+v"(mx.x[j][0]), "+v"(mx.x[j][1]), "+v"(mx.x[j][2]), "+v"(mx.x[j][3]),
+                     "+v"(mx.x[j][4]), "+v"(mx.x[j][5]), "+v"(mx.x[j][6]), "+v"(mx.x[j][7]), "+v"(mx.den));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The groups over S sources: G at a time, the last source on its own.  Group
+// gi uses LDS slot gi % 2 (a slot is written again two groups later, after
+// every thread has passed the barriers that end its readers' use).
+template <int S, int G, int VPT, int G0, int GI>
+__device__ __forceinline__ void mix_groups(const uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
+                                           Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8],
+                                           const Params& p, int tid)
+{
+    if constexpr (G0 < S) {
+        constexpr int LAST = S - 1;
+        constexpr int n = G0 == LAST ? 1 : (G < LAST - G0 ? G : LAST - G0);
+        mix_group<n, VPT, G0 == 0>(&k[G0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
+        mix_groups<S, G, VPT, G0 + n, GI + 1>(k, q, ok, mx, rows, tot, p, tid);
+    }
+}
+
+template <int NS, bool ADD2, int VPT, int MAXB, int G>
 __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 {
-    constexpr int S = NS + 1;                // sources: snapshots, then the updated prefix
-    constexpr int NV = 2 * S;                // partials per token
-    constexpr int NVP = (NV + 3) / 4 * 4;    // LDS record length
+    constexpr int S = NS + 1;
     constexpr int MAXW = MAXB / 64;
-    constexpr int MAXROWS = MAXB / 16;
-    __shared__ __align__(16) float rows[MAXROWS * NVP];
-    __shared__ __align__(16) float tot[NVP];
+    static_assert(MAXB / 16 <= 64, "rows of one group slot");
+    __shared__ __align__(16) float rows[2][64 * 8];
+    __shared__ __align__(16) float tot[2][8];
     __shared__ float red2[MAXW];
 
     const int tid = threadIdx.x;
@@ -279,55 +520,65 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
     const int nthreads = blockDim.x;
     const int nw = nthreads >> 6;
     const int nvec = p.nvec;
+    // entries of absent waves stay zero (ordered before use by the first barrier)
+    if (tid < MAXW && tid >= nw)
+        red2[tid] = 0.f;
+    for (int i = tid; i < 2 * 64 * 8; i += nthreads)
+        if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
+            rows[i >> 9][i & 511] = 0.f;
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
         const int64_t row = t * (int64_t)nvec;
         uint4 k[S][VPT], q[VPT], g[VPT], a[VPT], b[VPT], c[VPT];
         bool ok[VPT];
+        int vc[VPT];
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int v = tid + j * nthreads;
             ok[j] = v < nvec;
-            load_vectors<NS, ADD2>(p, row, v, ok[j], a[j], b[j], c[j], k, j, q[j], g[j]);
+            vc[j] = ok[j] ? v : nvec - 1; // past the row: reread the last vector, never stored
         }
+        load_token<NS, ADD2, VPT>(p, row, vc, q, g, a, b, c, k);
         // keep every load above this point: nothing that waits on a load may be
         // scheduled between them
         __builtin_amdgcn_sched_barrier(0);
 
         // A1
-        fold_add<ADD2, VPT>(a, b, c, k[NS]);
+        fold_add<ADD2, VPT>(a, b, c, k[0]);
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
             if (ok[j])
-                p.out_prefix[row + tid + j * nthreads] = k[NS][j];
+                p.out_prefix[row + tid + j * nthreads] = k[0][j];
 
-        // A2: per thread, then over the workgroup
-        float part[NV];
-        source_partials<S, VPT>(k, q, ok, part);
-        fence_sources<S, VPT>(k);
-        block_sums<NV, NVP, MAXROWS>(part, rows, tot, tid, nthreads);
+        // A2-A4
+        Mix<VPT> mx;
+        mix_groups<S, G, VPT, 0, 0>(k, q, ok, mx, rows, tot, p, tid);
 
-        // A3
-        float totr[NV], alpha[S];
+        // A4's division by den folded into A5: the mixture is x/den, so
+        // out = x * scale * gamma with scale = 1/(den*sqrt(mean((x/den)^2) + eps))
+        //                                    = 1/sqrt(mean(x^2) + eps*den^2).
+        float sx = 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            totr[i] = tot[i];
-        softmax_weights<S>(totr, p.inv_h, p.eps, alpha);
-
-        // A4 + A5
-        float x[VPT][8];
-        const float sx = wave_sum(combine<S, VPT>(k, alpha, ok, x));
+        for (int j = 0; j < VPT; ++j) {
+            float sxj = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sxj = __builtin_fmaf(mx.x[j][e], mx.x[j][e], sxj);
+            sx += ok[j] ? sxj : 0.f;
+        }
+        sx = wave_sum(sx);
         if (lane == 0)
             red2[wave] = sx;
         __syncthreads();
         float ssum = red2[0];
-        for (int w = 1; w < nw; ++w)
+#pragma unroll
+        for (int w = 1; w < MAXW; ++w)
             ssum += red2[w];
-        const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
+        const float scale = rsq(ssum * p.inv_h + (p.eps * mx.den) * mx.den);
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
             if (ok[j])
-                p.out_norm[row + tid + j * nthreads] = normalise(x[j], rstd, g[j]);
+                p.out_norm[row + tid + j * nthreads] = normalise(mx.x[j], scale, g[j]);
         __syncthreads(); // LDS reuse by the next token
     }
 }
@@ -507,10 +758,10 @@ __global__ __launch_bounds__(256) void bf16_add_kernel(const uint4* a, const uin
 
 using Kernel = void (*)(Params);
 
-template <bool A2, int VPT, int MAXB, int... I>
+template <bool A2, int VPT, int MAXB, int G, int... I>
 constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_wg<I, A2, VPT, MAXB>...}};
+    return {{&fwd_wg<I, A2, VPT, MAXB, G>...}};
 }
 
 template <bool A2, int MAXB, int MINT, int MAXC, int WPE, int... I>
@@ -522,9 +773,13 @@ constexpr std::array<Kernel, sizeof...(I)> split_table(std::integer_sequence<int
 using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
 
 // [add2][N]
-const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024>(Seq{}), wg_table<true, 1, 1024>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512>(Seq{}), wg_table<true, 2, 512>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512>(Seq{}), wg_table<true, 4, 512>(Seq{})};
+constexpr int WG_GROUP = 4; // sources per reduction group in kernel W
+const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024, WG_GROUP>(Seq{}),
+                                                  wg_table<true, 1, 1024, WG_GROUP>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GROUP>(Seq{}),
+                                                  wg_table<true, 2, 512, WG_GROUP>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512, WG_GROUP>(Seq{}),
+                                                  wg_table<true, 4, 512, WG_GROUP>(Seq{})};
 // split hidden, 1-2 waves per workgroup (up to 32 chunks)
 const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, 64, MAX_CHUNKS, 1>(Seq{}),
                                                       split_table<true, 128, 64, MAX_CHUNKS, 1>(Seq{})};
