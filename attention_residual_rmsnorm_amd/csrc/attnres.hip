@@ -68,32 +68,6 @@ struct Params {
     unsigned spin_limit;
 };
 
-// Softmax weights from the reduced partials tot[2s] = sum k^2, tot[2s+1] = q.k.
-template <int S>
-__device__ __forceinline__ void softmax_weights(const float* tot, float inv_h, float eps, float* alpha)
-{
-    float z[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float rstd = rsqrtf(tot[2 * s] * inv_h + eps);
-        z[s] = rstd * tot[2 * s + 1];
-    }
-    float zmax = z[0];
-#pragma unroll
-    for (int s = 1; s < S; ++s)
-        zmax = fmaxf(zmax, z[s]);
-    float sum = 0.f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        alpha[s] = __expf(z[s] - zmax);
-        sum += alpha[s];
-    }
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-        alpha[s] = alpha[s] * inv;
-}
-
 // A 16-byte load with the non-temporal hint, for the [M,H] streams: a decode
 // step reads each of them once, and between two calls of the op the layer in
 // between streams far more than the caches hold, so keeping these lines would
@@ -600,18 +574,18 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 //
 // Two families: MAXB = 128 (1-2 waves per workgroup, up to 32 chunks) and
 // MAXB = 512 (4-8 waves, at most 8 chunks; capped at 128 VGPRs so that two
-// workgroups share a CU).  MAXC*NV <= K1*MINT sizes the per-thread gather.
-template <int NS, bool ADD2, int MAXB, int MINT, int MAXC, int WPE>
+// workgroups share a CU).
+template <int NS, bool ADD2, int MAXB, int MAXC, int WPE>
 __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
 {
     constexpr int S = NS + 1;
     constexpr int NV = 2 * S;
     constexpr int NVP = (NV + 3) / 4 * 4;
     constexpr int MAXROWS = MAXB / 16;
-    constexpr int K1 = (MAXC * NV + MINT - 1) / MINT; // first-exchange records per thread
+    static_assert(S <= 16 && MAXC <= 64, "one lane per source in a row, one lane per chunk");
     __shared__ __align__(16) float rows[MAXROWS * NVP];
     __shared__ __align__(16) float tot[NVP];
-    __shared__ float xch[MAXC * NV];
+    __shared__ float alpha_sh[16];
     __shared__ float red2[MAXB / 64];
     __shared__ float ssum_sh;
 
@@ -654,21 +628,29 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
     if (tid < NV)
         publish(&rec1[chunk * REC_STRIDE + tid], tag1, tot[tid]);
-    {
-        // records of all chunks, read as [c][v] flattened over v < NV
-        const unsigned long long* src = rec1;
-        float* dst = xch;
-        const int n = C * NV;
-        unsigned long long w[K1];
+
+    // A3 in wave 0.  Lane l takes source s = l % 16 and chunks l/16, l/16 + 4,
+    // ...: all of its record loads are issued together, those not yet tagged
+    // are read again (bounded wait).  The four rows' sums are then added in
+    // row order, so every lane of source s (and every workgroup of the token)
+    // holds the same totals; the logits, their maximum and the exponentials'
+    // sum are taken across the 16 lanes of a row, and row 0 writes alpha.
+    if (wave == 0) {
+        constexpr int KC = (MAXC + 3) / 4;
+        const int s = lane & 15, c0 = lane >> 4;
+        const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
+        unsigned long long w[2 * KC];
 #pragma unroll
-        for (int kk = 0; kk < K1; ++kk) {
-            const int e = tid + kk * nthreads;
-            w[kk] = e < n ? peek(&src[(e / NV) * REC_STRIDE + e % NV]) : ((unsigned long long)tag1 << 32);
+        for (int kk = 0; kk < KC; ++kk) {
+            const int cc = c0 + 4 * kk;
+            const bool use = s < S && cc < C;
+            w[2 * kk] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s]) : ready_zero;
+            w[2 * kk + 1] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s + 1]) : ready_zero;
         }
         for (unsigned polls = 0;; ++polls) {
             bool ready = true;
 #pragma unroll
-            for (int kk = 0; kk < K1; ++kk)
+            for (int kk = 0; kk < 2 * KC; ++kk)
                 ready &= tag_of(w[kk]) == tag1;
             if (ready)
                 break;
@@ -678,60 +660,69 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             }
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-            for (int kk = 0; kk < K1; ++kk) {
-                const int e = tid + kk * nthreads;
-                if (e < n && tag_of(w[kk]) != tag1)
-                    w[kk] = peek(&src[(e / NV) * REC_STRIDE + e % NV]);
+            for (int kk = 0; kk < KC; ++kk) {
+                const int cc = c0 + 4 * kk;
+                if (s < S && cc < C) {
+                    if (tag_of(w[2 * kk]) != tag1)
+                        w[2 * kk] = peek(&rec1[cc * REC_STRIDE + 2 * s]);
+                    if (tag_of(w[2 * kk + 1]) != tag1)
+                        w[2 * kk + 1] = peek(&rec1[cc * REC_STRIDE + 2 * s + 1]);
+                }
             }
         }
+        float ss = 0.f, qd = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < K1; ++kk) {
-            const int e = tid + kk * nthreads;
-            if (e < n)
-                dst[e] = __uint_as_float((unsigned)w[kk]);
+        for (int kk = 0; kk < KC; ++kk) {
+            ss += __uint_as_float((unsigned)w[2 * kk]);
+            qd += __uint_as_float((unsigned)w[2 * kk + 1]);
         }
-    }
-    __syncthreads();
-    if (tid < NV) {
-        float acc = xch[tid];
-        for (int cc = 1; cc < C; ++cc)
-            acc += xch[cc * NV + tid];
-        tot[tid] = acc;
+        ss = ((__shfl(ss, s) + __shfl(ss, s + 16)) + __shfl(ss, s + 32)) + __shfl(ss, s + 48);
+        qd = ((__shfl(qd, s) + __shfl(qd, s + 16)) + __shfl(qd, s + 32)) + __shfl(qd, s + 48);
+        const float z = s < S ? rsqrtf(ss * p.inv_h + p.eps) * qd : -INFINITY;
+        const float zmax = row_max(z);
+        const float e = s < S ? __expf(z - zmax) : 0.f;
+        const float den = row_sum(e);
+        if (lane < S)
+            alpha_sh[lane] = e * (1.0f / den);
     }
     __syncthreads();
 
-    // A3, A4
-    float totr[NV], alpha[S];
+    // A4
+    float alpha[S];
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-        totr[i] = tot[i];
-    softmax_weights<S>(totr, p.inv_h, p.eps, alpha);
+    for (int i = 0; i < S; ++i)
+        alpha[i] = alpha_sh[i];
     float x[1][8];
     const float sx = wave_sum(combine<S, 1>(k, alpha, ok, x));
     if (lane == 0)
         red2[wave] = sx;
     __syncthreads();
 
-    // A5: the token's sum of x^2 through the second records
+    // A5: the token's sum of x^2 through the second records, gathered by wave 0
+    // (lane c reads chunk c's record) and added on DPP
     unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
-    if (tid == 0) {
-        float s = red2[0];
-        for (int w = 1; w < nw; ++w)
-            s += red2[w];
-        publish(&rec2[chunk], tag2, s);
-    }
     if (wave == 0) {
-        float* dst = xch; // first-exchange values are consumed (tot) before this point
-        gather_tagged<1>(rec2, C, tag2, dst, lane, 64, p.spin_limit, p.timeouts);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float s = xch[0];
-        for (int cc = 1; cc < C; ++cc)
-            s += xch[cc];
-        ssum_sh = s;
-        if (chunk == 0) // every chunk has published its second record: all have read the epoch
-            __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            float s2 = red2[0];
+            for (int w = 1; w < nw; ++w)
+                s2 += red2[w];
+            publish(&rec2[chunk], tag2, s2);
+        }
+        unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
+        for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
+            if (polls >= p.spin_limit) {
+                atomicAdd(p.timeouts, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w2 = peek(&rec2[lane]);
+        }
+        const float tot2 = wave_sum(__uint_as_float((unsigned)w2));
+        if (lane == 0) {
+            ssum_sh = tot2;
+            if (chunk == 0) // every chunk has published its second record: all have read the epoch
+                __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     const float rstd = rsqrtf(ssum_sh * p.inv_h + p.eps);
@@ -764,10 +755,10 @@ constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I
     return {{&fwd_wg<I, A2, VPT, MAXB, G>...}};
 }
 
-template <bool A2, int MAXB, int MINT, int MAXC, int WPE, int... I>
+template <bool A2, int MAXB, int MAXC, int WPE, int... I>
 constexpr std::array<Kernel, sizeof...(I)> split_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_split<I, A2, MAXB, MINT, MAXC, WPE>...}};
+    return {{&fwd_split<I, A2, MAXB, MAXC, WPE>...}};
 }
 
 using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
@@ -781,11 +772,11 @@ const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GRO
 const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512, WG_GROUP>(Seq{}),
                                                   wg_table<true, 4, 512, WG_GROUP>(Seq{})};
 // split hidden, 1-2 waves per workgroup (up to 32 chunks)
-const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, 64, MAX_CHUNKS, 1>(Seq{}),
-                                                      split_table<true, 128, 64, MAX_CHUNKS, 1>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, MAX_CHUNKS, 1>(Seq{}),
+                                                      split_table<true, 128, MAX_CHUNKS, 1>(Seq{})};
 // split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
-const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 256, 8, 4>(Seq{}),
-                                                      split_table<true, 512, 256, 8, 4>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8, 4>(Seq{}),
+                                                      split_table<true, 512, 8, 4>(Seq{})};
 
 struct Scratch {
     void* base = nullptr;

@@ -93,6 +93,17 @@ __device__ __forceinline__ float row_sum(float v)
     return v;
 }
 
+// Maximum over each 16-lane DPP row, returned in all 16 lanes.  All 64 lanes
+// must be active.
+__device__ __forceinline__ float row_max(float v)
+{
+    v = fmaxf(v, dpp<0xb1>(v));
+    v = fmaxf(v, dpp<0x4e>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return v;
+}
+
 // Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
 // lane: the four 16-lane row sums are read as scalars and added in a fixed
 // order.  All 64 lanes must be active.
@@ -129,47 +140,5 @@ __device__ __forceinline__ unsigned long long peek(const unsigned long long* rec
 }
 
 __device__ __forceinline__ unsigned tag_of(unsigned long long w) { return (unsigned)(w >> 32); }
-
-// Reads the n records rec[0..n) into out[0..n) (LDS) once each carries `tag`.
-// Thread tid takes entries tid, tid + nthreads, ... (at most K of them); all
-// of its loads are issued together and only the entries not yet tagged are
-// read again.  The wait is bounded: after `spin_limit` rounds the thread gives
-// up, bumps *timeouts and stores what it has, so a broken launch cannot hang.
-template <int K>
-__device__ __forceinline__ void gather_tagged(const unsigned long long* rec, int n, unsigned tag, float* out,
-                                              int tid, int nthreads, unsigned spin_limit, unsigned* timeouts)
-{
-    unsigned long long w[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int e = tid + k * nthreads;
-        w[k] = e < n ? peek(&rec[e]) : ((unsigned long long)tag << 32);
-    }
-    for (unsigned polls = 0;; ++polls) {
-        bool ready = true;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            ready &= tag_of(w[k]) == tag;
-        if (ready)
-            break;
-        if (polls >= spin_limit) {
-            atomicAdd(timeouts, 1u);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int e = tid + k * nthreads;
-            if (e < n && tag_of(w[k]) != tag)
-                w[k] = peek(&rec[e]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int e = tid + k * nthreads;
-        if (e < n)
-            out[e] = __uint_as_float((unsigned)w[k]);
-    }
-}
 
 } // namespace attnres

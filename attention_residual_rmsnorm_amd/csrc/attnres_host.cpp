@@ -136,17 +136,28 @@ bool valid_override(int variant, int param)
 
 int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, Plan& pl)
 {
-    (void)n;
     const int nvec = (int)(H / 8);
     if (force_variant == 1)
         return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     if (force_variant == 2)
         return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
-    // automatic, by measurement on MI355X at H = 7168: up to 64 tokens the
-    // call is latency-bound and spreading each token over 4-wave chunks on
-    // several CUs wins; beyond that one workgroup per token (no exchange) wins.
-    if (M <= SPLIT_MAX_AUTO_TOKENS && plan_split(M, nvec, 4, pl))
-        return ATTNRES_OK;
+    // Automatic, from per-call times of every variant on MI355X at H = 7168
+    // (graph replay, inputs cold in HBM, M = 1..512, N = 1, 4, 12):
+    //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
+    //  * M <= 32: the call is latency-bound; 2-wave chunks spread each token
+    //    over the most CUs;
+    //  * M <= 128 with N >= 8: 4-wave chunks;
+    //  * 256 < M <= 512 with N >= 8: two 7-wave halves per token, one round of
+    //    workgroups instead of a second, partial round of whole tokens;
+    //  * otherwise one workgroup per token.
+    if (n > 2) {
+        if (M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 2, pl))
+            return ATTNRES_OK;
+        if (n >= 8 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
+            return ATTNRES_OK;
+        if (n >= 8 && M > 256 && M <= MAX_SPLIT_TOKENS && plan_split(M, nvec, 7, pl))
+            return ATTNRES_OK;
+    }
     if (plan_wg(M, nvec, 0, pl))
         return ATTNRES_OK;
     return plan_split(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;

@@ -12,7 +12,8 @@ constexpr int MAX_SNAP = 12;             // == ATTNRES_MAX_SNAPSHOTS
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-constexpr int SPLIT_MAX_AUTO_TOKENS = 64; // automatic dispatch: split hidden up to this many tokens
+constexpr int SPLIT_SMALL_TOKENS = 32;   // automatic dispatch: 2-wave split up to this many tokens
+constexpr int SPLIT_MID_TOKENS = 128;    // automatic dispatch: 4-wave split up to this many tokens (N >= 8)
 
 struct Plan {
     int variant = 0; // 1 = workgroup per token, 2 = split hidden
