@@ -50,6 +50,11 @@ class Oracle:
             _u16p, _u16p, _u16p, ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p,
             ctypes.c_float, ctypes.c_int64, ctypes.c_int64, _u16p, _u16p, _f64p, _f64p]
         lib.oracle_attnres_fwd.restype = ctypes.c_int
+        lib.oracle_attnres_fwd_mix.argtypes = [
+            _u16p, _u16p, _u16p, ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p,
+            ctypes.c_float, ctypes.c_int64, ctypes.c_int64, _u16p, _u16p, _u16p, _f64p, _f64p,
+            _f64p]
+        lib.oracle_attnres_fwd_mix.restype = ctypes.c_int
         self.lib = lib
 
     # scalar helpers -------------------------------------------------------
@@ -70,11 +75,14 @@ class Oracle:
     # the fused operation --------------------------------------------------
     def fwd(self, prefix: np.ndarray, add: np.ndarray, add2: Optional[np.ndarray],
             snapshots: Sequence[np.ndarray], query: np.ndarray, gamma: np.ndarray,
-            eps: float, want_f64: bool = False, want_alpha: bool = False):
+            eps: float, want_f64: bool = False, want_alpha: bool = False,
+            want_mix: bool = False, want_mix_f64: bool = False):
         """Run the oracle on [M,H] bf16-bit arrays.
 
-        Returns ``(out_prefix, out_norm)`` plus ``out_norm_f64`` and/or ``alpha``
-        ([M, N+1], sources in the order snapshots..., updated prefix) on request.
+        Returns ``(out_prefix, out_norm)`` plus, on request and in this order,
+        ``out_norm_f64``, ``alpha`` ([M, N+1], sources in the order snapshots...,
+        updated prefix), ``out_mix`` (the pre-norm mixture rounded to bf16) and
+        ``out_mix_f64`` (the mixture in binary64).
         """
         prefix = np.ascontiguousarray(prefix, dtype=np.uint16)
         M, H = prefix.shape
@@ -92,17 +100,19 @@ class Oracle:
         out_norm = np.empty((M, H), np.uint16)
         f64 = np.empty((M, H), np.float64) if want_f64 else None
         alpha = np.empty((M, N + 1), np.float64) if want_alpha else None
-        rc = self.lib.oracle_attnres_fwd(
+        mix = np.empty((M, H), np.uint16) if want_mix else None
+        mix64 = np.empty((M, H), np.float64) if want_mix_f64 else None
+        rc = self.lib.oracle_attnres_fwd_mix(
             _ptr(prefix), _ptr(add), _ptr(add2), arr if N else None, N, _ptr(query),
             _ptr(gamma), ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm),
-            _ptr(f64, _f64p), _ptr(alpha, _f64p))
+            _ptr(mix), _ptr(f64, _f64p), _ptr(mix64, _f64p), _ptr(alpha, _f64p))
         if rc != 0:
-            raise RuntimeError("oracle_attnres_fwd returned %d" % rc)
+            raise RuntimeError("oracle_attnres_fwd_mix returned %d" % rc)
         res = [out_prefix, out_norm]
-        if want_f64:
-            res.append(f64)
-        if want_alpha:
-            res.append(alpha)
+        for want, arr_ in ((want_f64, f64), (want_alpha, alpha), (want_mix, mix),
+                           (want_mix_f64, mix64)):
+            if want:
+                res.append(arr_)
         return tuple(res)
 
 

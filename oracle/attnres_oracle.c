@@ -105,13 +105,13 @@ void oracle_bf16_add_tensor(const uint16_t* a, const uint16_t* b, uint16_t* out,
         out[i] = oracle_bf16_add(a[i], b[i]);
 }
 
-/* One token.  k: scratch of (N+1)*H doubles; pnew: H bf16 of the new prefix. */
+/* One token.  k: scratch of (N+2)*H doubles (the sources, then the mixture). */
 static void one_token(const uint16_t* prefix, const uint16_t* add,
                       const uint16_t* add2, const uint16_t* const* snap_rows,
                       int N, const uint16_t* query, const uint16_t* gamma,
                       double eps, int64_t H, uint16_t* out_prefix,
-                      uint16_t* out_norm, double* out_norm_f64, double* alpha,
-                      double* k, double* z)
+                      uint16_t* out_norm, uint16_t* out_mix, double* out_norm_f64,
+                      double* out_mix_f64, double* alpha, double* k, double* z)
 {
     /* 1. fold-add: the updated prefix, bit-exact */
     for (int64_t h = 0; h < H; ++h) {
@@ -162,6 +162,10 @@ static void one_token(const uint16_t* prefix, const uint16_t* add,
         for (int s = 0; s < S; ++s)
             x += z[s] * k[(int64_t)s * H + h];
         k[(int64_t)S * H + h] = x; /* one spare row holds the mixture */
+        if (out_mix_f64)
+            out_mix_f64[h] = x;
+        if (out_mix)
+            out_mix[h] = oracle_round_bf16(x); /* the pre-norm mixture, rounded once */
         sumsq += x * x;
     }
     double rstd = 1.0 / sqrt(sumsq / (double)H + eps);
@@ -179,6 +183,18 @@ int oracle_attnres_fwd(const uint16_t* prefix, const uint16_t* add,
                        const uint16_t* gamma, float eps, int64_t M, int64_t H,
                        uint16_t* out_prefix, uint16_t* out_norm,
                        double* out_norm_f64, double* alpha)
+{
+    return oracle_attnres_fwd_mix(prefix, add, add2, snapshots, n_snapshots, query,
+                                  gamma, eps, M, H, out_prefix, out_norm, NULL,
+                                  out_norm_f64, NULL, alpha);
+}
+
+int oracle_attnres_fwd_mix(const uint16_t* prefix, const uint16_t* add,
+                           const uint16_t* add2, const uint16_t* const* snapshots,
+                           int n_snapshots, const uint16_t* query,
+                           const uint16_t* gamma, float eps, int64_t M, int64_t H,
+                           uint16_t* out_prefix, uint16_t* out_norm, uint16_t* out_mix,
+                           double* out_norm_f64, double* out_mix_f64, double* alpha)
 {
     if (!prefix || !add || !query || !gamma || !out_prefix || !out_norm)
         return -1;
@@ -211,7 +227,9 @@ int oracle_attnres_fwd(const uint16_t* prefix, const uint16_t* add,
             rows[s] = snapshots[s] + off;
         one_token(prefix + off, add + off, add2 ? add2 + off : NULL, rows,
                   n_snapshots, query, gamma, eps_d, H, out_prefix + off,
-                  out_norm + off, out_norm_f64 ? out_norm_f64 + off : NULL,
+                  out_norm + off, out_mix ? out_mix + off : NULL,
+                  out_norm_f64 ? out_norm_f64 + off : NULL,
+                  out_mix_f64 ? out_mix_f64 + off : NULL,
                   alpha ? alpha + m * S : NULL, k, z);
     }
     free(k);

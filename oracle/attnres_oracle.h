@@ -58,6 +58,18 @@ int oracle_attnres_fwd(const uint16_t* prefix, const uint16_t* add,
                        uint16_t* out_prefix, uint16_t* out_norm,
                        double* out_norm_f64, double* alpha);
 
+/* The same operation with the pre-norm mixture as well (the speculative-decoding
+ * capture tap of the source page's "Model" section needs it):
+ *   out_mix          [M,H]  or NULL: x = sum_s alpha_s k_s rounded once to bf16
+ *   out_mix_f64      [M,H]  or NULL: x before the rounding
+ * Every other argument and the return value as oracle_attnres_fwd. */
+int oracle_attnres_fwd_mix(const uint16_t* prefix, const uint16_t* add,
+                           const uint16_t* add2, const uint16_t* const* snapshots,
+                           int n_snapshots, const uint16_t* query,
+                           const uint16_t* gamma, float eps, int64_t M, int64_t H,
+                           uint16_t* out_prefix, uint16_t* out_norm, uint16_t* out_mix,
+                           double* out_norm_f64, double* out_mix_f64, double* alpha);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,6 +195,45 @@ def check_identical_sources(orc):
     assert_close(y, textbook_rmsnorm(f64(p), case.gamma, case.eps), 1e-13, 1e-300, "identical")
 
 
+def check_mix_output(orc):
+    """The pre-norm mixture output (the capture tap of the "Model" section).
+    N = 0 and identical sources: the mixture is the updated prefix, bit for
+    bit.  q = 0: it is the plain numpy mean of the sources.  Always: the bf16
+    mixture is the binary64 one rounded once, and out_norm is the textbook
+    RMSNorm of that binary64 mixture."""
+    case = rand_case(4, 768, 0, add2=True, seed=30)
+    p = torch_prefix(case.prefix, case.add, case.add2)
+    _, _, mix, mix64 = orc.fwd(case.prefix, case.add, case.add2, [], case.query, case.gamma,
+                               case.eps, want_mix=True, want_mix_f64=True)
+    assert np.array_equal(mix, p) and np.array_equal(mix64, f64(p)), "N=0 mixture"
+    _, _, mix, mix64 = orc.fwd(case.prefix, case.add, case.add2, [p] * 5, case.query, case.gamma,
+                               case.eps, want_mix=True, want_mix_f64=True)
+    assert np.array_equal(mix, p), "identical sources mixture"
+    assert_close(mix64, f64(p), 1e-15, 0, "identical sources mixture f64")
+
+    M, H, N = 3, 640, 6
+    case = rand_case(M, H, N, add2=True, seed=31)
+    snaps = [scale_pow2(s, k) for s, k in zip(case.snapshots, (-3, -1, 0, 1, 2, 4))]
+    q = np.zeros_like(case.query)
+    _, _, mix, mix64 = orc.fwd(case.prefix, case.add, case.add2, snaps, q, case.gamma, case.eps,
+                               want_mix=True, want_mix_f64=True)
+    p = torch_prefix(case.prefix, case.add, case.add2)
+    stack = np.stack([f64(s) for s in snaps] + [f64(p)])
+    mean = np.mean(stack, axis=0)
+    # binary64 summation error, bounded by the magnitudes of the terms
+    assert_close(mix64, mean, 1e-12, 1e-15 * np.mean(np.abs(stack), axis=0), "q=0 mixture")
+    rounded = np.array([orc.round_bf16(v) for v in mix64.ravel()], np.uint16).reshape(M, H)
+    assert np.array_equal(mix, rounded), "mixture rounded once"
+
+    case = rand_case(3, 896, 5, add2=True, seed=32)
+    _, _, y, mix, mix64 = orc.fwd(case.prefix, case.add, case.add2, case.snapshots, case.query,
+                                  case.gamma, case.eps, want_f64=True, want_mix=True,
+                                  want_mix_f64=True)
+    assert_close(y, textbook_rmsnorm(mix64, case.gamma, case.eps), 1e-12, 1e-300, "norm of mixture")
+    rounded = np.array([orc.round_bf16(v) for v in mix64.ravel()], np.uint16).reshape(mix.shape)
+    assert np.array_equal(mix, rounded), "mixture rounded once (random case)"
+
+
 def check_dominant_logit(orc):
     """A query aligned with one RMS-normalised source gives it a logit of
     about 4H (~1000 here): its weight is exactly 1 in binary64 (the others
@@ -350,6 +389,7 @@ QUICK = [
     check_self_snapshot_q0,
     check_q0_uniform_mean,
     check_identical_sources,
+    check_mix_output,
     check_two_source_closed_form,
     check_dominant_logit,
     check_token_permutation,

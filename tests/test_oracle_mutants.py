@@ -71,6 +71,12 @@ MUTANTS = {
     "final_sqrt_missing": (
         "    double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n    for",
         "    double rstd = 1.0 / (sumsq / (double)H + eps);\n    for"),
+    "mixture_output_reports_prefix": (
+        "            out_mix[h] = oracle_round_bf16(x); /* the pre-norm mixture, rounded once */",
+        "            out_mix[h] = oracle_round_bf16(k[(int64_t)N * H + h]);"),
+    "mixture_output_scaled": (
+        "            out_mix_f64[h] = x;",
+        "            out_mix_f64[h] = x * 1.0000001;"),
     "gamma_dropped": (
         "* rstd * oracle_bf16_to_f64(gamma[h]);",
         "* rstd;"),
