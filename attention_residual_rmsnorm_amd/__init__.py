@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     ATTNRES_OK,
     AttnResError,
     attnres_add_rmsnorm_fwd,
+    attnres_add_rmsnorm_mix_fwd,
     attnres_bf16_add,
     attnres_debug_timeouts,
     attnres_init,

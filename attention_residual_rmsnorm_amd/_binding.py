@@ -46,6 +46,10 @@ def library():
             _vp, _vp, _vp, ctypes.POINTER(_vp), ctypes.c_int, _vp, _vp, ctypes.c_float,
             ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
         lib.attnres_add_rmsnorm_fwd.restype = ctypes.c_int
+        lib.attnres_add_rmsnorm_mix_fwd.argtypes = [
+            _vp, _vp, _vp, ctypes.POINTER(_vp), ctypes.c_int, _vp, _vp, ctypes.c_float,
+            ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp, _vp]
+        lib.attnres_add_rmsnorm_mix_fwd.restype = ctypes.c_int
         lib.attnres_bf16_add.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp]
         lib.attnres_bf16_add.restype = ctypes.c_int
         lib.attnres_init.argtypes = []
@@ -105,15 +109,7 @@ def _check_tensor(name, t, shape):
         raise ValueError("%s must be a device tensor" % name)
 
 
-def attnres_add_rmsnorm_fwd(prefix, add, add2, snapshots: Sequence, query, gamma, eps: float,
-                            out_prefix=None, out_norm=None, stream=None):
-    """Fused fold-add + AttnRes mix + RMSNorm on bf16 device tensors.
-
-    prefix, add, add2 (or None), each snapshot, out_prefix, out_norm: [M, H];
-    query, gamma: [H].  Outputs are allocated when not given.  Returns
-    ``(out_prefix, out_norm)``.  Runs on the current torch stream unless
-    ``stream`` (a torch stream or raw handle) is given.
-    """
+def _fwd_args(prefix, add, add2, snapshots, query, gamma, out_prefix, out_norm):
     import torch
 
     M, H = prefix.shape
@@ -133,11 +129,43 @@ def attnres_add_rmsnorm_fwd(prefix, add, add2, snapshots: Sequence, query, gamma
     _check_tensor("out_norm", out_norm, (M, H))
     n = len(snapshots)
     arr = (_vp * max(n, 1))(*[_ptr(s) for s in snapshots])
+    return M, H, n, arr, out_prefix, out_norm
+
+
+def attnres_add_rmsnorm_fwd(prefix, add, add2, snapshots: Sequence, query, gamma, eps: float,
+                            out_prefix=None, out_norm=None, stream=None):
+    """Fused fold-add + AttnRes mix + RMSNorm on bf16 device tensors.
+
+    prefix, add, add2 (or None), each snapshot, out_prefix, out_norm: [M, H];
+    query, gamma: [H].  Outputs are allocated when not given.  Returns
+    ``(out_prefix, out_norm)``.  Runs on the current torch stream unless
+    ``stream`` (a torch stream or raw handle) is given.
+    """
+    M, H, n, arr, out_prefix, out_norm = _fwd_args(prefix, add, add2, snapshots, query, gamma,
+                                                   out_prefix, out_norm)
     rc = library().attnres_add_rmsnorm_fwd(
         _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
         ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _stream(stream))
     _check(rc, "attnres_add_rmsnorm_fwd")
     return out_prefix, out_norm
+
+
+def attnres_add_rmsnorm_mix_fwd(prefix, add, add2, snapshots: Sequence, query, gamma, eps: float,
+                                out_prefix=None, out_norm=None, out_mix=None, stream=None):
+    """attnres_add_rmsnorm_fwd plus the pre-norm mixture (bf16 [M, H], for a
+    hidden-state capture tap).  Returns ``(out_prefix, out_norm, out_mix)``."""
+    import torch
+
+    M, H, n, arr, out_prefix, out_norm = _fwd_args(prefix, add, add2, snapshots, query, gamma,
+                                                   out_prefix, out_norm)
+    if out_mix is None:
+        out_mix = torch.empty_like(prefix)
+    _check_tensor("out_mix", out_mix, (M, H))
+    rc = library().attnres_add_rmsnorm_mix_fwd(
+        _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
+        ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _ptr(out_mix), _stream(stream))
+    _check(rc, "attnres_add_rmsnorm_mix_fwd")
+    return out_prefix, out_norm, out_mix
 
 
 def attnres_bf16_add(a, b, out=None, stream=None):

@@ -56,6 +56,7 @@ struct Params {
     const uint4* gamma;
     uint4* out_prefix;
     uint4* out_norm;
+    uint4* out_mix;     // or null: no pre-norm mixture output
     float eps;
     float inv_h;        // 1/H: mean = sum * inv_h
     int nvec;           // H / 8 (16-byte vectors per row)
@@ -261,6 +262,13 @@ __device__ __forceinline__ float combine(const uint4 (&k)[S][VPT], const float* 
         sx += ok[j] ? sxj : 0.f;
     }
     return sx;
+}
+
+// Eight binary32 values times s, rounded to bf16 and packed.
+__device__ __forceinline__ uint4 pack_scaled(const float (&x)[8], float s)
+{
+    return make_uint4(pack_bf16(x[0] * s, x[1] * s), pack_bf16(x[2] * s, x[3] * s),
+                      pack_bf16(x[4] * s, x[5] * s), pack_bf16(x[6] * s, x[7] * s));
 }
 
 __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, const uint4& g)
@@ -553,6 +561,13 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
         for (int j = 0; j < VPT; ++j)
             if (ok[j])
                 p.out_norm[row + tid + j * nthreads] = normalise(mx.x[j], scale, g[j]);
+        if (p.out_mix) { // the pre-norm mixture x/den (a uniform branch)
+            const float inv = 1.0f / mx.den;
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    p.out_mix[row + tid + j * nthreads] = pack_scaled(mx.x[j], inv);
+        }
         __syncthreads(); // LDS reuse by the next token
     }
 }
@@ -726,8 +741,11 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     }
     __syncthreads();
     const float rstd = rsqrtf(ssum_sh * p.inv_h + p.eps);
-    if (ok[0])
+    if (ok[0]) {
         p.out_norm[row + v] = normalise(x[0], rstd, g[0]);
+        if (p.out_mix) // the pre-norm mixture (the weights sum to one here)
+            p.out_mix[row + v] = pack_scaled(x[0], 1.0f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -828,14 +846,14 @@ int scratch_for_current_device(Scratch** out)
 
 using namespace attnres;
 
-extern "C" int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, const void* add2,
-                                       const void* const* snapshots, int n_snapshots,
-                                       const void* query, const void* gamma, float eps, int64_t M,
-                                       int64_t H, void* out_prefix, void* out_norm,
-                                       hipStream_t stream)
+namespace attnres {
+
+int launch_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
+               int n_snapshots, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
+               void* out_prefix, void* out_norm, void* out_mix, hipStream_t stream)
 {
     int rc = validate_fwd(prefix, add, add2, snapshots, n_snapshots, query, gamma, eps, M, H,
-                          out_prefix, out_norm);
+                          out_prefix, out_norm, out_mix);
     if (rc != ATTNRES_OK)
         return rc;
     Plan pl;
@@ -855,6 +873,7 @@ extern "C" int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, cons
     p.gamma = static_cast<const uint4*>(gamma);
     p.out_prefix = static_cast<uint4*>(out_prefix);
     p.out_norm = static_cast<uint4*>(out_norm);
+    p.out_mix = static_cast<uint4*>(out_mix);
     p.eps = eps;
     p.inv_h = 1.0f / (float)H;
     p.nvec = (int)(H / 8);
@@ -882,6 +901,28 @@ extern "C" int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, cons
                         args, 0, stream) != hipSuccess)
         return ATTNRES_EHIP;
     return ATTNRES_OK;
+}
+
+} // namespace attnres
+
+extern "C" int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, const void* add2,
+                                       const void* const* snapshots, int n_snapshots,
+                                       const void* query, const void* gamma, float eps, int64_t M,
+                                       int64_t H, void* out_prefix, void* out_norm,
+                                       hipStream_t stream)
+{
+    return launch_fwd(prefix, add, add2, snapshots, n_snapshots, query, gamma, eps, M, H, out_prefix,
+                      out_norm, nullptr, stream);
+}
+
+extern "C" int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void* add2,
+                                           const void* const* snapshots, int n_snapshots,
+                                           const void* query, const void* gamma, float eps, int64_t M,
+                                           int64_t H, void* out_prefix, void* out_norm, void* out_mix,
+                                           hipStream_t stream)
+{
+    return launch_fwd(prefix, add, add2, snapshots, n_snapshots, query, gamma, eps, M, H, out_prefix,
+                      out_norm, out_mix, stream);
 }
 
 extern "C" int attnres_bf16_add(const void* a, const void* b, void* out, int64_t n, hipStream_t stream)
@@ -965,4 +1006,4 @@ extern "C" const char* attnres_status_string(int status)
     }
 }
 
-extern "C" int attnres_version(void) { return 100; }
+extern "C" int attnres_version(void) { return 101; }

@@ -78,7 +78,7 @@ int validate_sizes(int64_t M, int n, int64_t H)
 
 int validate_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
                  int n, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
-                 const void* out_prefix, const void* out_norm)
+                 const void* out_prefix, const void* out_norm, const void* out_mix)
 {
     int rc = validate_sizes(M, n, H);
     if (rc != ATTNRES_OK)
@@ -95,7 +95,8 @@ int validate_fwd(const void* prefix, const void* add, const void* add2, const vo
         if (!snapshots[s] || !aligned16(snapshots[s]))
             return ATTNRES_EINVAL;
     if (!aligned16(prefix) || !aligned16(add) || (add2 && !aligned16(add2)) || !aligned16(query) ||
-        !aligned16(gamma) || !aligned16(out_prefix) || !aligned16(out_norm))
+        !aligned16(gamma) || !aligned16(out_prefix) || !aligned16(out_norm) ||
+        (out_mix && !aligned16(out_mix)))
         return ATTNRES_EINVAL;
 
     // Every read-only buffer other than prefix: add, add2, query, gamma, snapshots.
@@ -121,6 +122,16 @@ int validate_fwd(const void* prefix, const void* add, const void* add2, const vo
         if (overlaps(out_prefix, row_bytes, ins[i], sizes[i]) ||
             overlaps(out_norm, row_bytes, ins[i], sizes[i]))
             return ATTNRES_EALIAS;
+    // out_mix (optional): disjoint from every other buffer
+    if (out_mix) {
+        if (overlaps(out_mix, row_bytes, prefix, row_bytes) ||
+            overlaps(out_mix, row_bytes, out_prefix, row_bytes) ||
+            overlaps(out_mix, row_bytes, out_norm, row_bytes))
+            return ATTNRES_EALIAS;
+        for (int i = 0; i < ni; ++i)
+            if (overlaps(out_mix, row_bytes, ins[i], sizes[i]))
+                return ATTNRES_EALIAS;
+    }
     return ATTNRES_OK;
 }
 

@@ -24,9 +24,10 @@ struct Plan {
 };
 
 // Full validation of a fused call; returns a status code (ATTNRES_*).
+// out_mix may be NULL (no mixture output).
 int validate_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
                  int n, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
-                 const void* out_prefix, const void* out_norm);
+                 const void* out_prefix, const void* out_norm, const void* out_mix = nullptr);
 
 // Size-only validation (what attnres_plan checks).
 int validate_sizes(int64_t M, int n, int64_t H);

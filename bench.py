@@ -111,6 +111,7 @@ class Launcher:
         self.ar = ar
         self.lib = ar.library()
         self.fwd = self.lib.attnres_add_rmsnorm_fwd
+        self.fwd_mix = self.lib.attnres_add_rmsnorm_mix_fwd
         self.add = self.lib.attnres_bf16_add
         self._keep = []
 
@@ -128,6 +129,11 @@ class Launcher:
         rc = self.fwd(*args, stream)
         if rc != 0:
             raise RuntimeError("attnres_add_rmsnorm_fwd -> %d" % rc)
+
+    def run_mix(self, args, out_mix, stream):
+        rc = self.fwd_mix(*args, out_mix, stream)
+        if rc != 0:
+            raise RuntimeError("attnres_add_rmsnorm_mix_fwd -> %d" % rc)
 
     def run_add(self, a, b, out, stream):
         rc = self.add(a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(), stream)
@@ -366,6 +372,38 @@ def latency_suite(launcher, rotate=16, calls=96):
     return out
 
 
+def tap_suite(launcher, calls=64):
+    """Cost of the pre-norm mixture output (the capture tap): µs per call of the
+    fused call with and without out_mix, graph replay over >= 1 GB of rotating
+    buffer sets, at the bandwidth shape (M=256, N=12) and the single-token one."""
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    out = {}
+    for name, M, N in (("m256_n12", 256, 12), ("cfg4b", 1, 12)):
+        case = W.make_case(cfg=90, M=M, N=N, add2=True)
+        nbytes = call_bytes(M, case.H, N, True)
+        rotate = min(32, max(4, int(1.1e9 // (nbytes + M * case.H * 2)) + 1))
+        sets = []
+        for r in range(rotate):
+            t = [dev(x) for x in [case.prefix, case.add, case.add2] + case.snapshots + [case.query, case.gamma]]
+            op, on, om = (torch.empty_like(t[0]) for _ in range(3))
+            sets.append((launcher.fused_args(t[0], t[1], t[2], t[3:3 + N], t[-2], t[-1], case.eps, op, on),
+                         om.data_ptr(), t, op, on, om))
+        plain, _ = graph_time(lambda s: [launcher.run_fused(sets[k % rotate][0], s) for k in range(calls)], 12, 2)
+        mix, _ = graph_time(lambda s: [launcher.run_mix(sets[k % rotate][0], sets[k % rotate][1], s)
+                                       for k in range(calls)], 12, 2)
+        p_us, m_us = plain / calls * 1e6, mix / calls * 1e6
+        out[name] = {"M": M, "N": N, "plain_us_per_call": round(p_us, 3), "mix_us_per_call": round(m_us, 3),
+                     "extra_us": round(m_us - p_us, 3),
+                     "mix_GBps": round((nbytes + M * case.H * 2) / (m_us * 1e-6) / 1e9, 1)}
+        log("tap %s: %s" % (name, out[name]))
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,6 +522,7 @@ def main():
                           "saving_us_per_call": round((sec_u - sec) / launches * 1e6, 3)}
         log("fold: %s" % result["fold"])
         result["latency_us"] = latency_suite(launcher)
+        result["tap"] = tap_suite(launcher)
         if not args.no_cpu_baseline:
             threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
             result["cpu_baseline"] = cpu_baseline(chain, threads)

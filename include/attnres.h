@@ -110,6 +110,29 @@ int attnres_add_rmsnorm_fwd(const void* prefix, const void* add, const void* add
                             hipStream_t stream);
 
 /*
+ * attnres_add_rmsnorm_mix_fwd -- the same fused step, also writing the
+ * pre-norm mixture for a speculative-decoding hidden-state capture tap (the
+ * page's section "Model" lists such a layer among the fused path's fallbacks
+ * because the tap needs x; with this call it stays on the fused path).
+ *
+ *   out_mix      device bf16 [M,H] or NULL: x = sum_s alpha_s * k_s rounded
+ *                once to bf16 (nearest even), within 2 bf16 ulps (or 1e-2
+ *                absolute) of x evaluated in binary64.  Written in the same
+ *                launch; must be 16-byte aligned and must not overlap any other
+ *                buffer (ATTNRES_EALIAS).  NULL makes the call identical to
+ *                attnres_add_rmsnorm_fwd.
+ *
+ * Every other argument, the accuracy of out_prefix / out_norm (bitwise the
+ * same as attnres_add_rmsnorm_fwd's for the same inputs and dispatch), the
+ * scratch and the status codes are those of attnres_add_rmsnorm_fwd.
+ */
+int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void* add2,
+                                const void* const* snapshots, int n_snapshots,
+                                const void* query, const void* gamma, float eps,
+                                int64_t M, int64_t H, void* out_prefix, void* out_norm,
+                                void* out_mix, hipStream_t stream);
+
+/*
  * attnres_bf16_add -- the unfused MoE-tail addition: out = bf16(a + b)
  * elementwise (binary32 round-to-nearest add, subnormals kept), n elements.
  * This is the standalone kernel the fold replaces (page "[#20545][perf] Kimi

@@ -55,6 +55,20 @@ int main()
                                     at(reinterpret_cast<uintptr_t>(snaps[n - 1]) + 4096), outn) ==
                        ATTNRES_EALIAS);
             }
+            // the optional mixture output: valid when disjoint, aliasing rejected
+            const void* outm = at(base + 6 * row);
+            EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn, outm) == want);
+            if (n <= 12) {
+                EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn, outp) ==
+                       ATTNRES_EALIAS);
+                EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn,
+                                    at(base + 5 * row + 16)) == ATTNRES_EALIAS);
+                EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn,
+                                    at(base + 6 * row + 8)) == ATTNRES_EINVAL);
+                if (n >= 1)
+                    EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn,
+                                        snaps[n - 1]) == ATTNRES_EALIAS);
+            }
             Plan pl;
             for (int fv = 0; fv <= 2; ++fv)
                 for (int fp = 0; fp <= 9; ++fp) {

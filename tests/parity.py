@@ -89,3 +89,29 @@ def run_gpu(case: W.Case, add2=True, out_prefix=None, out_norm=None):
 
 def run_oracle(orc, case: W.Case):
     return orc.fwd(case.prefix, case.add, case.add2, case.snapshots, case.query, case.gamma, case.eps)
+
+
+def run_gpu_mix(case: W.Case):
+    """The fused call with the pre-norm mixture output; numpy (out_prefix, out_norm, out_mix)."""
+    import attention_residual_rmsnorm_amd as ar
+
+    d = lambda x: None if x is None else dev(x)
+    op, on, om = ar.attnres_add_rmsnorm_mix_fwd(
+        d(case.prefix), d(case.add), d(case.add2), [d(s) for s in case.snapshots],
+        d(case.query), d(case.gamma), case.eps)
+    return host(op), host(on), host(om)
+
+
+def run_oracle_mix(orc, case: W.Case):
+    """Oracle (out_prefix, out_norm, out_mix)."""
+    return orc.fwd(case.prefix, case.add, case.add2, case.snapshots, case.query, case.gamma, case.eps,
+                   want_mix=True)
+
+
+def assert_mix_parity(gpu_mix, ref_mix, what=""):
+    """The mixture has out_norm's bar: 2 bf16 ulps or 1e-2 absolute, no NaN."""
+    mask = norm_mismatches(gpu_mix, ref_mix)
+    if mask.any():
+        i = tuple(np.argwhere(mask)[0])
+        raise AssertionError("%s: out_mix outside 2 ulps / 1e-2 at %d places, first %s: gpu %04x oracle %04x"
+                             % (what, int(mask.sum()), i, np.asarray(gpu_mix)[i], np.asarray(ref_mix)[i]))

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attnres_add_rmsnorm_fwd", "attnres_bf16_add", "attnres_init", "attnres_plan",
+    for n in ("attnres_add_rmsnorm_fwd", "attnres_add_rmsnorm_mix_fwd", "attnres_bf16_add",
+              "attnres_init", "attnres_plan",
               "attnres_set_variant", "attnres_status_string", "attnres_version", "attnres_debug_timeouts",
               "attnres_selftest_rounding"):
         assert n in names, n
@@ -118,6 +119,29 @@ def test_snapshot_count():
 ])
 def test_aliasing(kw):
     assert call(base_args(**kw)) == ar.ATTNRES_EALIAS
+
+
+def call_mix(d, out_mix):
+    lib = ar.library()
+    snaps = d["snaps"]
+    arr = (ctypes.c_void_p * len(snaps))(*snaps)
+    return lib.attnres_add_rmsnorm_mix_fwd(d["prefix"], d["add"], d["add2"], arr, len(snaps), d["query"],
+                                           d["gamma"], ctypes.c_float(d["eps"]), d["M"], d["H"],
+                                           d["out_prefix"], d["out_norm"], out_mix, None)
+
+
+@pytest.mark.parametrize("out_mix,code", [
+    (A + 9 * ROW + 8, ar.ATTNRES_EINVAL),   # misaligned
+    (A, ar.ATTNRES_EALIAS),                  # == prefix
+    (A + 3 * ROW + 64, ar.ATTNRES_EALIAS),   # inside a snapshot
+    (A + 5 * ROW + 65536 - 16, ar.ATTNRES_EALIAS),  # overlaps gamma
+    (A + 7 * ROW, ar.ATTNRES_EALIAS),        # == out_prefix
+    (A + 8 * ROW + 16, ar.ATTNRES_EALIAS),   # overlaps out_norm
+])
+def test_mix_validation(out_mix, code):
+    assert call_mix(base_args(), out_mix) == code
+    # the same call with a valid destination but an invalid other argument is still rejected
+    assert call_mix(base_args(M=-1), A + 9 * ROW) == ar.ATTNRES_EINVAL
 
 
 def test_bf16_add_validation():
