@@ -10,7 +10,7 @@ ATTNRES_EINVAL = -1
 ATTNRES_EUNSUPPORTED = -2
 ATTNRES_EALIAS = -3
 ATTNRES_EHIP = -4
-ATTNRES_MAX_SNAPSHOTS = 12
+ATTNRES_MAX_SNAPSHOTS = 64
 ATTNRES_MAX_HIDDEN = 16384
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -472,8 +472,11 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
 
 // The groups over S sources: G at a time, the last source on its own.  Group
 // gi uses LDS slot gi % 2 (a slot is written again two groups later, after
-// every thread has passed the barriers that end its readers' use).
-template <int S, int G, int VPT, int G0, int GI>
+// every thread has passed the barriers that end its readers' use; a batch
+// of sources always starts at gi = 0 and the group before it, the previous
+// batch's last, ends on an odd gi, so consecutive groups never share a slot).
+// FIRSTBATCH: the first group starts the running softmax.
+template <int S, int G, int VPT, int G0, int GI, bool FIRSTBATCH>
 __device__ __forceinline__ void mix_groups(const uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
                                            Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8],
                                            const Params& p, int tid)
@@ -481,9 +484,70 @@ __device__ __forceinline__ void mix_groups(const uint4 (&k)[S][VPT], const uint4
     if constexpr (G0 < S) {
         constexpr int LAST = S - 1;
         constexpr int n = G0 == LAST ? 1 : (G < LAST - G0 ? G : LAST - G0);
-        mix_group<n, VPT, G0 == 0>(&k[G0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
-        mix_groups<S, G, VPT, G0 + n, GI + 1>(k, q, ok, mx, rows, tot, p, tid);
+        mix_group<n, VPT, FIRSTBATCH && G0 == 0>(&k[G0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
+        mix_groups<S, G, VPT, G0 + n, GI + 1, FIRSTBATCH>(k, q, ok, mx, rows, tot, p, tid);
     }
+}
+
+// Number of groups mix_groups makes of S sources (G at a time, the last alone).
+template <int S, int G>
+constexpr int group_count()
+{
+    return S <= 1 ? S : 1 + (S - 1 + G - 1) / G;
+}
+
+// LDS set-up shared by both forms of kernel W: entries of absent waves stay
+// zero (ordered before use by the first barrier).
+template <int MAXW>
+__device__ __forceinline__ void wg_prologue(float (*rows)[64 * 8], float* red2, int tid, int nthreads)
+{
+    const int nw = nthreads >> 6;
+    if (tid < MAXW && tid >= nw)
+        red2[tid] = 0.f;
+    for (int i = tid; i < 2 * 64 * 8; i += nthreads)
+        if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
+            rows[i >> 9][i & 511] = 0.f;
+}
+
+// A5 (and the optional mixture output) of one token from the running softmax
+// state.  A4's division by den is folded into the norm: the mixture is x/den,
+// so out = x * scale * gamma with
+//   scale = 1/(den*sqrt(mean((x/den)^2) + eps)) = 1/sqrt(mean(x^2) + eps*den^2).
+template <int VPT, int MAXW>
+__device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, const uint4* g, const Params& p,
+                                          int64_t row, float* red2, int tid, int nthreads)
+{
+    const int lane = tid & 63, wave = tid >> 6;
+    float sx = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        float sxj = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sxj = __builtin_fmaf(mx.x[j][e], mx.x[j][e], sxj);
+        sx += ok[j] ? sxj : 0.f;
+    }
+    sx = wave_sum(sx);
+    if (lane == 0)
+        red2[wave] = sx;
+    __syncthreads();
+    float ssum = red2[0];
+#pragma unroll
+    for (int w = 1; w < MAXW; ++w)
+        ssum += red2[w];
+    const float scale = rsq(ssum * p.inv_h + (p.eps * mx.den) * mx.den);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+        if (ok[j])
+            p.out_norm[row + tid + j * nthreads] = normalise(mx.x[j], scale, g[j]);
+    if (p.out_mix) { // the pre-norm mixture x/den (a uniform branch)
+        const float inv = 1.0f / mx.den;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            if (ok[j])
+                p.out_mix[row + tid + j * nthreads] = pack_scaled(mx.x[j], inv);
+    }
+    __syncthreads(); // LDS reuse by the next token
 }
 
 template <int NS, bool ADD2, int VPT, int MAXB, int G>
@@ -497,17 +561,9 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
     __shared__ float red2[MAXW];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     const int nthreads = blockDim.x;
-    const int nw = nthreads >> 6;
     const int nvec = p.nvec;
-    // entries of absent waves stay zero (ordered before use by the first barrier)
-    if (tid < MAXW && tid >= nw)
-        red2[tid] = 0.f;
-    for (int i = tid; i < 2 * 64 * 8; i += nthreads)
-        if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
-            rows[i >> 9][i & 511] = 0.f;
+    wg_prologue<MAXW>(rows, red2, tid, nthreads);
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
         const int64_t row = t * (int64_t)nvec;
@@ -534,41 +590,90 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 
         // A2-A4
         Mix<VPT> mx;
-        mix_groups<S, G, VPT, 0, 0>(k, q, ok, mx, rows, tot, p, tid);
+        mix_groups<S, G, VPT, 0, 0, true>(k, q, ok, mx, rows, tot, p, tid);
+        // A5
+        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
+    }
+}
 
-        // A4's division by den folded into A5: the mixture is x/den, so
-        // out = x * scale * gamma with scale = 1/(den*sqrt(mean((x/den)^2) + eps))
-        //                                    = 1/sqrt(mean(x^2) + eps*den^2).
-        float sx = 0.f;
+// ---------------------------------------------------------------------------
+// Kernel W for more than MAX_SNAP snapshots: the sources come in batches that
+// reuse the same registers.  Batch 0 is p' and snapshots 0..MAX_SNAP-1 (the
+// code of fwd_wg for N = MAX_SNAP); then pl.n_full batches of MAX_SNAP
+// snapshots and a last batch of NB_LAST.  Each batch's loads are issued at
+// once and its groups mixed into the same running softmax as they arrive.
+struct ParamsLong {
+    Params p;
+    const uint4* more[MAX_SNAP_LONG - MAX_SNAP]; // snapshots MAX_SNAP, MAX_SNAP + 1, ...
+    int n_full;                                  // full batches after batch 0
+};
+
+template <int NB, int VPT>
+__device__ __forceinline__ void load_batch(const uint4* const* src, int64_t row, const int (&vc)[VPT],
+                                           uint4 (&k)[NB][VPT])
+{
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            float sxj = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sxj = __builtin_fmaf(mx.x[j][e], mx.x[j][e], sxj);
-            sx += ok[j] ? sxj : 0.f;
-        }
-        sx = wave_sum(sx);
-        if (lane == 0)
-            red2[wave] = sx;
-        __syncthreads();
-        float ssum = red2[0];
-#pragma unroll
-        for (int w = 1; w < MAXW; ++w)
-            ssum += red2[w];
-        const float scale = rsq(ssum * p.inv_h + (p.eps * mx.den) * mx.den);
+    for (int s = 0; s < NB; ++s) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
-            if (ok[j])
-                p.out_norm[row + tid + j * nthreads] = normalise(mx.x[j], scale, g[j]);
-        if (p.out_mix) { // the pre-norm mixture x/den (a uniform branch)
-            const float inv = 1.0f / mx.den;
+            k[s][j] = load_stream(&src[s][row + vc[j]]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int NB_LAST, bool ADD2, int VPT, int MAXB, int G>
+__global__ __launch_bounds__(MAXB) void fwd_wg_long(ParamsLong pl)
+{
+    constexpr int B = MAX_SNAP;
+    constexpr int MAXW = MAXB / 64;
+    static_assert(group_count<B + 1, G>() % 2 == 0 && group_count<B, G>() % 2 == 0,
+                  "batches must end on an odd group index");
+    __shared__ __align__(16) float rows[2][64 * 8];
+    __shared__ __align__(16) float tot[2][8];
+    __shared__ float red2[MAXW];
+    const Params& p = pl.p;
+
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int nvec = p.nvec;
+    wg_prologue<MAXW>(rows, red2, tid, nthreads);
+
+    for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
+        const int64_t row = t * (int64_t)nvec;
+        uint4 q[VPT], g[VPT];
+        bool ok[VPT];
+        int vc[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int v = tid + j * nthreads;
+            ok[j] = v < nvec;
+            vc[j] = ok[j] ? v : nvec - 1;
+        }
+        Mix<VPT> mx;
+        {
+            uint4 k[B + 1][VPT], a[VPT], b[VPT], c[VPT];
+            load_token<B, ADD2, VPT>(p, row, vc, q, g, a, b, c, k);
+            __builtin_amdgcn_sched_barrier(0);
+            fold_add<ADD2, VPT>(a, b, c, k[0]);
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
                 if (ok[j])
-                    p.out_mix[row + tid + j * nthreads] = pack_scaled(mx.x[j], inv);
+                    p.out_prefix[row + tid + j * nthreads] = k[0][j];
+            mix_groups<B + 1, G, VPT, 0, 0, true>(k, q, ok, mx, rows, tot, p, tid);
         }
-        __syncthreads(); // LDS reuse by the next token
+        for (int bi = 0; bi < pl.n_full; ++bi) {
+            uint4 k[B][VPT];
+            load_batch<B, VPT>(pl.more + bi * B, row, vc, k);
+            __builtin_amdgcn_sched_barrier(0);
+            mix_groups<B, G, VPT, 0, 0, false>(k, q, ok, mx, rows, tot, p, tid);
+        }
+        {
+            uint4 k[NB_LAST][VPT];
+            load_batch<NB_LAST, VPT>(pl.more + pl.n_full * B, row, vc, k);
+            __builtin_amdgcn_sched_barrier(0);
+            mix_groups<NB_LAST, G, VPT, 0, 0, false>(k, q, ok, mx, rows, tot, p, tid);
+        }
+        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
     }
 }
 
@@ -789,6 +894,20 @@ const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GRO
                                                   wg_table<true, 2, 512, WG_GROUP>(Seq{})};
 const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512, WG_GROUP>(Seq{}),
                                                   wg_table<true, 4, 512, WG_GROUP>(Seq{})};
+// more than MAX_SNAP snapshots: [add2][size of the last batch - 1]
+using KernelLong = void (*)(ParamsLong);
+
+template <bool A2, int VPT, int MAXB, int G, int... I>
+constexpr std::array<KernelLong, sizeof...(I)> wg_long_table(std::integer_sequence<int, I...>)
+{
+    return {{&fwd_wg_long<I + 1, A2, VPT, MAXB, G>...}};
+}
+
+using SeqBatch = std::make_integer_sequence<int, MAX_SNAP>;
+const std::array<KernelLong, MAX_SNAP> kWgLong2[2] = {wg_long_table<false, 2, 512, WG_GROUP>(SeqBatch{}),
+                                                      wg_long_table<true, 2, 512, WG_GROUP>(SeqBatch{})};
+const std::array<KernelLong, MAX_SNAP> kWgLong4[2] = {wg_long_table<false, 4, 512, WG_GROUP>(SeqBatch{}),
+                                                      wg_long_table<true, 4, 512, WG_GROUP>(SeqBatch{})};
 // split hidden, 1-2 waves per workgroup (up to 32 chunks)
 const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, MAX_CHUNKS, 1>(Seq{}),
                                                       split_table<true, 128, MAX_CHUNKS, 1>(Seq{})};
@@ -867,7 +986,7 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.prefix = static_cast<const uint4*>(prefix);
     p.add = static_cast<const uint4*>(add);
     p.add2 = static_cast<const uint4*>(add2);
-    for (int s = 0; s < n_snapshots; ++s)
+    for (int s = 0; s < n_snapshots && s < MAX_SNAP; ++s)
         p.snap[s] = static_cast<const uint4*>(snapshots[s]);
     p.query = static_cast<const uint4*>(query);
     p.gamma = static_cast<const uint4*>(gamma);
@@ -882,6 +1001,23 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.spin_limit = SPIN_LIMIT;
 
     const int a2 = add2 ? 1 : 0;
+    if (n_snapshots > MAX_SNAP) {
+        // batched sources: batch 0 = p' + snapshots 0..11, then full batches of
+        // 12 and a last batch of 1..12
+        ParamsLong lp{};
+        lp.p = p;
+        for (int s = MAX_SNAP; s < n_snapshots; ++s)
+            lp.more[s - MAX_SNAP] = static_cast<const uint4*>(snapshots[s]);
+        const int rest = n_snapshots - MAX_SNAP;
+        const int nb_last = (rest - 1) % MAX_SNAP + 1;
+        lp.n_full = (rest - nb_last) / MAX_SNAP;
+        KernelLong fl = (pl.vpt == 2 ? kWgLong2 : kWgLong4)[a2][nb_last - 1];
+        void* largs[] = {&lp};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(fl), dim3((unsigned)pl.grid), dim3(pl.threads), largs,
+                            0, stream) != hipSuccess)
+            return ATTNRES_EHIP;
+        return ATTNRES_OK;
+    }
     Kernel fn = nullptr;
     if (pl.variant == 2) {
         Scratch* sc = nullptr;

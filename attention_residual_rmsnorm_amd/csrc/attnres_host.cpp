@@ -8,7 +8,7 @@
 
 namespace attnres {
 
-static_assert(MAX_SNAP == ATTNRES_MAX_SNAPSHOTS, "snapshot limit mismatch");
+static_assert(MAX_SNAP_LONG == ATTNRES_MAX_SNAPSHOTS, "snapshot limit mismatch");
 static_assert(MAX_HIDDEN == ATTNRES_MAX_HIDDEN, "hidden limit mismatch");
 
 namespace {
@@ -69,7 +69,7 @@ int validate_sizes(int64_t M, int n, int64_t H)
 {
     if (n < 0)
         return ATTNRES_EINVAL;
-    if (n > MAX_SNAP)
+    if (n > MAX_SNAP_LONG)
         return ATTNRES_EUNSUPPORTED;
     if (M < 0 || M > INT32_MAX || H < 8 || H % 8 != 0 || H > MAX_HIDDEN)
         return ATTNRES_EINVAL;
@@ -101,8 +101,8 @@ int validate_fwd(const void* prefix, const void* add, const void* add2, const vo
 
     // Every read-only buffer other than prefix: add, add2, query, gamma, snapshots.
     const size_t row_bytes = (size_t)M * (size_t)H * 2u, vec_bytes = (size_t)H * 2u;
-    const void* ins[4 + MAX_SNAP];
-    size_t sizes[4 + MAX_SNAP];
+    const void* ins[4 + MAX_SNAP_LONG];
+    size_t sizes[4 + MAX_SNAP_LONG];
     int ni = 0;
     ins[ni] = add, sizes[ni++] = row_bytes;
     if (add2)
@@ -148,6 +148,14 @@ bool valid_override(int variant, int param)
 int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, Plan& pl)
 {
     const int nvec = (int)(H / 8);
+    if (n > MAX_SNAP) {
+        // more sources than one pass holds: workgroup per token, sources in
+        // batches of MAX_SNAP (instantiated for 2 and 4 vectors per thread)
+        if (force_variant == 2 || (force_variant == 1 && force_param == 1))
+            return ATTNRES_EINVAL;
+        const int vpt = force_variant == 1 && force_param ? force_param : nvec <= 1024 ? 2 : 4;
+        return plan_wg(M, nvec, vpt, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    }
     if (force_variant == 1)
         return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     if (force_variant == 2)

@@ -57,13 +57,18 @@ extern "C" {
                                      bad variant request */
 #define ATTNRES_EUNSUPPORTED (-2) /* n_snapshots > ATTNRES_MAX_SNAPSHOTS: the caller
                                      adds the tail first and takes an unfused route
-                                     (the page's fallback for N > 12, section "Model") */
+                                     (the page's fallback beyond its source limit,
+                                     section "Model") */
 #define ATTNRES_EALIAS (-3)       /* forbidden overlap between an output and any other
                                      buffer */
 #define ATTNRES_EHIP (-4)         /* a HIP call failed (launch error, no device,
                                      out of memory for the scratch) */
 
-#define ATTNRES_MAX_SNAPSHOTS 12 /* the fused window's source limit (section "Model") */
+#define ATTNRES_MAX_SNAPSHOTS 64 /* up to 12 (the page's fused window, section "Model")
+                                    the sources are taken in one pass; 13..64 take the
+                                    batched path (the same running softmax carried over
+                                    batches of 12 snapshots), so the page's N > 12
+                                    fallback is not needed below 65 */
 #define ATTNRES_MAX_HIDDEN 16384
 
 /*
@@ -76,7 +81,7 @@ extern "C" {
  *   snapshots    HOST array of n_snapshots device pointers, each bf16 [M,H]
  *                (the snapshot bank, read); may be NULL when n_snapshots == 0.
  *                Entries may repeat.  The array is read during the call only.
- *   n_snapshots  N, 0 <= N <= 12; N = 0 mixes the updated prefix alone (weight
+ *   n_snapshots  N, 0 <= N <= 64; N = 0 mixes the updated prefix alone (weight
  *                1), i.e. plain fold-add + RMSNorm
  *   query        device bf16 [H]    per-layer query of the mix (read)
  *   gamma        device bf16 [H]    RMSNorm weight, applied as y = x*rstd*gamma

@@ -28,8 +28,8 @@ int main()
     const uintptr_t base = uintptr_t(1) << 40;
     const int64_t M = 4, H = 7168;
     const uintptr_t row = uintptr_t(M * H * 2);
-    const void* snaps[13];
-    for (int s = 0; s < 13; ++s)
+    const void* snaps[ATTNRES_MAX_SNAPSHOTS + 1];
+    for (int s = 0; s <= ATTNRES_MAX_SNAPSHOTS; ++s)
         snaps[s] = at(base + (uintptr_t)(10 + s) * row);
     const void* prefix = at(base);
     const void* add = at(base + row);
@@ -40,13 +40,13 @@ int main()
     const void* outn = at(base + 5 * row);
 
     for (int with2 = 0; with2 < 2; ++with2) {
-        for (int n = 0; n <= 13; ++n) {
+        for (int n = 0; n <= ATTNRES_MAX_SNAPSHOTS + 1; ++n) {
             const void* a2 = with2 ? add2 : nullptr;
-            const int want = n <= 12 ? ATTNRES_OK : ATTNRES_EUNSUPPORTED;
+            const int want = n <= ATTNRES_MAX_SNAPSHOTS ? ATTNRES_OK : ATTNRES_EUNSUPPORTED;
             EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn) == want);
             // in place is allowed
             EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, prefix, outn) == want);
-            if (n >= 1 && n <= 12) {
+            if (n >= 1 && n <= ATTNRES_MAX_SNAPSHOTS) {
                 // out_norm equal to the last snapshot
                 EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp,
                                     snaps[n - 1]) == ATTNRES_EALIAS);
@@ -58,7 +58,7 @@ int main()
             // the optional mixture output: valid when disjoint, aliasing rejected
             const void* outm = at(base + 6 * row);
             EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn, outm) == want);
-            if (n <= 12) {
+            if (n <= ATTNRES_MAX_SNAPSHOTS) {
                 EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn, outp) ==
                        ATTNRES_EALIAS);
                 EXPECT(validate_fwd(prefix, add, a2, snaps, n, query, gamma, 1e-6f, M, H, outp, outn,
@@ -83,6 +83,8 @@ int main()
                                 EXPECT(pl.threads % 64 == 0 && pl.threads >= 64 && pl.threads <= 1024);
                                 EXPECT(pl.grid >= 1);
                                 EXPECT((int64_t)pl.threads * pl.vpt * pl.chunks * 8 >= h);
+                                if (n > MAX_SNAP)
+                                    EXPECT(pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4));
                                 if (pl.variant == 2)
                                     EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
                                            pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&

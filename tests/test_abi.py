@@ -100,9 +100,16 @@ def test_invalid_sizes_and_alignment(kw, code):
 
 
 def test_snapshot_count():
+    assert ar.ATTNRES_MAX_SNAPSHOTS == 64
     assert call(base_args(), n=-1) == ar.ATTNRES_EINVAL
-    many = [A + (10 + i) * ROW for i in range(13)]
+    many = [A + (10 + i) * ROW for i in range(65)]
     assert call(base_args(snaps=many)) == ar.ATTNRES_EUNSUPPORTED
+    # more than one pass of snapshots is accepted; a bad pointer among them is still caught
+    bad = [A + (10 + i) * ROW for i in range(30)]
+    bad[20] += 2
+    assert call(base_args(snaps=bad)) == ar.ATTNRES_EINVAL
+    alias = [A + (10 + i) * ROW for i in range(30)]
+    assert call(base_args(snaps=alias, out_norm=alias[25])) == ar.ATTNRES_EALIAS
     assert call(base_args(snaps=None), n=2) == ar.ATTNRES_EINVAL
 
 
@@ -164,8 +171,12 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
+    # more sources than one pass: workgroup per token in batches, at every M
+    assert ar.attnres_plan(1, 13, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
     with pytest.raises(ar.AttnResError):
-        ar.attnres_plan(1, 13, 7168)
+        ar.attnres_plan(1, 65, 7168)
     with pytest.raises(ar.AttnResError):
         ar.attnres_plan(1, 4, 7170)
 
@@ -186,6 +197,11 @@ def test_set_variant_validation():
         assert ar.attnres_plan(3, 4, 7168) == (2, 14, 64)
         ar.attnres_set_variant(1, 1)
         assert ar.attnres_plan(1, 4, 7168) == (1, 1, 896)
+        with pytest.raises(ar.AttnResError):  # no one-vector batched kernel
+            ar.attnres_plan(1, 13, 7168)
+        ar.attnres_set_variant(2, 2)
+        with pytest.raises(ar.AttnResError):  # the split kernel takes one pass only
+            ar.attnres_plan(1, 13, 7168)
     finally:
         ar.attnres_set_variant(0, 0)
 

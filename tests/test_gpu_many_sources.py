@@ -1,0 +1,88 @@
+"""GPU parity beyond one pass of sources: 13..64 snapshots.
+
+The page "[#20545][perf] Kimi K3: fold the MoE-tail additions into the next
+attention-residual", section "Model", sends calls with more than 12 snapshot
+sources down an unfused fallback.  Here kernel W takes them in batches of 12
+with the running softmax carried across batches.  Checked against the oracle
+(out_prefix bit-exact, out_norm and the mixture within 2 bf16 ulps or 1e-2)
+across batch boundaries (13, 24, 25, 36, 64 sources), ragged H, one and many
+tokens, both vector widths, with and without the second addend.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import parity as P
+from attention_residual_rmsnorm_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_residual_rmsnorm_amd as ar
+
+    ar.library()
+    ar.attnres_init()
+    yield ar
+    ar.attnres_set_variant(0, 0)
+
+
+@pytest.fixture
+def variant(request, ar):
+    v, param = request.param
+    ar.attnres_set_variant(v, param)
+    yield (v, param)
+    ar.attnres_set_variant(0, 0)
+
+
+SHAPES = [(1, 7168, 13), (3, 7168, 24), (2, 7168, 25), (5, 1000, 36), (2, 520, 64), (33, 7168, 30),
+          (2, 7176, 14), (3, 16384, 20), (1, 8, 64), (260, 512, 13)]
+
+
+@pytest.mark.parametrize("variant", [(0, 0), (1, 2), (1, 4)], ids=["auto", "W2", "W4"], indirect=True)
+@pytest.mark.parametrize("M,H,N", SHAPES)
+def test_many_sources(ar, orc, variant, M, H, N):
+    try:
+        ar.attnres_plan(M, N, H)
+    except ar.AttnResError:
+        pytest.skip("variant not available for this size")
+    case = W.make_case(cfg=85, M=M, H=H, N=N, add2=(N % 2 == 1))
+    say("many sources", M, H, N, "variant", variant, ar.attnres_plan(M, N, H))
+    gp, gn, gm = P.run_gpu_mix(case)
+    rp, rn, rm = P.run_oracle_mix(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+    P.assert_mix_parity(gm, rm, "M=%d H=%d N=%d" % (M, H, N))
+
+
+def test_many_sources_scaled_and_presummed(ar, orc):
+    """Sources of very different magnitudes across batches (the scaled
+    workload's structure), and add2 == one pre-summed addend bitwise."""
+    import dataclasses
+
+    import pins
+
+    case = W.make_case(cfg=86, M=4, N=40, add2=True, special="scaled")
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "scaled N=40")
+    t = pins.bits_of(pins.tbf(case.add) + pins.tbf(case.add2))
+    b = P.run_gpu(dataclasses.replace(case, add=t, add2=None))
+    assert np.array_equal(gp, b[0]) and np.array_equal(gn, b[1])
+
+
+def test_many_sources_deterministic(ar):
+    case = W.make_case(cfg=87, M=16, N=30, add2=True)
+    first = P.run_gpu(case)
+    for _ in range(5):
+        again = P.run_gpu(case)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
