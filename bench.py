@@ -404,6 +404,36 @@ def tap_suite(launcher, calls=64):
     return out
 
 
+def prefill_suite(launcher, calls=8):
+    """Prefill-sized calls (M beyond the decode window, one launch): µs per call
+    and GB/s at N = 12, graph replay over >= 1 GB of rotating buffer sets."""
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    out = {}
+    for M in (1024, 4096):
+        N = 12
+        case = W.make_case(cfg=91, M=M, N=N, add2=True)
+        nbytes = call_bytes(M, case.H, N, True)
+        rotate = max(2, int(1.1e9 // nbytes) + 1)
+        sets = []
+        for r in range(rotate):
+            t = [dev(x) for x in [case.prefix, case.add, case.add2] + case.snapshots + [case.query, case.gamma]]
+            op, on = torch.empty_like(t[0]), torch.empty_like(t[0])
+            sets.append((launcher.fused_args(t[0], t[1], t[2], t[3:3 + N], t[-2], t[-1], case.eps, op, on),
+                         t, op, on))
+        sec, _ = graph_time(lambda s: [launcher.run_fused(sets[k % rotate][0], s) for k in range(calls)], 6, 2)
+        us = sec / calls * 1e6
+        out["m%d_n%d" % (M, N)] = {"M": M, "N": N, "us_per_call": round(us, 2),
+                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                   "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}
+        log("prefill %s" % out["m%d_n%d" % (M, N)])
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -523,6 +553,7 @@ def main():
         log("fold: %s" % result["fold"])
         result["latency_us"] = latency_suite(launcher)
         result["tap"] = tap_suite(launcher)
+        result["prefill"] = prefill_suite(launcher)
         if not args.no_cpu_baseline:
             threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
             result["cpu_baseline"] = cpu_baseline(chain, threads)
