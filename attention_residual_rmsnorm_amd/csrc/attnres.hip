@@ -286,39 +286,57 @@ __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, cons
 // owns vectors tid + j*blockDim.x, j < VPT, of the row (coalesced 16-byte
 // loads).  blockDim.x is a multiple of 64, at most MAXB.
 //
-// All of the token's loads are issued at once, in the order query, gamma,
-// prefix, add, add2, snapshot 0..N-1; the hardware returns them in that
-// order.  The sources are then consumed in that order, p' first, in groups
-// of up to G (the last source alone): A2 for the group, its token-wide sums,
-// its logits, and its share of A4 under a running maximum and running sum of
-// the softmax (what was gathered so far is rescaled when the maximum grows).
-// A group's work runs while later sources are still in flight, so after the
-// last load lands only one source's step and A5 remain.
+// The token's sources are p' (from prefix, add, add2) and snapshots 0..N-1,
+// consumed in that order in groups of up to G (the last source alone): A2 for
+// the group, its token-wide sums, its logits, and its share of A4 under a
+// running maximum and running sum of the softmax (what was gathered so far is
+// rescaled when the maximum grows).  Loads are software-pipelined LA groups
+// ahead: the loads of group g + LA are issued, then group g is mixed, so each
+// group's work runs while later groups are in flight and after the last load
+// lands only one source's step and A5 remain.  (A CU accepts loads only as
+// fast as memory drains them: a wave that issued all of its loads before any
+// work would sit in the issue phase for most of the load time.)
 
-// Sources in arrival order: k[0] = p', k[1 + s] = snapshot s.
-template <int NS, bool ADD2, int VPT>
-__device__ __forceinline__ void load_token(const Params& p, int64_t row, const int (&vc)[VPT], uint4 (&q)[VPT],
-                                           uint4 (&g)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT], uint4 (&c)[VPT],
-                                           uint4 (&k)[NS + 1][VPT])
+// Issue-order fence across the workgroup's waves: a bare s_barrier (no
+// memory fence, no wait on outstanding loads).  A CU accepts loads only as
+// fast as memory drains them, and each SIMD keeps issuing from its oldest
+// wave, so without it a SIMD's first wave would issue all of its sources
+// before its second wave issued one: the data would arrive wave by wave and
+// no source group would be complete until late.  With a fence after each
+// source every wave issues source s before any issues source s + 1, so the
+// sources arrive in order across the workgroup and each group can be mixed
+// while the next is in flight.
+__device__ __forceinline__ void issue_fence()
 {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        q[j] = p.query[vc[j]];
-        g[j] = p.gamma[vc[j]];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-        a[j] = load_stream(&p.prefix[row + vc[j]]);
-        b[j] = load_stream(&p.add[row + vc[j]]);
-        c[j] = ADD2 ? load_stream(&p.add2[row + vc[j]]) : make_uint4(0u, 0u, 0u, 0u);
-    }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Loads of sources [S0, S1) of a batch, one issue_fence after each source.
+// With HASP the batch starts with p' (source 0: prefix, add, add2) and source
+// s >= 1 is snap[s - 1]; otherwise source s is snap[s].
+template <int S0, int S1, bool HASP, bool ADD2, int VPT, int NK>
+__device__ __forceinline__ void issue_range(const Params& p, const uint4* const* snap, int64_t row,
+                                            const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
+                                            uint4 (&c)[VPT], uint4 (&k)[NK][VPT])
+{
+    if constexpr (S0 < S1) {
+        if constexpr (HASP && S0 == 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+            for (int j = 0; j < VPT; ++j) {
+                a[j] = load_stream(&p.prefix[row + vc[j]]);
+                b[j] = load_stream(&p.add[row + vc[j]]);
+                c[j] = ADD2 ? load_stream(&p.add2[row + vc[j]]) : make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else {
+            const uint4* src = snap[HASP ? S0 - 1 : S0];
 #pragma unroll
-        for (int j = 0; j < VPT; ++j)
-            k[1 + s][j] = load_stream(&p.snap[s][row + vc[j]]);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < VPT; ++j)
+                k[S0][j] = load_stream(&src[row + vc[j]]);
+        }
+        issue_fence();
+        issue_range<S0 + 1, S1, HASP, ADD2, VPT, NK>(p, snap, row, vc, a, b, c, k);
     }
 }
 
@@ -470,30 +488,69 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The groups over S sources: G at a time, the last source on its own.  Group
-// gi uses LDS slot gi % 2 (a slot is written again two groups later, after
-// every thread has passed the barriers that end its readers' use; a batch
-// of sources always starts at gi = 0 and the group before it, the previous
-// batch's last, ends on an odd gi, so consecutive groups never share a slot).
-// FIRSTBATCH: the first group starts the running softmax.
-template <int S, int G, int VPT, int G0, int GI, bool FIRSTBATCH>
-__device__ __forceinline__ void mix_groups(const uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
-                                           Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8],
-                                           const Params& p, int tid)
-{
-    if constexpr (G0 < S) {
-        constexpr int LAST = S - 1;
-        constexpr int n = G0 == LAST ? 1 : (G < LAST - G0 ? G : LAST - G0);
-        mix_group<n, VPT, FIRSTBATCH && G0 == 0>(&k[G0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
-        mix_groups<S, G, VPT, G0 + n, GI + 1, FIRSTBATCH>(k, q, ok, mx, rows, tot, p, tid);
-    }
-}
-
-// Number of groups mix_groups makes of S sources (G at a time, the last alone).
+// Groups over S sources: G at a time over sources [0, S-1), then the last
+// source alone.  group_count is their number, group_start(i) the first source
+// of group i (group_start(group_count) = S).
 template <int S, int G>
 constexpr int group_count()
 {
     return S <= 1 ? S : 1 + (S - 1 + G - 1) / G;
+}
+
+template <int S, int G>
+constexpr int group_start(int i)
+{
+    return S <= 1 ? (i == 0 ? 0 : S) : i < (S - 1 + G - 1) / G ? i * G : (i == (S - 1 + G - 1) / G ? S - 1 : S);
+}
+
+// Kernel W's pipeline over one batch of S sources, step GI: issue the loads of
+// group GI + LA, then (batch with p', step 0) apply A1 and store out_prefix,
+// then mix group GI.  Group gi uses LDS slot gi % 2.  Any reuse of a slot is
+// ordered by the two barriers of every group: a thread writes a group's rows
+// only after the previous group's second barrier (wave 0 has read that
+// group's rows), and wave 0 writes a group's totals only after its first
+// barrier (every thread has read the previous totals).  FIRSTBATCH: the first
+// group starts the running softmax.
+template <int S, int G, int LA, int GI, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT>
+__device__ __forceinline__ void stream_groups(const Params& p, const uint4* const* snap, int64_t row,
+                                              const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
+                                              uint4 (&c)[VPT], uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
+                                              Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8], int tid,
+                                              int nthreads)
+{
+    constexpr int NG = group_count<S, G>();
+    if constexpr (GI < NG) {
+        if constexpr (GI + LA < NG)
+            issue_range<group_start<S, G>(GI + LA), group_start<S, G>(GI + LA + 1), HASP, ADD2, VPT, S>(
+                p, snap, row, vc, a, b, c, k);
+        if constexpr (HASP && GI == 0) {
+            // A1
+            fold_add<ADD2, VPT>(a, b, c, k[0]);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j)
+                if (ok[j])
+                    p.out_prefix[row + tid + j * nthreads] = k[0][j];
+        }
+        constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
+        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
+        stream_groups<S, G, LA, GI + 1, HASP, FIRSTBATCH, ADD2, VPT>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows,
+                                                                     tot, tid, nthreads);
+    }
+}
+
+// One batch of S sources through the pipeline: the first LA groups' loads,
+// then the steps.
+template <int S, int G, int LA, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT>
+__device__ __forceinline__ void stream_batch(const Params& p, const uint4* const* snap, int64_t row,
+                                             const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
+                                             uint4 (&c)[VPT], uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
+                                             Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8], int tid,
+                                             int nthreads)
+{
+    constexpr int NG = group_count<S, G>();
+    issue_range<0, group_start<S, G>(LA < NG ? LA : NG), HASP, ADD2, VPT, S>(p, snap, row, vc, a, b, c, k);
+    stream_groups<S, G, LA, 0, HASP, FIRSTBATCH, ADD2, VPT>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows, tot,
+                                                            tid, nthreads);
 }
 
 // LDS set-up shared by both forms of kernel W: entries of absent waves stay
@@ -550,7 +607,7 @@ __device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, co
     __syncthreads(); // LDS reuse by the next token
 }
 
-template <int NS, bool ADD2, int VPT, int MAXB, int G>
+template <int NS, bool ADD2, int VPT, int MAXB, int G, int LA>
 __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 {
     constexpr int S = NS + 1;
@@ -576,21 +633,15 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
             ok[j] = v < nvec;
             vc[j] = ok[j] ? v : nvec - 1; // past the row: reread the last vector, never stored
         }
-        load_token<NS, ADD2, VPT>(p, row, vc, q, g, a, b, c, k);
-        // keep every load above this point: nothing that waits on a load may be
-        // scheduled between them
-        __builtin_amdgcn_sched_barrier(0);
-
-        // A1
-        fold_add<ADD2, VPT>(a, b, c, k[0]);
 #pragma unroll
-        for (int j = 0; j < VPT; ++j)
-            if (ok[j])
-                p.out_prefix[row + tid + j * nthreads] = k[0][j];
-
-        // A2-A4
+        for (int j = 0; j < VPT; ++j) {
+            q[j] = p.query[vc[j]];
+            g[j] = p.gamma[vc[j]];
+        }
+        // A1 (in step 0), A2-A4
         Mix<VPT> mx;
-        mix_groups<S, G, VPT, 0, 0, true>(k, q, ok, mx, rows, tot, p, tid);
+        stream_batch<S, G, LA, true, true, ADD2, VPT>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot, tid,
+                                                      nthreads);
         // A5
         wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
     }
@@ -600,34 +651,19 @@ __global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
 // Kernel W for more than MAX_SNAP snapshots: the sources come in batches that
 // reuse the same registers.  Batch 0 is p' and snapshots 0..MAX_SNAP-1 (the
 // code of fwd_wg for N = MAX_SNAP); then pl.n_full batches of MAX_SNAP
-// snapshots and a last batch of NB_LAST.  Each batch's loads are issued at
-// once and its groups mixed into the same running softmax as they arrive.
+// snapshots and a last batch of NB_LAST, each through the same load pipeline
+// and mixed into the same running softmax.
 struct ParamsLong {
     Params p;
     const uint4* more[MAX_SNAP_LONG - MAX_SNAP]; // snapshots MAX_SNAP, MAX_SNAP + 1, ...
     int n_full;                                  // full batches after batch 0
 };
 
-template <int NB, int VPT>
-__device__ __forceinline__ void load_batch(const uint4* const* src, int64_t row, const int (&vc)[VPT],
-                                           uint4 (&k)[NB][VPT])
-{
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-#pragma unroll
-        for (int j = 0; j < VPT; ++j)
-            k[s][j] = load_stream(&src[s][row + vc[j]]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-template <int NB_LAST, bool ADD2, int VPT, int MAXB, int G>
+template <int NB_LAST, bool ADD2, int VPT, int MAXB, int G, int LA>
 __global__ __launch_bounds__(MAXB) void fwd_wg_long(ParamsLong pl)
 {
     constexpr int B = MAX_SNAP;
     constexpr int MAXW = MAXB / 64;
-    static_assert(group_count<B + 1, G>() % 2 == 0 && group_count<B, G>() % 2 == 0,
-                  "batches must end on an odd group index");
     __shared__ __align__(16) float rows[2][64 * 8];
     __shared__ __align__(16) float tot[2][8];
     __shared__ float red2[MAXW];
@@ -649,29 +685,27 @@ __global__ __launch_bounds__(MAXB) void fwd_wg_long(ParamsLong pl)
             ok[j] = v < nvec;
             vc[j] = ok[j] ? v : nvec - 1;
         }
-        Mix<VPT> mx;
-        {
-            uint4 k[B + 1][VPT], a[VPT], b[VPT], c[VPT];
-            load_token<B, ADD2, VPT>(p, row, vc, q, g, a, b, c, k);
-            __builtin_amdgcn_sched_barrier(0);
-            fold_add<ADD2, VPT>(a, b, c, k[0]);
 #pragma unroll
-            for (int j = 0; j < VPT; ++j)
-                if (ok[j])
-                    p.out_prefix[row + tid + j * nthreads] = k[0][j];
-            mix_groups<B + 1, G, VPT, 0, 0, true>(k, q, ok, mx, rows, tot, p, tid);
+        for (int j = 0; j < VPT; ++j) {
+            q[j] = p.query[vc[j]];
+            g[j] = p.gamma[vc[j]];
+        }
+        Mix<VPT> mx;
+        uint4 a[VPT], b[VPT], c[VPT];
+        {
+            uint4 k[B + 1][VPT];
+            stream_batch<B + 1, G, LA, true, true, ADD2, VPT>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot,
+                                                              tid, nthreads);
         }
         for (int bi = 0; bi < pl.n_full; ++bi) {
             uint4 k[B][VPT];
-            load_batch<B, VPT>(pl.more + bi * B, row, vc, k);
-            __builtin_amdgcn_sched_barrier(0);
-            mix_groups<B, G, VPT, 0, 0, false>(k, q, ok, mx, rows, tot, p, tid);
+            stream_batch<B, G, LA, false, false, ADD2, VPT>(p, pl.more + bi * B, row, vc, a, b, c, k, q, ok, mx,
+                                                            rows, tot, tid, nthreads);
         }
         {
             uint4 k[NB_LAST][VPT];
-            load_batch<NB_LAST, VPT>(pl.more + pl.n_full * B, row, vc, k);
-            __builtin_amdgcn_sched_barrier(0);
-            mix_groups<NB_LAST, G, VPT, 0, 0, false>(k, q, ok, mx, rows, tot, p, tid);
+            stream_batch<NB_LAST, G, LA, false, false, ADD2, VPT>(p, pl.more + pl.n_full * B, row, vc, a, b, c, k,
+                                                                  q, ok, mx, rows, tot, tid, nthreads);
         }
         wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
     }
@@ -872,10 +906,13 @@ __global__ __launch_bounds__(256) void bf16_add_kernel(const uint4* a, const uin
 
 using Kernel = void (*)(Params);
 
+constexpr int WG_GROUP = 2;     // sources per reduction group in kernel W
+constexpr int WG_LOOKAHEAD = 1; // groups whose loads are in flight ahead of the one being mixed
+
 template <bool A2, int VPT, int MAXB, int G, int... I>
 constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_wg<I, A2, VPT, MAXB, G>...}};
+    return {{&fwd_wg<I, A2, VPT, MAXB, G, WG_LOOKAHEAD>...}};
 }
 
 template <bool A2, int MAXB, int MAXC, int WPE, int... I>
@@ -887,7 +924,6 @@ constexpr std::array<Kernel, sizeof...(I)> split_table(std::integer_sequence<int
 using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
 
 // [add2][N]
-constexpr int WG_GROUP = 4; // sources per reduction group in kernel W
 const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024, WG_GROUP>(Seq{}),
                                                   wg_table<true, 1, 1024, WG_GROUP>(Seq{})};
 const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GROUP>(Seq{}),
@@ -900,7 +936,7 @@ using KernelLong = void (*)(ParamsLong);
 template <bool A2, int VPT, int MAXB, int G, int... I>
 constexpr std::array<KernelLong, sizeof...(I)> wg_long_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_wg_long<I + 1, A2, VPT, MAXB, G>...}};
+    return {{&fwd_wg_long<I + 1, A2, VPT, MAXB, G, WG_LOOKAHEAD>...}};
 }
 
 using SeqBatch = std::make_integer_sequence<int, MAX_SNAP>;

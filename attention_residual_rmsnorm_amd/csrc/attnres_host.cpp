@@ -161,20 +161,17 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     if (force_variant == 2)
         return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     // Automatic, from per-call times of every variant on MI355X at H = 7168
-    // (graph replay, inputs cold in HBM, M = 1..512, N = 1, 4, 12):
+    // (graph replay, inputs cold in HBM, M = 1..512, N = 1, 4, 8, 12):
     //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
-    //  * M <= 32: the call is latency-bound; 2-wave chunks spread each token
-    //    over the most CUs;
-    //  * M <= 128 with N >= 8: 4-wave chunks;
-    //  * 256 < M <= 512 with N >= 8: two 7-wave halves per token, one round of
-    //    workgroups instead of a second, partial round of whole tokens;
+    //  * M <= 16, or M <= 32 with N >= 5: the call is latency-bound; 2-wave
+    //    chunks spread each token over the most CUs;
+    //  * M <= 64 with N >= 8: 4-wave chunks;
     //  * otherwise one workgroup per token.
     if (n > 2) {
-        if (M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 2, pl))
+        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_SMALL_TOKENS_WIDE);
+        if (small && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
         if (n >= 8 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
-            return ATTNRES_OK;
-        if (n >= 8 && M > 256 && M <= MAX_SPLIT_TOKENS && plan_split(M, nvec, 7, pl))
             return ATTNRES_OK;
     }
     if (plan_wg(M, nvec, 0, pl))

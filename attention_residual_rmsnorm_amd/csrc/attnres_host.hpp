@@ -13,8 +13,12 @@ constexpr int MAX_SNAP_LONG = 64;        // == ATTNRES_MAX_SNAPSHOTS: W in batch
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-constexpr int SPLIT_SMALL_TOKENS = 32;   // automatic dispatch: 2-wave split up to this many tokens
-constexpr int SPLIT_MID_TOKENS = 128;    // automatic dispatch: 4-wave split up to this many tokens (N >= 8)
+// automatic dispatch (see make_plan): 2-wave split up to SPLIT_SMALL_TOKENS
+// tokens (N >= 3), or SPLIT_SMALL_TOKENS_WIDE (N >= 5); 4-wave split up to
+// SPLIT_MID_TOKENS (N >= 8)
+constexpr int SPLIT_SMALL_TOKENS = 16;
+constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
+constexpr int SPLIT_MID_TOKENS = 64;
 
 struct Plan {
     int variant = 0; // 1 = workgroup per token, 2 = split hidden

@@ -162,12 +162,13 @@ def test_bf16_add_validation():
 def test_plan_is_pure_and_sane():
     # the measured automatic dispatch at H = 7168
     assert ar.attnres_plan(1, 12, 7168) == (2, 7, 128)     # 2-wave chunks
-    assert ar.attnres_plan(32, 4, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(16, 4, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(32, 5, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(32, 4, 7168)[0] == 1
     assert ar.attnres_plan(1, 2, 7168) == (1, 1, 448)      # small rows: workgroup per token
-    assert ar.attnres_plan(33, 4, 7168)[0] == 1
-    assert ar.attnres_plan(128, 8, 7168) == (2, 4, 256)    # 4-wave chunks
-    assert ar.attnres_plan(129, 12, 7168)[0] == 1
-    assert ar.attnres_plan(384, 12, 7168) == (2, 2, 448)   # two 7-wave halves
+    assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks
+    assert ar.attnres_plan(65, 12, 7168)[0] == 1
+    assert ar.attnres_plan(384, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
