@@ -130,3 +130,47 @@ def test_mix_null_is_the_plain_call(ar):
     assert rc == 0
     pp, pn = P.run_gpu(case)
     assert np.array_equal(P.host(op), pp) and np.array_equal(P.host(on), pn)
+
+
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+def test_mix_graph_replay(ar, variant):
+    """The mixture call captured into a HIP graph and replayed with fresh inputs:
+    every replay equals the eager call, bit for bit."""
+    import torch
+
+    cases = [W.make_case(cfg=84 + i, M=16, N=7, add2=True) for i in range(3)]
+    c0 = cases[0]
+    d = P.dev
+    ins = dict(prefix=d(c0.prefix), add=d(c0.add), add2=d(c0.add2), snaps=[d(s) for s in c0.snapshots],
+               query=d(c0.query), gamma=d(c0.gamma))
+    outp, outn, outm = (torch.empty_like(ins["prefix"]) for _ in range(3))
+
+    def call():
+        ar.attnres_add_rmsnorm_mix_fwd(ins["prefix"], ins["add"], ins["add2"], ins["snaps"], ins["query"],
+                                       ins["gamma"], c0.eps, out_prefix=outp, out_norm=outn, out_mix=outm)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(6):
+        c = cases[rep % len(cases)]
+        for key, src in (("prefix", c.prefix), ("add", c.add), ("add2", c.add2), ("query", c.query),
+                         ("gamma", c.gamma)):
+            ins[key].copy_(d(src))
+        for t, src in zip(ins["snaps"], c.snapshots):
+            t.copy_(d(src))
+        for o in (outp, outn, outm):
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ep, en, em = P.run_gpu_mix(c)
+        assert np.array_equal(P.host(outp), ep) and np.array_equal(P.host(outn), en) \
+            and np.array_equal(P.host(outm), em), "replay %d" % rep
+    assert ar.attnres_debug_timeouts() == 0
