@@ -13,12 +13,13 @@
 //
 // Two kernels, both HBM-bound streaming kernels (no dense contraction, so no
 // MFMA):
-//   W  one workgroup per token: all of the token's loads are in flight at
-//      once (N+1 sources x VPT 16-byte vectors per thread, in registers) and
-//      the sources are mixed group by group as they arrive, under a running
+//   W  one workgroup per token: the sources (VPT 16-byte vectors per thread,
+//      in registers) are loaded in a software pipeline, source-major across
+//      the waves, and mixed two at a time as they arrive, under a running
 //      softmax maximum and sum; each group's partials are summed on DPP
 //      within rows and by one wave across rows.  No inter-workgroup
-//      communication.  Used when there are many tokens.
+//      communication.  Used when there are many tokens, and for more than
+//      12 sources (in batches of 12).
 //   S  split hidden: C workgroups per token, each owning a contiguous chunk of
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
@@ -43,7 +44,7 @@
 
 namespace attnres {
 
-constexpr int REC_STRIDE = 32;           // records per (token, chunk) of the first exchange (>= 2*13)
+constexpr int REC_STRIDE = 64;           // records per (token, chunk) of the first exchange (>= 2*32)
 constexpr int STATE_STRIDE = 32;         // epoch word per token: one 128-byte line each
 constexpr unsigned SPIN_LIMIT = 1u << 20;
 
@@ -51,7 +52,7 @@ struct Params {
     const uint4* prefix;
     const uint4* add;
     const uint4* add2;
-    const uint4* snap[MAX_SNAP];
+    const uint4* snap[MAX_SPLIT_SNAP]; // snapshot rows (kernel W reads the first MAX_SNAP)
     const uint4* query;
     const uint4* gamma;
     uint4* out_prefix;
@@ -736,10 +737,10 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     constexpr int NV = 2 * S;
     constexpr int NVP = (NV + 3) / 4 * 4;
     constexpr int MAXROWS = MAXB / 16;
-    static_assert(S <= 16 && MAXC <= 64, "one lane per source in a row, one lane per chunk");
+    static_assert(S <= 32 && 2 * S <= REC_STRIDE && MAXC <= 64, "one lane per source and per chunk");
     __shared__ __align__(16) float rows[MAXROWS * NVP];
     __shared__ __align__(16) float tot[NVP];
-    __shared__ float alpha_sh[16];
+    __shared__ float alpha_sh[32];
     __shared__ float red2[MAXB / 64];
     __shared__ float ssum_sh;
 
@@ -783,20 +784,24 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     if (tid < NV)
         publish(&rec1[chunk * REC_STRIDE + tid], tag1, tot[tid]);
 
-    // A3 in wave 0.  Lane l takes source s = l % 16 and chunks l/16, l/16 + 4,
-    // ...: all of its record loads are issued together, those not yet tagged
-    // are read again (bounded wait).  The four rows' sums are then added in
-    // row order, so every lane of source s (and every workgroup of the token)
-    // holds the same totals; the logits, their maximum and the exponentials'
-    // sum are taken across the 16 lanes of a row, and row 0 writes alpha.
+    // A3 in wave 0.  SL lanes hold one set of sources (16 for up to 16
+    // sources, 32 for up to 32) and the wave holds NR = 64/SL sets: lane l
+    // takes source s = l % SL and chunks l/SL, l/SL + NR, ...; all of its
+    // record loads are issued together, those not yet tagged are read again
+    // (bounded wait).  The NR sets' sums are then added in set order, so
+    // every lane of source s (and every workgroup of the token) holds the
+    // same totals; the logits, their maximum and the exponentials' sum are
+    // taken across the SL lanes of a set (one or two DPP rows), and lanes
+    // 0..S-1 write alpha.
     if (wave == 0) {
-        constexpr int KC = (MAXC + 3) / 4;
-        const int s = lane & 15, c0 = lane >> 4;
+        constexpr int SL = S <= 16 ? 16 : 32, NR = 64 / SL;
+        constexpr int KC = (MAXC + NR - 1) / NR;
+        const int s = lane & (SL - 1), c0 = lane / SL;
         const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
         unsigned long long w[2 * KC];
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
-            const int cc = c0 + 4 * kk;
+            const int cc = c0 + NR * kk;
             const bool use = s < S && cc < C;
             w[2 * kk] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s]) : ready_zero;
             w[2 * kk + 1] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s + 1]) : ready_zero;
@@ -815,7 +820,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk) {
-                const int cc = c0 + 4 * kk;
+                const int cc = c0 + NR * kk;
                 if (s < S && cc < C) {
                     if (tag_of(w[2 * kk]) != tag1)
                         w[2 * kk] = peek(&rec1[cc * REC_STRIDE + 2 * s]);
@@ -830,12 +835,24 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             ss += __uint_as_float((unsigned)w[2 * kk]);
             qd += __uint_as_float((unsigned)w[2 * kk + 1]);
         }
-        ss = ((__shfl(ss, s) + __shfl(ss, s + 16)) + __shfl(ss, s + 32)) + __shfl(ss, s + 48);
-        qd = ((__shfl(qd, s) + __shfl(qd, s + 16)) + __shfl(qd, s + 32)) + __shfl(qd, s + 48);
+        {
+            float st = __shfl(ss, s), qt = __shfl(qd, s);
+#pragma unroll
+            for (int r = 1; r < NR; ++r) {
+                st += __shfl(ss, s + SL * r);
+                qt += __shfl(qd, s + SL * r);
+            }
+            ss = st;
+            qd = qt;
+        }
         const float z = s < S ? rsqrtf(ss * p.inv_h + p.eps) * qd : -INFINITY;
-        const float zmax = row_max(z);
+        float zmax = row_max(z);
+        if (SL == 32) // the set's two rows (max is exact: same bits in both)
+            zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
         const float e = s < S ? __expf(z - zmax) : 0.f;
-        const float den = row_sum(e);
+        float den = row_sum(e);
+        if (SL == 32) // a + b == b + a: same bits in both rows
+            den = den + __shfl_xor(den, 16);
         if (lane < S)
             alpha_sh[lane] = e * (1.0f / den);
     }
@@ -922,6 +939,7 @@ constexpr std::array<Kernel, sizeof...(I)> split_table(std::integer_sequence<int
 }
 
 using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
+using SeqSplitSmall = std::make_integer_sequence<int, MAX_SPLIT_SNAP + 1>;
 
 // [add2][N]
 const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024, WG_GROUP>(Seq{}),
@@ -945,8 +963,9 @@ const std::array<KernelLong, MAX_SNAP> kWgLong2[2] = {wg_long_table<false, 2, 51
 const std::array<KernelLong, MAX_SNAP> kWgLong4[2] = {wg_long_table<false, 4, 512, WG_GROUP>(SeqBatch{}),
                                                       wg_long_table<true, 4, 512, WG_GROUP>(SeqBatch{})};
 // split hidden, 1-2 waves per workgroup (up to 32 chunks)
-const std::array<Kernel, MAX_SNAP + 1> kSpSmall[2] = {split_table<false, 128, MAX_CHUNKS, 1>(Seq{}),
-                                                      split_table<true, 128, MAX_CHUNKS, 1>(Seq{})};
+// (up to MAX_SPLIT_SNAP snapshots: the 1-2-wave family has the registers)
+const std::array<Kernel, MAX_SPLIT_SNAP + 1> kSpSmall[2] = {
+    split_table<false, 128, MAX_CHUNKS, 1>(SeqSplitSmall{}), split_table<true, 128, MAX_CHUNKS, 1>(SeqSplitSmall{})};
 // split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
 const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8, 4>(Seq{}),
                                                       split_table<true, 512, 8, 4>(Seq{})};
@@ -1022,7 +1041,7 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.prefix = static_cast<const uint4*>(prefix);
     p.add = static_cast<const uint4*>(add);
     p.add2 = static_cast<const uint4*>(add2);
-    for (int s = 0; s < n_snapshots && s < MAX_SNAP; ++s)
+    for (int s = 0; s < n_snapshots && s < MAX_SPLIT_SNAP; ++s)
         p.snap[s] = static_cast<const uint4*>(snapshots[s]);
     p.query = static_cast<const uint4*>(query);
     p.gamma = static_cast<const uint4*>(gamma);
@@ -1037,7 +1056,7 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.spin_limit = SPIN_LIMIT;
 
     const int a2 = add2 ? 1 : 0;
-    if (n_snapshots > MAX_SNAP) {
+    if (n_snapshots > MAX_SNAP && pl.variant == 1) {
         // batched sources: batch 0 = p' + snapshots 0..11, then full batches of
         // 12 and a last batch of 1..12
         ParamsLong lp{};
@@ -1064,7 +1083,7 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
         p.rec2 = sc->rec2;
         p.state = sc->state;
         p.timeouts = sc->timeouts;
-        fn = (pl.threads <= 128 ? kSpSmall : kSpLarge)[a2][n_snapshots];
+        fn = pl.threads <= 128 ? kSpSmall[a2][n_snapshots] : kSpLarge[a2][n_snapshots];
     } else {
         fn = (pl.vpt == 1 ? kWg1 : pl.vpt == 2 ? kWg2 : kWg4)[a2][n_snapshots];
     }

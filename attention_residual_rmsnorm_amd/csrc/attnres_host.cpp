@@ -148,35 +148,42 @@ bool valid_override(int variant, int param)
 int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, Plan& pl)
 {
     const int nvec = (int)(H / 8);
-    if (n > MAX_SNAP) {
-        // more sources than one pass holds: workgroup per token, sources in
-        // batches of MAX_SNAP (instantiated for 2 and 4 vectors per thread)
-        if (force_variant == 2 || (force_variant == 1 && force_param == 1))
+    // More sources than one pass of kernel W holds: W takes them in batches of
+    // MAX_SNAP (instantiated for 2 and 4 vectors per thread); the split kernel
+    // takes up to MAX_SPLIT_SNAP in its 1-2-wave family.
+    const bool many = n > MAX_SNAP;
+    const int wg_vpt = many ? nvec <= 1024 ? 2 : 4 : 0;
+    const bool split_ok = !many || n <= MAX_SPLIT_SNAP;
+    if (force_variant == 1) {
+        if (many && force_param == 1)
             return ATTNRES_EINVAL;
-        const int vpt = force_variant == 1 && force_param ? force_param : nvec <= 1024 ? 2 : 4;
-        return plan_wg(M, nvec, vpt, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+        return plan_wg(M, nvec, force_param ? force_param : wg_vpt, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     }
-    if (force_variant == 1)
-        return plan_wg(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
-    if (force_variant == 2)
-        return plan_split(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    if (force_variant == 2) {
+        if (!split_ok || (many && force_param > 2))
+            return ATTNRES_EINVAL;
+        return plan_split(M, nvec, many && force_param == 0 ? 2 : force_param, pl) ? ATTNRES_OK
+                                                                                    : ATTNRES_EINVAL;
+    }
     // Automatic, from per-call times of every variant on MI355X at H = 7168
     // (graph replay, inputs cold in HBM, M = 1..512, N = 1, 4, 8, 12):
     //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
     //  * M <= 16, or M <= 32 with N >= 5: the call is latency-bound; 2-wave
     //    chunks spread each token over the most CUs;
-    //  * M <= 64 with N >= 8: 4-wave chunks;
+    //  * M <= 64 with N >= 8: 4-wave chunks, or 2-wave chunks above 12
+    //    sources (only that family holds them);
     //  * otherwise one workgroup per token.
     if (n > 2) {
-        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_SMALL_TOKENS_WIDE);
-        if (small && plan_split(M, nvec, 2, pl))
+        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_SMALL_TOKENS_WIDE) ||
+                           (many && M <= SPLIT_MID_TOKENS);
+        if (small && split_ok && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
-        if (n >= 8 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
+        if (n >= 8 && !many && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;
     }
-    if (plan_wg(M, nvec, 0, pl))
+    if (plan_wg(M, nvec, wg_vpt, pl))
         return ATTNRES_OK;
-    return plan_split(M, nvec, 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+    return split_ok && plan_split(M, nvec, many ? 2 : 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
 }
 
 int validate_add(const void* a, const void* b, const void* out, int64_t n)

@@ -10,6 +10,7 @@ namespace attnres {
 
 constexpr int MAX_SNAP = 12;             // snapshots of one pass (kernel S, and W's batch size)
 constexpr int MAX_SNAP_LONG = 64;        // == ATTNRES_MAX_SNAPSHOTS: W in batches of MAX_SNAP
+constexpr int MAX_SPLIT_SNAP = 31;       // split hidden, 1-2 waves per workgroup: up to 32 sources
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel

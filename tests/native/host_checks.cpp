@@ -84,7 +84,8 @@ int main()
                                 EXPECT(pl.grid >= 1);
                                 EXPECT((int64_t)pl.threads * pl.vpt * pl.chunks * 8 >= h);
                                 if (n > MAX_SNAP)
-                                    EXPECT(pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4));
+                                    EXPECT((pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4)) ||
+                                           (pl.variant == 2 && n <= MAX_SPLIT_SNAP && pl.threads <= 128));
                                 if (pl.variant == 2)
                                     EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
                                            pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&

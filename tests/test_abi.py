@@ -172,8 +172,13 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
-    # more sources than one pass: workgroup per token in batches, at every M
-    assert ar.attnres_plan(1, 13, 7168) == (1, 1, 448)
+    # more sources than one pass: the 2-wave split up to 31 snapshots at small
+    # M, else workgroup per token in batches
+    assert ar.attnres_plan(1, 13, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(32, 31, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(1, 32, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(64, 13, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(65, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
     assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
     with pytest.raises(ar.AttnResError):
@@ -201,7 +206,11 @@ def test_set_variant_validation():
         with pytest.raises(ar.AttnResError):  # no one-vector batched kernel
             ar.attnres_plan(1, 13, 7168)
         ar.attnres_set_variant(2, 2)
-        with pytest.raises(ar.AttnResError):  # the split kernel takes one pass only
+        assert ar.attnres_plan(1, 31, 7168) == (2, 7, 128)
+        with pytest.raises(ar.AttnResError):  # beyond the split kernel's registers
+            ar.attnres_plan(1, 32, 7168)
+        ar.attnres_set_variant(2, 4)
+        with pytest.raises(ar.AttnResError):  # more than 12 only in the 1-2-wave family
             ar.attnres_plan(1, 13, 7168)
     finally:
         ar.attnres_set_variant(0, 0)

@@ -46,10 +46,11 @@ def variant(request, ar):
 
 
 SHAPES = [(1, 7168, 13), (3, 7168, 24), (2, 7168, 25), (5, 1000, 36), (2, 520, 64), (33, 7168, 30),
-          (2, 7176, 14), (3, 16384, 20), (1, 8, 64), (260, 512, 13)]
+          (2, 7176, 14), (3, 16384, 20), (1, 8, 64), (260, 512, 13), (1, 7168, 31), (17, 1000, 16), (8, 520, 31)]
 
 
-@pytest.mark.parametrize("variant", [(0, 0), (1, 2), (1, 4)], ids=["auto", "W2", "W4"], indirect=True)
+@pytest.mark.parametrize("variant", [(0, 0), (1, 2), (1, 4), (2, 1), (2, 2)], ids=["auto", "W2", "W4", "S1w", "S2w"],
+                         indirect=True)
 @pytest.mark.parametrize("M,H,N", SHAPES)
 def test_many_sources(ar, orc, variant, M, H, N):
     try:
