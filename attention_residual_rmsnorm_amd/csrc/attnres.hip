@@ -297,6 +297,9 @@ __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, cons
 // lands only one source's step and A5 remain.  (A CU accepts loads only as
 // fast as memory drains them: a wave that issued all of its loads before any
 // work would sit in the issue phase for most of the load time.)
+// With VPT = 2 (hidden sizes up to 8192) the kernel is held to 128 VGPRs, so
+// two workgroups share a CU once there are more tokens than CUs: the second
+// token's loads then overlap the first one's reduction and tail.
 
 // Issue-order fence across the workgroup's waves: a bare s_barrier (no
 // memory fence, no wait on outstanding loads).  A CU accepts loads only as
@@ -314,6 +317,34 @@ __device__ __forceinline__ void issue_fence()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Base address of a token's row, held in scalar registers as one opaque
+// value: otherwise the compiler re-splits it into (tensor + thread offset),
+// hoisted per source out of the token loop at two VGPRs each, plus the row.
+// A load is then this base plus the thread's one 32-bit byte offset.  The
+// pointer is typed in the global address space: the opaque value hides where
+// it came from, and a generic pointer would turn every load into a flat load,
+// which also counts against the LDS counter and so serialises with LDS work.
+typedef const __attribute__((address_space(1))) char* gptr_t;
+typedef const __attribute__((address_space(1))) uint32_t* gword_t;
+
+__device__ __forceinline__ gptr_t row_base(const uint4* tensor, int64_t row)
+{
+    gptr_t b = (gptr_t)(const void*)(tensor + row); // generic -> global: same address
+    asm volatile("" : "+s"(b));
+    return b;
+}
+
+__device__ __forceinline__ uint4 load_row(gptr_t base, unsigned byte_off)
+{
+    const gword_t w = reinterpret_cast<gword_t>(base + byte_off);
+    uint4 r;
+    r.x = __builtin_nontemporal_load(w + 0);
+    r.y = __builtin_nontemporal_load(w + 1);
+    r.z = __builtin_nontemporal_load(w + 2);
+    r.w = __builtin_nontemporal_load(w + 3);
+    return r;
+}
+
 // Loads of sources [S0, S1) of a batch, one issue_fence after each source.
 // With HASP the batch starts with p' (source 0: prefix, add, add2) and source
 // s >= 1 is snap[s - 1]; otherwise source s is snap[s].
@@ -324,17 +355,21 @@ __device__ __forceinline__ void issue_range(const Params& p, const uint4* const*
 {
     if constexpr (S0 < S1) {
         if constexpr (HASP && S0 == 0) {
+            gptr_t pa = row_base(p.prefix, row);
+            gptr_t pb = row_base(p.add, row);
+            gptr_t pc = ADD2 ? row_base(p.add2, row) : nullptr;
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
-                a[j] = load_stream(&p.prefix[row + vc[j]]);
-                b[j] = load_stream(&p.add[row + vc[j]]);
-                c[j] = ADD2 ? load_stream(&p.add2[row + vc[j]]) : make_uint4(0u, 0u, 0u, 0u);
+                const unsigned off = (unsigned)vc[j] * 16u;
+                a[j] = load_row(pa, off);
+                b[j] = load_row(pb, off);
+                c[j] = ADD2 ? load_row(pc, off) : make_uint4(0u, 0u, 0u, 0u);
             }
         } else {
-            const uint4* src = snap[HASP ? S0 - 1 : S0];
+            gptr_t src = row_base(snap[HASP ? S0 - 1 : S0], row);
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
-                k[S0][j] = load_stream(&src[row + vc[j]]);
+                k[S0][j] = load_row(src, (unsigned)vc[j] * 16u);
         }
         issue_fence();
         issue_range<S0 + 1, S1, HASP, ADD2, VPT, NK>(p, snap, row, vc, a, b, c, k);
@@ -609,7 +644,7 @@ __device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, co
 }
 
 template <int NS, bool ADD2, int VPT, int MAXB, int G, int LA>
-__global__ __launch_bounds__(MAXB) void fwd_wg(Params p)
+__global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
 {
     constexpr int S = NS + 1;
     constexpr int MAXW = MAXB / 64;
@@ -661,7 +696,7 @@ struct ParamsLong {
 };
 
 template <int NB_LAST, bool ADD2, int VPT, int MAXB, int G, int LA>
-__global__ __launch_bounds__(MAXB) void fwd_wg_long(ParamsLong pl)
+__global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLong pl)
 {
     constexpr int B = MAX_SNAP;
     constexpr int MAXW = MAXB / 64;
