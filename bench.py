@@ -26,10 +26,17 @@ Also reported on the same JSON line:
                 the current kernel source
   cpu_baseline  the CPU oracle on the same chain (all 256 tokens, one
                 micro-batch), parallel over token blocks
-  latency_us    per-call time of the small named calls over 16 rotated buffer
-                sets: graph replay, and eager back-to-back launches
+  cpu_latency   the CPU oracle on each small named call (median of 5), one
+                thread and token-parallel
+  latency_us    per-call time of the small named calls with inputs cold in
+                HBM (>= 1.1 GB of distinct buffer sets): graph replay, and
+                eager back-to-back launches; plus a warm figure (16 sets,
+                resident in the Infinity Cache)
   fold          the pages' comparison: fused call with add2 vs the unfused
                 route (standalone add, then the fused call without add2)
+  fold_per_config  the same comparison per small named call and per kernel
+                variant: fused with add2, fused with the pre-summed addend,
+                standalone add
 
 Every timing follows a parity check against the CPU oracle.
 """
@@ -317,6 +324,41 @@ def cpu_baseline(chain, threads, min_cpu_seconds=12.0, max_passes=8):
                       "binary64, token blocks over %d threads; %.2f s wall" % (passes, threads, wall)}
 
 
+def cpu_latency(threads, repeats=5):
+    """The CPU oracle (as it stands) on each small named call: median wall time
+    of `repeats` runs on one thread, and with the tokens split over `threads`
+    threads (the single-token calls cannot use more than one)."""
+    import statistics
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    orc = oracle.get()
+    out = {}
+    with ThreadPoolExecutor(threads) as ex:
+        for name in ("cfg1", "cfg2", "cfg3", "cfg4", "cfg4b"):
+            case = W.config_case(name)
+            run = lambda c: orc.fwd(c.prefix, c.add, c.add2, c.snapshots, c.query, c.gamma, c.eps)
+
+            def median(fn):
+                ts = []
+                for _ in range(repeats):
+                    t0 = time.perf_counter()
+                    fn()
+                    ts.append(time.perf_counter() - t0)
+                return statistics.median(ts)
+
+            one = median(lambda: run(case))
+            subs = [case.rows(idx) for idx in np.array_split(np.arange(case.M), min(threads, case.M))]
+            many = median(lambda: list(ex.map(run, subs)))
+            out[name] = {"M": case.M, "N": case.N, "ms_1_thread": round(one * 1e3, 3),
+                         "ms_threads": round(many * 1e3, 3), "threads": len(subs)}
+    return out
+
+
 def read_traffic(src_hash):
     """HBM bytes per fused launch from the committed PMC summary, if it was
     taken on the current kernel source; else None."""
@@ -335,8 +377,59 @@ def read_traffic(src_hash):
         return None
 
 
-def latency_suite(launcher, rotate=16, calls=96):
-    """µs per call of the small named workloads, over `rotate` distinct buffer sets."""
+def pool_sets(launcher, case, nsets, tail=False):
+    """`nsets` distinct buffer sets of one call shape, carved out of one device
+    pool (inputs copied from the case, outputs uninitialised).  Returns the
+    pool (keep it alive) and a dict of per-set ctypes argument tuples:
+    "fused" for the fused call; with `tail` also "add" (the standalone add of
+    the two addends into a tail row of the set, run here once) and
+    "presummed" (the fused call given that tail and no second addend)."""
+    import torch
+
+    M, H, N = case.M, case.H, case.N
+    has2 = case.add2 is not None
+    rows = [case.prefix, case.add] + ([case.add2] if has2 else []) + list(case.snapshots)
+    nr, row_elems, vec_elems = len(rows), M * H, H
+    per_set = (nr + 2 + int(tail)) * row_elems + 2 * vec_elems  # rows, outputs, [tail], query, gamma
+    pool = torch.empty((nsets, per_set), dtype=torch.bfloat16, device="cuda")
+    # layout per set: rows [0, nr), out_prefix nr, out_norm nr+1, [tail nr+2], query, gamma
+    q_off = (nr + 2 + int(tail)) * row_elems
+    places = [(r, i * row_elems, row_elems) for i, r in enumerate(rows)]
+    places += [(case.query, q_off, vec_elems), (case.gamma, q_off + vec_elems, vec_elems)]
+    for src, off, n in places:
+        pool[:, off:off + n].copy_(dev(src).reshape(1, n).expand(nsets, n))
+    base, esz = pool.data_ptr(), pool.element_size()
+    vp = ctypes.c_void_p
+    out = {"fused": [], "presummed": [], "add": []}
+    stream = torch.cuda.current_stream().cuda_stream
+    first_snap = 3 if has2 else 2
+    for k in range(nsets):
+        a = base + k * per_set * esz
+        ptr = lambda i: a + i * row_elems * esz
+        snaps = (vp * max(N, 1))(*[ptr(first_snap + j) for j in range(N)])
+        launcher._keep.append(snaps)
+        q = a + q_off * esz
+        g = q + vec_elems * esz
+        out["fused"].append((ptr(0), ptr(1), ptr(2) if has2 else None, snaps if N else None, N, q, g,
+                             ctypes.c_float(case.eps), M, H, ptr(nr), ptr(nr + 1)))
+        if tail:
+            out["add"].append((ptr(1), ptr(2), ptr(nr + 2), row_elems))
+            rc = launcher.add(*out["add"][-1], stream)
+            if rc != 0:
+                raise RuntimeError("attnres_bf16_add -> %d" % rc)
+            out["presummed"].append((ptr(0), ptr(nr + 2), None, snaps if N else None, N, q, g,
+                                     ctypes.c_float(case.eps), M, H, ptr(nr), ptr(nr + 1)))
+    torch.cuda.synchronize()
+    return pool, out
+
+
+def latency_suite(launcher, calls=96, warm_sets=16, cold_bytes=1.1e9):
+    """µs per call of the small named workloads.  Cold: graph replay of one
+    launch per distinct buffer set, with at least `cold_bytes` of sets, so
+    every call's inputs come from HBM (the 256 MB Infinity Cache has been
+    cycled since they were last touched); eager back-to-back launches over the
+    sets touched longest ago.  Warm: graph replay of `calls` launches over
+    `warm_sets` sets (a few MB, resident in the Infinity Cache)."""
     import torch
 
     from attention_residual_rmsnorm_amd import workloads as W
@@ -344,31 +437,75 @@ def latency_suite(launcher, rotate=16, calls=96):
     out = {}
     for name in ("cfg1", "cfg2", "cfg3", "cfg4", "cfg4b"):
         case = W.config_case(name)
-        sets = []
-        for r in range(rotate):
-            t = lambda x: None if x is None else dev(x)
-            prefix, add, add2 = t(case.prefix), t(case.add), t(case.add2)
-            snaps = [t(s) for s in case.snapshots]
-            q, g = t(case.query), t(case.gamma)
-            op, on = torch.empty_like(prefix), torch.empty_like(prefix)
-            sets.append(launcher.fused_args(prefix, add, add2, snaps, q, g, case.eps, op, on))
-            sets[-1] = (sets[-1], (prefix, add, add2, snaps, q, g, op, on))
-        args = [s[0] for s in sets]
-
-        def many(stream, args=args):
-            for k in range(calls):
-                launcher.run_fused(args[k % len(args)], stream)
-
-        per_replay, _ = graph_time(many, steps=20, warmup=3)
-        grp = event_group_times([[lambda h, a=args[k % len(args)]: launcher.run_fused(a, h) for k in range(calls)]
-                                 for _ in range(3)], sleep_cycles=50_000_000)
-        eager = min(grp) / calls
         nbytes = call_bytes(case.M, case.H, case.N, case.add2 is not None)
-        out[name] = {"M": case.M, "N": case.N, "graph_us_per_call": round(per_replay / calls * 1e6, 3),
-                     "eager_us_per_call": round(eager * 1e6, 3),
-                     "GBps_graph": round(nbytes / (per_replay / calls) / 1e9, 1),
-                     "variant": launcher.ar.attnres_plan(case.M, case.N, case.H)[0]}
+        nsets = max(calls * 3, int(cold_bytes // nbytes) + 1)
+        pool, sets = pool_sets(launcher, case, nsets)
+        args = sets["fused"]
+
+        def cold(stream):
+            for a in args:
+                launcher.run_fused(a, stream)
+
+        per_cold, _ = graph_time(cold, steps=3, warmup=1)
+        grp = event_group_times([[lambda h, a=args[g * calls + k]: launcher.run_fused(a, h) for k in range(calls)]
+                                 for g in range(3)], sleep_cycles=50_000_000)
+        per_warm, _ = graph_time(lambda s: [launcher.run_fused(args[k % warm_sets], s) for k in range(calls)],
+                                 steps=20, warmup=3)
+        out[name] = {"M": case.M, "N": case.N, "graph_us_per_call": round(per_cold / nsets * 1e6, 3),
+                     "eager_us_per_call": round(min(grp) / calls * 1e6, 3),
+                     "GBps_graph": round(nbytes / (per_cold / nsets) / 1e9, 1),
+                     "warm_graph_us_per_call": round(per_warm / calls * 1e6, 3),
+                     "cold_sets": nsets, "variant": launcher.ar.attnres_plan(case.M, case.N, case.H)[0]}
         log("latency %s: %s" % (name, out[name]))
+        del pool, sets, args
+        torch.cuda.empty_cache()
+    return out
+
+
+def fold_suite(launcher, cold_bytes=1.1e9):
+    """The pages' own comparison of the fold, per small named workload and per
+    kernel variant (W: one workgroup per token; S: split hidden): µs per call
+    of the fused call with both addends, of the fused call given the pre-summed
+    addend (add2 = NULL), and of the standalone bf16 add that the pre-summed
+    route needs first.  Graph replay of one launch per distinct buffer set,
+    with at least `cold_bytes` of sets (inputs cold in HBM)."""
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    ar = launcher.ar
+    out = {}
+    for name in ("cfg2", "cfg3", "cfg4", "cfg4b"):
+        case = W.config_case(name)
+        nbytes = call_bytes(case.M, case.H, case.N, True)
+        nsets = int(cold_bytes // nbytes) + 1
+        pool, sets = pool_sets(launcher, case, nsets, tail=True)
+
+        def timed(kind, fn):
+            sec, _ = graph_time(lambda s: [fn(a, s) for a in sets[kind]], 3, 1)
+            return sec / nsets * 1e6
+
+        def add(a, s):
+            rc = launcher.add(*a, s)
+            if rc != 0:
+                raise RuntimeError("attnres_bf16_add -> %d" % rc)
+
+        t_add = timed("add", add)
+        row = {"M": case.M, "N": case.N, "standalone_add_us": round(t_add, 3)}
+        for vname, var in (("W", (1, 0)), ("S", (2, 0))):
+            ar.attnres_set_variant(*var)
+            try:
+                f_us = timed("fused", launcher.run_fused)
+                p_us = timed("presummed", launcher.run_fused)
+            finally:
+                ar.attnres_set_variant(0, 0)
+            row[vname] = {"fused_us": round(f_us, 3), "presummed_us": round(p_us, 3),
+                          "fold_cost_us": round(f_us - p_us, 3), "unfused_us": round(p_us + t_add, 3)}
+        row["auto_variant"] = "W" if ar.attnres_plan(case.M, case.N, case.H)[0] == 1 else "S"
+        out[name] = row
+        log("fold %s: %s" % (name, row))
+        del pool, sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -440,11 +577,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--micro-batches", type=int, default=16)
-    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy"], default="full",
+    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy", "latency"], default="full",
                     help="full: everything; chain: the timed chain only (for kernel-trace "
                          "profiling); eager: --steps eager steps of the chain, no graph and no "
                          "timing (for counter collection); copy: a plain 1 GiB device copy, the "
-                         "calibration kernel for the HBM byte counters")
+                         "calibration kernel for the HBM byte counters; latency: the parity gate, "
+                         "then only the small named calls and the per-config fold comparison "
+                         "(for kernel-trace profiling of the latency workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     args = ap.parse_args()
@@ -481,6 +620,12 @@ def main():
     import oracle
 
     parity_gate(chain, launcher, oracle.get())
+
+    if args.mode == "latency":
+        res = {"mode": "latency", "latency_us": latency_suite(launcher), "fold_per_config": fold_suite(launcher)}
+        assert launcher.ar.attnres_debug_timeouts() == 0
+        print(json.dumps(res))
+        return
 
     dc = DeviceChains(chain, args.micro_batches, launcher)
     log("device buffers: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
@@ -552,12 +697,15 @@ def main():
                           "saving_us_per_call": round((sec_u - sec) / launches * 1e6, 3)}
         log("fold: %s" % result["fold"])
         result["latency_us"] = latency_suite(launcher)
+        result["fold_per_config"] = fold_suite(launcher)
         result["tap"] = tap_suite(launcher)
         result["prefill"] = prefill_suite(launcher)
         if not args.no_cpu_baseline:
             threads = args.cpu_threads or max(1, min(16, os.cpu_count() or 1))
             result["cpu_baseline"] = cpu_baseline(chain, threads)
             log("cpu baseline: %s" % result["cpu_baseline"])
+            result["cpu_latency"] = cpu_latency(threads)
+            log("cpu latency: %s" % result["cpu_latency"])
     assert launcher.ar.attnres_debug_timeouts() == 0
     print(json.dumps(result))
 
