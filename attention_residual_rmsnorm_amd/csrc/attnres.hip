@@ -15,11 +15,12 @@
 // MFMA):
 //   W  one workgroup per token: the sources (VPT 16-byte vectors per thread,
 //      in registers) are loaded in a software pipeline, source-major across
-//      the waves, and mixed two at a time as they arrive, under a running
-//      softmax maximum and sum; each group's partials are summed on DPP
-//      within rows and by one wave across rows.  No inter-workgroup
-//      communication.  Used when there are many tokens, and for more than
-//      12 sources (in batches of 12).
+//      the waves, and mixed two at a time as they arrive (up to four
+//      sources as one group), under a running softmax maximum and sum; each
+//      group's partials are summed on DPP within rows and by one wave across
+//      rows.  No inter-workgroup communication.  Used when there are many
+//      tokens, and for more than 12 sources (in batches of 12).
+// Outputs are written with the non-temporal hint in both kernels.
 //   S  split hidden: C workgroups per token, each owning a contiguous chunk of
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
@@ -299,7 +300,8 @@ __device__ __forceinline__ uint4 normalise(const float (&x)[8], float rstd, cons
 // loads).  blockDim.x is a multiple of 64, at most MAXB.
 //
 // The token's sources are p' (from prefix, add, add2) and snapshots 0..N-1,
-// consumed in that order in groups of up to G (the last source alone): A2 for
+// consumed in that order in groups of up to G (the last source alone; up to
+// ONE_GROUP sources form a single group): A2 for
 // the group, its token-wide sums, its logits, and its share of A4 under a
 // running maximum and running sum of the softmax (what was gathered so far is
 // rescaled when the maximum grows).  Loads are software-pipelined LA groups

@@ -64,11 +64,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_only(text: str) -> str:
+    """C++ source with comments removed and runs of whitespace collapsed to one
+    space (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the kernel sources' code (comments
+    and layout do not count): identifies the kernels a stored profile was
+    taken on."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p, encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
