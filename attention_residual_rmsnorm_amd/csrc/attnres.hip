@@ -179,46 +179,6 @@ __device__ __forceinline__ void source_partials(const uint4 (&k)[S][VPT], const 
     }
 }
 
-// Workgroup-wide sums of NV per-thread values; afterwards tot[0..NV-1] (LDS)
-// holds the totals, which every thread reads with identical bits.  Each
-// 16-lane row is summed on DPP; lane 0 of the row stores its NV row sums as a
-// row of `rows` (NVP floats, zero padded); thread v < NV then adds the rows in
-// row order.  The order is fixed by blockDim.x alone.  MAXROWS = MAXB / 16.
-template <int NV, int NVP, int MAXROWS>
-__device__ __forceinline__ void block_sums(float (&part)[NV], float* rows, float* tot, int tid, int nthreads)
-{
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        part[i] = row_sum(part[i]);
-    if ((tid & 15) == 0) {
-        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * NVP);
-#pragma unroll
-        for (int i = 0; i < NVP / 4; ++i)
-            r[i] = make_float4(4 * i + 0 < NV ? part[(4 * i + 0) % NV] : 0.f,
-                               4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
-                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
-                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
-    }
-    __syncthreads();
-    if (tid < NV) {
-        // rows in order, loaded 8 at a time so the loads overlap
-        const int nrows = nthreads >> 4;
-        float acc = rows[tid];
-        for (int r0 = 1; r0 < nrows; r0 += 8) {
-            float v[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                v[r] = r0 + r < nrows ? rows[(r0 + r) * NVP + tid] : 0.f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r0 + r < nrows)
-                    acc += v[r];
-        }
-        tot[tid] = acc;
-    }
-    __syncthreads();
-}
-
 // 32-bit word w (0..3) of a 16-byte vector: elements 2w (low half) and 2w+1.
 __device__ __forceinline__ uint32_t word(const uint4& v, int w)
 {
@@ -791,11 +751,14 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     constexpr int NV = 2 * S;
     constexpr int NVP = (NV + 3) / 4 * 4;
     constexpr int MAXROWS = MAXB / 16;
-    static_assert(S <= 32 && 2 * S <= REC_STRIDE && MAXC <= 64, "one lane per source and per chunk");
+    static_assert(S <= 32 && NV <= 64 && NV <= REC_STRIDE && MAXC <= 64, "one lane per value and per chunk");
+    // 1-2 waves per workgroup: every wave gathers the records itself (no
+    // barrier after either exchange); 4-8 waves: wave 0 gathers and shares
+    // through LDS (less polling traffic when many workgroups wait at once)
+    constexpr bool PERWAVE = MAXB <= 128;
     __shared__ __align__(16) float rows[MAXROWS * NVP];
-    __shared__ __align__(16) float tot[NVP];
-    __shared__ float alpha_sh[32];
     __shared__ float red2[MAXB / 64];
+    __shared__ float alpha_sh[PERWAVE ? 1 : 32];
     __shared__ float ssum_sh;
 
     const int tid = threadIdx.x;
@@ -829,110 +792,119 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     if (ok[0])
         store_stream(&p.out_prefix[row + v], k[NS][0]);
 
-    // A2: this chunk's partials, then the token's totals through the records
+    // A2: this chunk's partials (row sums on DPP, rows through LDS); thread
+    // v < NV adds the rows of value v and publishes it
     float part[NV];
     source_partials<S, 1>(k, q, ok, part);
     fence_sources<S, 1>(k);
-    block_sums<NV, NVP, MAXROWS>(part, rows, tot, tid, nthreads);
-    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
-    if (tid < NV)
-        publish(&rec1[chunk * REC_STRIDE + tid], tag1, tot[tid]);
-
-    // A3 in wave 0.  SL lanes hold one set of sources (16 for up to 16
-    // sources, 32 for up to 32) and the wave holds NR = 64/SL sets: lane l
-    // takes source s = l % SL and chunks l/SL, l/SL + NR, ...; all of its
-    // record loads are issued together, those not yet tagged are read again
-    // (bounded wait).  The NR sets' sums are then added in set order, so
-    // every lane of source s (and every workgroup of the token) holds the
-    // same totals; the logits, their maximum and the exponentials' sum are
-    // taken across the SL lanes of a set (one or two DPP rows), and lanes
-    // 0..S-1 write alpha.
-    if (wave == 0) {
-        constexpr int SL = S <= 16 ? 16 : 32, NR = 64 / SL;
-        constexpr int KC = (MAXC + NR - 1) / NR;
-        const int s = lane & (SL - 1), c0 = lane / SL;
-        const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
-        unsigned long long w[2 * KC];
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            const int cc = c0 + NR * kk;
-            const bool use = s < S && cc < C;
-            w[2 * kk] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s]) : ready_zero;
-            w[2 * kk + 1] = use ? peek(&rec1[cc * REC_STRIDE + 2 * s + 1]) : ready_zero;
-        }
-        for (unsigned polls = 0;; ++polls) {
-            bool ready = true;
+    for (int i = 0; i < NV; ++i)
+        part[i] = row_sum(part[i]);
+    if ((tid & 15) == 0) {
+        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * NVP);
 #pragma unroll
-            for (int kk = 0; kk < 2 * KC; ++kk)
-                ready &= tag_of(w[kk]) == tag1;
-            if (ready)
-                break;
-            if (polls >= p.spin_limit) {
-                atomicAdd(p.timeouts, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int kk = 0; kk < KC; ++kk) {
-                const int cc = c0 + NR * kk;
-                if (s < S && cc < C) {
-                    if (tag_of(w[2 * kk]) != tag1)
-                        w[2 * kk] = peek(&rec1[cc * REC_STRIDE + 2 * s]);
-                    if (tag_of(w[2 * kk + 1]) != tag1)
-                        w[2 * kk + 1] = peek(&rec1[cc * REC_STRIDE + 2 * s + 1]);
-                }
-            }
-        }
-        float ss = 0.f, qd = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            ss += __uint_as_float((unsigned)w[2 * kk]);
-            qd += __uint_as_float((unsigned)w[2 * kk + 1]);
-        }
-        {
-            float st = __shfl(ss, s), qt = __shfl(qd, s);
-#pragma unroll
-            for (int r = 1; r < NR; ++r) {
-                st += __shfl(ss, s + SL * r);
-                qt += __shfl(qd, s + SL * r);
-            }
-            ss = st;
-            qd = qt;
-        }
-        const float z = s < S ? rsqrtf(ss * p.inv_h + p.eps) * qd : -INFINITY;
-        float zmax = row_max(z);
-        if (SL == 32) // the set's two rows (max is exact: same bits in both)
-            zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
-        const float e = s < S ? __expf(z - zmax) : 0.f;
-        float den = row_sum(e);
-        if (SL == 32) // a + b == b + a: same bits in both rows
-            den = den + __shfl_xor(den, 16);
-        if (lane < S)
-            alpha_sh[lane] = e * (1.0f / den);
+        for (int i = 0; i < NVP / 4; ++i)
+            r[i] = make_float4(4 * i + 0 < NV ? part[(4 * i + 0) % NV] : 0.f,
+                               4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
+                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
+                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
     }
     __syncthreads();
+    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
+    if (tid < NV) { // rows in order, loaded 8 at a time so the loads overlap
+        const int nrows = nthreads >> 4;
+        float acc = rows[tid];
+        for (int r0 = 1; r0 < nrows; r0 += 8) {
+            float vr[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                vr[r] = r0 + r < nrows ? rows[(r0 + r) * NVP + tid] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r0 + r < nrows)
+                    acc += vr[r];
+        }
+        publish(&rec1[chunk * REC_STRIDE + tid], tag1, acc);
+    }
+
+    // A3 in every wave (PERWAVE) or in wave 0: lane v < NV adds value v (2s:
+    // sum k_s^2, 2s+1: q.k_s) over the chunks in chunk order, 8 chunks' records
+    // in flight at a time (those not yet tagged read again; bounded wait), so
+    // it holds the same bits in every wave of every workgroup of the token.  A
+    // DPP swap of neighbouring lanes puts q.k_s beside sum k_s^2 in lane 2s,
+    // whose logit, the wave's maximum and the exponentials' sum (DPP and
+    // scalar reads, fixed order) give alpha_s in lane 2s.
+    float alpha[S];
+    if (PERWAVE || wave == 0) {
+        const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
+        float tv = 0.f;
+        for (int c0 = 0; c0 < C; c0 += 8) {
+            unsigned long long r0[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                r0[j] = c0 + j < C && lane < NV ? peek(&rec1[(c0 + j) * REC_STRIDE + lane]) : ready_zero;
+            for (unsigned polls = 0;; ++polls) {
+                bool ready = true;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    ready &= tag_of(r0[j]) == tag1;
+                if (ready)
+                    break;
+                if (polls >= p.spin_limit) {
+                    atomicAdd(p.timeouts, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (c0 + j < C && lane < NV && tag_of(r0[j]) != tag1)
+                        r0[j] = peek(&rec1[(c0 + j) * REC_STRIDE + lane]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                tv += __uint_as_float((unsigned)r0[j]);
+        }
+        const float qd = dpp<0xb1>(tv); // quad_perm [1,0,3,2]: lane 2s gets lane 2s+1's value
+        const bool src = (lane & 1) == 0 && lane < NV;
+        const float z = src ? rsqrtf(tv * p.inv_h + p.eps) * qd : -INFINITY;
+        const float zmax = wave_max(z);
+        const float e = src ? __expf(z - zmax) : 0.f;
+        const float den = wave_sum(e);
+        const float al = e * (1.0f / den);
+        if constexpr (PERWAVE) {
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * i));
+        } else if (src) {
+            alpha_sh[lane >> 1] = al;
+        }
+    }
+    if constexpr (!PERWAVE) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            alpha[i] = alpha_sh[i];
+    }
 
     // A4
-    float alpha[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-        alpha[i] = alpha_sh[i];
     float x[1][8];
     const float sx = wave_sum(combine<S, 1>(k, alpha, ok, x));
     if (lane == 0)
         red2[wave] = sx;
     __syncthreads();
 
-    // A5: the token's sum of x^2 through the second records, gathered by wave 0
-    // (lane c reads chunk c's record) and added on DPP
+    // A5: the chunk's sum of x^2 (its waves in order) published by thread 0;
+    // every wave (PERWAVE) or wave 0 reads the C records (lane c: chunk c) and
+    // adds them on DPP
     unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
-    if (wave == 0) {
-        if (lane == 0) {
-            float s2 = red2[0];
-            for (int w = 1; w < nw; ++w)
-                s2 += red2[w];
-            publish(&rec2[chunk], tag2, s2);
-        }
+    if (tid == 0) {
+        float s2 = red2[0];
+        for (int w = 1; w < nw; ++w)
+            s2 += red2[w];
+        publish(&rec2[chunk], tag2, s2);
+    }
+    float ssum = 0.f;
+    if (PERWAVE || wave == 0) {
         unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
         for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
             if (polls >= p.spin_limit) {
@@ -942,15 +914,17 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             __builtin_amdgcn_s_sleep(1);
             w2 = peek(&rec2[lane]);
         }
-        const float tot2 = wave_sum(__uint_as_float((unsigned)w2));
-        if (lane == 0) {
-            ssum_sh = tot2;
-            if (chunk == 0) // every chunk has published its second record: all have read the epoch
-                __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        ssum = wave_sum(__uint_as_float((unsigned)w2));
+        if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
+            __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!PERWAVE && lane == 0)
+            ssum_sh = ssum;
     }
-    __syncthreads();
-    const float rstd = rsqrtf(ssum_sh * p.inv_h + p.eps);
+    if constexpr (!PERWAVE) {
+        __syncthreads();
+        ssum = ssum_sh;
+    }
+    const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
     if (ok[0]) {
         store_stream(&p.out_norm[row + v], normalise(x[0], rstd, g[0]));
         if (p.out_mix) // the pre-norm mixture (the weights sum to one here)

@@ -117,6 +117,18 @@ __device__ __forceinline__ float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Maximum over the 64 lanes of a wave, in every lane (the four row maxima read
+// as scalars).  All 64 lanes must be active.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = row_max(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // ---- cross-workgroup exchange --------------------------------------------
 //
 // Workgroups that share a token exchange binary32 partial sums through 64-bit
