@@ -166,16 +166,20 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
                                                                                     : ATTNRES_EINVAL;
     }
     // Automatic, from per-call times of every variant on MI355X at H = 7168
-    // (graph replay, inputs cold in HBM, M = 1..512, N = 1, 4, 8, 12):
+    // (graph replay, inputs cold in HBM, M = 1..512, N = 1..12):
     //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
-    //  * M <= 16, or M <= 32 with N >= 5: the call is latency-bound; 2-wave
-    //    chunks spread each token over the most CUs;
+    //  * N >= 3, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
+    //    each token over the most CUs (one token: 2-wave chunks, whose
+    //    exchanges have half as many partners);
+    //  * N >= 5: 2-wave chunks up to 24 tokens, and up to 32 with N < 8;
     //  * M <= 64 with N >= 8: 4-wave chunks, or 2-wave chunks above 12
     //    sources (only that family holds them);
     //  * otherwise one workgroup per token.
     if (n > 2) {
-        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_SMALL_TOKENS_WIDE) ||
-                           (many && M <= SPLIT_MID_TOKENS);
+        if (!many && M >= 2 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
+            return ATTNRES_OK;
+        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_2WAVE_TOKENS) ||
+                           (n >= 5 && n < 8 && M <= SPLIT_SMALL_TOKENS_WIDE) || (many && M <= SPLIT_MID_TOKENS);
         if (small && split_ok && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
         if (n >= 8 && !many && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))

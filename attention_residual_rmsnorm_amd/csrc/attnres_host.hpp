@@ -14,10 +14,12 @@ constexpr int MAX_SPLIT_SNAP = 31;       // split hidden, 1-2 waves per workgrou
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-// automatic dispatch (see make_plan): 2-wave split up to SPLIT_SMALL_TOKENS
-// tokens (N >= 3), or SPLIT_SMALL_TOKENS_WIDE (N >= 5); 4-wave split up to
-// SPLIT_MID_TOKENS (N >= 8)
+// automatic dispatch (see make_plan), N >= 3: 1-wave split for 2 to
+// SPLIT_SMALL_TOKENS tokens (2-wave for one token); 2-wave split up to
+// SPLIT_2WAVE_TOKENS (N >= 5) or SPLIT_SMALL_TOKENS_WIDE (5 <= N < 8); 4-wave
+// split up to SPLIT_MID_TOKENS (N >= 8)
 constexpr int SPLIT_SMALL_TOKENS = 16;
+constexpr int SPLIT_2WAVE_TOKENS = 24;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_MID_TOKENS = 64;
 
