@@ -87,14 +87,28 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p)
 }
 
 // Output rows are written once and not read again by this call: streamed with
-// the non-temporal hint (fewer dirty lines left in L2 when the kernel ends;
-// about 0.1 us per call at M = 256).
+// the non-temporal hint, so the call does not end with them dirty in L2 (at
+// M = 256, N = 1: 6.70 -> 5.98 us per call).
 __device__ __forceinline__ void store_stream(uint4* p, const uint4& v)
 {
     __builtin_nontemporal_store(v.x, &p->x);
     __builtin_nontemporal_store(v.y, &p->y);
     __builtin_nontemporal_store(v.z, &p->z);
     __builtin_nontemporal_store(v.w, &p->w);
+}
+
+// Kernel W's out_prefix, written right after the first group arrives: in a
+// call with many sources (S >= 9) a plain store does better, because its
+// lines leave L2 in the background while the remaining sources stream in
+// instead of competing with them (M = 256, N = 10: 11.84 -> 11.54 us; with
+// N <= 7 the streamed store wins, N = 5: 8.46 against 8.97 us).
+template <int S>
+__device__ __forceinline__ void store_prefix(uint4* p, const uint4& v)
+{
+    if constexpr (S >= 9)
+        *p = v;
+    else
+        store_stream(p, v);
 }
 
 // Loads of vector v of one token's rows (16 bytes = 8 bf16 each).  The loads
@@ -544,7 +558,7 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
 #pragma unroll
             for (int j = 0; j < VPT; ++j)
                 if (ok[j])
-                    store_stream(&p.out_prefix[row + tid + j * nthreads], k[0][j]);
+                    store_prefix<S>(&p.out_prefix[row + tid + j * nthreads], k[0][j]);
         }
         constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
         mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
