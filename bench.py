@@ -37,6 +37,10 @@ Also reported on the same JSON line:
   fold_per_config  the same comparison per small named call and per kernel
                 variant: fused with add2, fused with the pre-summed addend,
                 standalone add
+  tap           cost of the optional pre-norm mixture output (the capture tap)
+                at M = 256 and at one token, N = 12
+  prefill       prefill-sized calls (M = 1,024 and 4,096, N = 12): µs per call
+                and the fraction of 8 TB/s
 
 Every timing follows a parity check against the CPU oracle.
 """
