@@ -157,6 +157,20 @@ def test_shapes(ar, orc, variant, M, H, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
+@pytest.mark.parametrize("N", [3, 4, 7, 8, 12])
+@pytest.mark.parametrize("M", [2, 16, 17, 24, 25, 32, 33, 64, 65])
+def test_dispatch_boundaries(ar, orc, M, N):
+    """The automatic dispatch on both sides of each of its token-count bounds
+    (1-wave chunks up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64,
+    then a workgroup per token) and source-count bounds (one group of up to four
+    sources in kernel W; the store policy changes at nine sources)."""
+    case = case_for(("bound", M, N), lambda: W.make_case(cfg=62, M=M, N=N, add2=(M % 2 == 0)))
+    say("boundary", M, N, ar.attnres_plan(M, N, case.H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
+
+
 def test_beyond_split_slots_and_grid(ar, orc):
     """M above the split-hidden token slots (workgroup per token; 600 tokens put
     two workgroups on some CUs), the prefill-sized call bench.py times (1,024
