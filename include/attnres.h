@@ -65,10 +65,12 @@ extern "C" {
                                      out of memory for the scratch) */
 
 #define ATTNRES_MAX_SNAPSHOTS 64 /* up to 12 (the page's fused window, section "Model")
-                                    the sources are taken in one pass; 13..64 take the
-                                    batched path (the same running softmax carried over
-                                    batches of 12 snapshots), so the page's N > 12
-                                    fallback is not needed below 65 */
+                                    the sources are taken in one pass; 13..64 are fused
+                                    too (the workgroup-per-token kernel carries one
+                                    running softmax over batches of 12 snapshots; the
+                                    split-hidden kernel, used for a few tokens, holds
+                                    up to 31 at once), so the page's N > 12 fallback is
+                                    not needed below 65 */
 #define ATTNRES_MAX_HIDDEN 16384
 
 /*
