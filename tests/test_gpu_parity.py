@@ -213,7 +213,11 @@ def test_in_place_prefix(ar, orc, variant):
 
 # --- determinism, graphs, canaries ---------------------------------------------
 
-@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+SYNC_VARIANTS = [(1, 0), (2, 1), (2, 2), (2, 7)]  # W; split with 1, 2 (gather in every wave), 7 waves (wave 0)
+SYNC_VID = ["W", "S1w", "S2w", "S7w"]
+
+
+@pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
 def test_deterministic(ar, variant):
     case = case_for("cfg4", lambda: W.config_case("cfg4"))
     first = P.run_gpu(case)
@@ -222,7 +226,7 @@ def test_deterministic(ar, variant):
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
-@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+@pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
 def test_graph_replay(ar, variant):
     """Capture one call into a HIP graph; replay it with fresh inputs copied
     in between (eager work and synchronisation between replays); every replay
