@@ -541,6 +541,37 @@ def fold_suite(launcher, cold_bytes=1.1e9):
     return out
 
 
+def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), Ns=(0, 1, 2, 4, 8, 12),
+               cold_bytes=1.1e9):
+    """The metric over a grid of token and source counts (H = 7168, add2,
+    automatic dispatch): µs per call with inputs cold in HBM (graph replay of
+    one launch per distinct buffer set over >= 1.1 GB of sets) and the
+    achieved GB/s of the algorithmic bytes."""
+    import torch
+
+    from attention_residual_rmsnorm_amd import workloads as W
+
+    out = []
+    for N in Ns:
+        for M in Ms:
+            case = W.make_case(cfg=93, M=M, N=N, add2=True)
+            nbytes = call_bytes(M, case.H, N, True)
+            nsets = max(64, int(cold_bytes // nbytes) + 1)
+            pool, sets = pool_sets(launcher, case, nsets)
+            args = sets["fused"]
+            sec, _ = graph_time(lambda s: [launcher.run_fused(a, s) for a in args], 3, 1)
+            us = sec / nsets * 1e6
+            plan = launcher.ar.attnres_plan(M, N, case.H)
+            row = {"M": M, "N": N, "us_per_call": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                   "frac": round(nbytes / (us * 1e-6) / 8e12, 4),
+                   "kernel": "W" if plan[0] == 1 else "S%dw" % (plan[2] // 64)}
+            log("grid %s" % row)
+            out.append(row)
+            del pool, sets, args
+            torch.cuda.empty_cache()
+    return out
+
+
 def tap_suite(launcher, calls=64):
     """Cost of the pre-norm mixture output (the capture tap): µs per call of the
     fused call with and without out_mix, graph replay over >= 1 GB of rotating
@@ -609,13 +640,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--micro-batches", type=int, default=16)
-    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy", "latency"], default="full",
+    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy", "latency", "grid"], default="full",
                     help="full: everything; chain: the timed chain only (for kernel-trace "
                          "profiling); eager: --steps eager steps of the chain, no graph and no "
                          "timing (for counter collection); copy: a plain 1 GiB device copy, the "
                          "calibration kernel for the HBM byte counters; latency: the parity gate, "
                          "then only the small named calls and the per-config fold comparison "
-                         "(for kernel-trace profiling of the latency workloads)")
+                         "(for kernel-trace profiling of the latency workloads); grid: the parity "
+                         "gate, then µs per call and GB/s over a grid of token and source counts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     args = ap.parse_args()
@@ -652,6 +684,12 @@ def main():
     import oracle
 
     parity_gate(chain, launcher, oracle.get())
+
+    if args.mode == "grid":
+        res = {"mode": "grid", "grid": grid_suite(launcher)}
+        assert launcher.ar.attnres_debug_timeouts() == 0
+        print(json.dumps(res))
+        return
 
     if args.mode == "latency":
         res = {"mode": "latency", "latency_us": latency_suite(launcher), "fold_per_config": fold_suite(launcher)}
