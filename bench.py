@@ -744,6 +744,7 @@ def main():
                               "frac": round(b12 / t12 / 1e9 / HBM_PEAK_GBS, 4)},
                 "n1_layer": {"kernel_us": round(t1 * 1e6, 3), "GBps": round(b1 / t1 / 1e9, 1),
                              "frac": round(b1 / t1 / 1e9 / HBM_PEAK_GBS, 4)},
+                "layer_us_by_snapshots": {str(n): round(sum(v) / len(v) * 1e6, 3) for n, v in sorted(per_layer.items())},
                 "kernel_source_sha256_16": src_hash}
     log("roofline: %s" % roofline)
 
