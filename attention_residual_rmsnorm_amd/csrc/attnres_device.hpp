@@ -138,6 +138,10 @@ __device__ __forceinline__ float wave_max(float v)
 // whole-cache writeback/invalidate that device-scope release/acquire costs on
 // gfx950) is needed.  Tags come from a per-token epoch word that advances once
 // per call (see fwd_split), so records left by earlier calls never match.
+// (The 32-bit tags repeat after 2^31 calls on one token slot.  Every call
+// rewrites the records of every chunk it uses, so an old record could match
+// only if a chunk index went unused for exactly that many calls and a later
+// call with more chunks then read it; this is not guarded against.)
 
 __device__ __forceinline__ void publish(unsigned long long* rec, unsigned tag, float v)
 {
