@@ -353,7 +353,20 @@ def cpu_baseline(chain, threads, min_cpu_seconds=12.0, max_passes=8):
     nbytes = passes * sum(call_bytes(chain.M, chain.H, l.n_sources) for l in chain.layers)
     return {"value": round(nbytes / wall / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "the full 25-layer chain (256 tokens, H=7168, N=1..12, add2) %d times, oracle in "
-                      "binary64, token blocks over %d threads; %.2f s wall" % (passes, threads, wall)}
+                      "binary64, token blocks over %d threads; %.2f s wall; host: %s, %d logical CPUs"
+                      % (passes, threads, wall, cpu_model(), os.cpu_count() or 0)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_latency(threads, repeats=5):
