@@ -92,6 +92,39 @@ def test_named_workload_structure():
     assert sub(t).mean() > 0.009
 
 
+# --- how far inside the bar -------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(W.CONFIGS) + ["m256_n12"])
+def test_error_margin(ar, orc, name):
+    """How far inside the bar: the GPU's out_norm against the oracle's binary64
+    value before its final rounding.  The binary32 arithmetic leaves an error
+    that is absolute rather than relative (the logits' relative error of a few
+    1e-6 moves the mixture by a few 1e-6, whatever the output's size), so two
+    figures: for |value| >= 0.1 the error in bf16 ulps of the value (rounding
+    alone accounts for up to 1/2) must stay within 0.75 ulp, and everywhere the
+    error beyond half an ulp of rounding must stay below 1e-4 (the contract
+    allows 2 ulps against the rounded oracle, or 1e-2)."""
+    if name == "m256_n12":
+        case = case_for(name, lambda: W.make_case(cfg=65, M=256, N=12, add2=True))
+    else:
+        case = case_for(name, lambda: W.config_case(name))
+    gp, gn = P.run_gpu(case)
+    _, _, exact = orc.fwd(case.prefix, case.add, case.add2, case.snapshots, case.query, case.gamma, case.eps,
+                          want_f64=True)
+    got = W.bf16_bits_to_f32(gn).astype(np.float64)
+    nz = exact != 0
+    ulp = np.where(nz, np.exp2(np.floor(np.log2(np.abs(np.where(nz, exact, 1.0)))) - 7), 2.0 ** -133)
+    err_ulp = np.abs(got - exact) / ulp
+    beyond = np.maximum(np.abs(got - exact) - ulp / 2, 0.0)
+    big = np.abs(exact) >= 0.1
+    say("error margin", name, ar.attnres_plan(case.M, case.N, case.H),
+        "|v| >= 0.1: max %.4f ulp, mean %.4f; beyond rounding: max %.2e, at |v| %.3g (%.3f ulp)"
+        % (err_ulp[big].max(), err_ulp[big].mean(), beyond.max(), abs(exact.flat[beyond.argmax()]),
+           err_ulp.flat[beyond.argmax()]))
+    assert err_ulp[big].max() <= 0.75, "%s: %.3f ulp" % (name, err_ulp[big].max())
+    assert beyond.max() <= 1e-4, "%s: %.2e beyond rounding" % (name, beyond.max())
+
+
 # --- two addends == one pre-summed addend, bitwise, N = 0..12 -----------------
 
 @pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
