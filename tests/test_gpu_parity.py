@@ -204,6 +204,39 @@ def test_dispatch_boundaries(ar, orc, M, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
 
 
+def _random_cases(n=40, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        H = int(rng.choice([8, 16, 64, 520, 1000, 4104, 7168, 7176, 8192, 8200, 12000, 16384]))
+        M = int(rng.integers(1, 81))
+        if M * H > 400_000:
+            continue
+        N = int(rng.integers(0, 13)) if rng.random() < 0.8 else int(rng.integers(13, 32))
+        out.append((M, H, N, bool(rng.random() < 0.7), VARIANTS[int(rng.integers(0, len(VARIANTS)))]))
+    return out
+
+
+@pytest.mark.parametrize("M,H,N,add2,var", _random_cases())
+def test_random_shapes(ar, orc, M, H, N, add2, var):
+    """Seeded random token counts, hidden sizes (ragged tails included), source
+    counts up to 31, with and without the second addend, under a random forced
+    kernel variant (skipped where that variant cannot serve the size)."""
+    ar.attnres_set_variant(*var)
+    try:
+        try:
+            ar.attnres_plan(M, N, H)
+        except ar.AttnResError:
+            pytest.skip("variant not available for this size")
+        case = W.make_case(cfg=66, M=M, H=H, N=N, add2=add2)
+        say("random", M, H, N, add2, var, ar.attnres_plan(M, N, H))
+        gp, gn = P.run_gpu(case)
+    finally:
+        ar.attnres_set_variant(0, 0)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d add2=%s variant=%s" % (M, H, N, add2, var))
+
+
 def test_beyond_split_slots_and_grid(ar, orc):
     """M above the split-hidden token slots (workgroup per token; 600 tokens put
     two workgroups on some CUs), the prefill-sized call bench.py times (1,024
