@@ -416,6 +416,47 @@ __device__ __forceinline__ void group_sums(float (&part)[NV], float* rows, float
     __syncthreads();
 }
 
+// Workgroup totals of NV <= 32 per-thread values, for workgroups of at most
+// 16 * MAXROWS threads: each 16-lane row is summed on DPP and lane 0 of row r
+// stores its NV sums at rows[32r..32r+NV); after a barrier thread v < NV adds
+// value v over the present rows in order and stores tot[v].  After a second
+// barrier every thread reads the same bits.  One round for all of a token's
+// sources where the rows are short (few threads per token).  A kernel uses
+// either this or group_sums for all its groups: this one leaves entries that
+// group_sums expects to be zero.
+template <int NV, int MAXROWS>
+__device__ __forceinline__ void group_sums_wide(float (&part)[NV], float* rows, float* tot, int tid, int nthreads)
+{
+    static_assert(NV >= 1 && NV <= 32, "at most 32 values per group");
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        part[i] = row_sum(part[i]);
+    if ((tid & 15) == 0) {
+        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * 32);
+#pragma unroll
+        for (int i = 0; i < (NV + 3) / 4; ++i)
+            r[i] = make_float4(part[4 * i], 4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
+                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
+                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
+    }
+    __syncthreads();
+    if (tid < NV) {
+        // all MAXROWS entries read at once; those of absent rows (stale) are
+        // dropped by a select, never added
+        const int nrows = nthreads >> 4;
+        float t[MAXROWS];
+#pragma unroll
+        for (int r = 0; r < MAXROWS; ++r)
+            t[r] = rows[32 * r + tid];
+        float acc = t[0];
+#pragma unroll
+        for (int r = 1; r < MAXROWS; ++r)
+            acc += r < nrows ? t[r] : 0.f;
+        tot[tid] = acc;
+    }
+    __syncthreads();
+}
+
 // Running softmax state of one token: x = sum_s e^(z_s - m) k_s and
 // den = sum_s e^(z_s - m) over the sources so far, m their largest logit.
 // z, m and den hold the same bits in every lane (uniform branches).
@@ -426,9 +467,9 @@ struct Mix {
 };
 
 // A2-A4 for one group of n consecutive sources ks[0..n).
-template <int n, int VPT, bool FIRST>
+template <int n, int VPT, bool FIRST, int MAXROWS>
 __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q, const bool* ok, Mix<VPT>& mx,
-                                          float* rows, float* tot, const Params& p, int tid)
+                                          float* rows, float* tot, const Params& p, int tid, int nthreads)
 {
     float part[2 * n];
 #pragma unroll
@@ -437,7 +478,10 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
         part[2 * s] = v.x;
         part[2 * s + 1] = v.y;
     }
-    group_sums<2 * n>(part, rows, tot, tid);
+    if constexpr (MAXROWS > 0)
+        group_sums_wide<2 * n, MAXROWS>(part, rows, tot, tid, nthreads);
+    else
+        group_sums<2 * n>(part, rows, tot, tid);
     float z[n];
 #pragma unroll
     for (int s = 0; s < n; ++s)
@@ -512,24 +556,43 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
 }
 
 // Groups over S sources: G at a time over sources [0, S-1), then the last
-// source alone; up to ONE_GROUP sources form a single group (with so few, all
-// loads are in flight at once anyway, and one group needs one set of
+// source alone; up to max(ONE_GROUP, G) sources form a single group (with so
+// few, all loads are in flight at once anyway, and one group needs one set of
 // workgroup sums instead of two or three: 2-4 % faster at N <= 3).
 // group_count is their number, group_start(i) the first source of group i
 // (group_start(group_count) = S).
 constexpr int ONE_GROUP = 4;
 
+// LDS totals per group slot: 2 per source, up to one pass of sources in one
+// group (group_sums_wide, used by the kernels with G > ONE_GROUP).
+constexpr int TOT_SLOT = 32;
+static_assert(2 * (MAX_SNAP + 1) <= TOT_SLOT, "one pass of sources in one group");
+
+// Kernel W's LDS floats per group slot: group_sums' 64 rows of 8 values, or
+// (G > ONE_GROUP) group_sums_wide's MAXB/16 rows of 32.
+template <int G, int MAXB>
+constexpr int row_slot()
+{
+    return G > ONE_GROUP ? 32 * (MAXB / 16) : 64 * 8;
+}
+
+template <int S, int G>
+constexpr bool single_group()
+{
+    return S <= ONE_GROUP || S <= G;
+}
+
 template <int S, int G>
 constexpr int group_count()
 {
-    return S <= ONE_GROUP ? (S > 0 ? 1 : 0) : 1 + (S - 1 + G - 1) / G;
+    return single_group<S, G>() ? (S > 0 ? 1 : 0) : 1 + (S - 1 + G - 1) / G;
 }
 
 template <int S, int G>
 constexpr int group_start(int i)
 {
-    return S <= ONE_GROUP ? (i == 0 ? 0 : S)
-                          : i < (S - 1 + G - 1) / G ? i * G : (i == (S - 1 + G - 1) / G ? S - 1 : S);
+    return single_group<S, G>() ? (i == 0 ? 0 : S)
+                                : i < (S - 1 + G - 1) / G ? i * G : (i == (S - 1 + G - 1) / G ? S - 1 : S);
 }
 
 // Kernel W's pipeline over one batch of S sources, step GI: issue the loads of
@@ -540,12 +603,12 @@ constexpr int group_start(int i)
 // group's rows), and wave 0 writes a group's totals only after its first
 // barrier (every thread has read the previous totals).  FIRSTBATCH: the first
 // group starts the running softmax.
-template <int S, int G, int LA, int GI, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT>
+template <int S, int G, int LA, int GI, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT, int MAXB>
 __device__ __forceinline__ void stream_groups(const Params& p, const uint4* const* snap, int64_t row,
                                               const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
                                               uint4 (&c)[VPT], uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
-                                              Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8], int tid,
-                                              int nthreads)
+                                              Mix<VPT>& mx, float (*rows)[row_slot<G, MAXB>()],
+                                              float (*tot)[TOT_SLOT], int tid, int nthreads)
 {
     constexpr int NG = group_count<S, G>();
     if constexpr (GI < NG) {
@@ -561,38 +624,44 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
                     store_prefix<S>(&p.out_prefix[row + tid + j * nthreads], k[0][j]);
         }
         constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
-        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p, tid);
-        stream_groups<S, G, LA, GI + 1, HASP, FIRSTBATCH, ADD2, VPT>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows,
-                                                                     tot, tid, nthreads);
+        constexpr int wide_rows = G > ONE_GROUP ? MAXB / 16 : 0;
+        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, wide_rows>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p,
+                                                                   tid, nthreads);
+        stream_groups<S, G, LA, GI + 1, HASP, FIRSTBATCH, ADD2, VPT, MAXB>(p, snap, row, vc, a, b, c, k, q, ok, mx,
+                                                                           rows, tot, tid, nthreads);
     }
 }
 
 // One batch of S sources through the pipeline: the first LA groups' loads,
 // then the steps.
-template <int S, int G, int LA, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT>
+template <int S, int G, int LA, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT, int MAXB>
 __device__ __forceinline__ void stream_batch(const Params& p, const uint4* const* snap, int64_t row,
                                              const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
                                              uint4 (&c)[VPT], uint4 (&k)[S][VPT], const uint4* q, const bool* ok,
-                                             Mix<VPT>& mx, float (*rows)[64 * 8], float (*tot)[8], int tid,
-                                             int nthreads)
+                                             Mix<VPT>& mx, float (*rows)[row_slot<G, MAXB>()],
+                                             float (*tot)[TOT_SLOT], int tid, int nthreads)
 {
     constexpr int NG = group_count<S, G>();
     issue_range<0, group_start<S, G>(LA < NG ? LA : NG), HASP, ADD2, VPT, S>(p, snap, row, vc, a, b, c, k);
-    stream_groups<S, G, LA, 0, HASP, FIRSTBATCH, ADD2, VPT>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows, tot,
-                                                            tid, nthreads);
+    stream_groups<S, G, LA, 0, HASP, FIRSTBATCH, ADD2, VPT, MAXB>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows,
+                                                                  tot, tid, nthreads);
 }
 
-// LDS set-up shared by both forms of kernel W: entries of absent waves stay
-// zero (ordered before use by the first barrier).
-template <int MAXW>
-__device__ __forceinline__ void wg_prologue(float (*rows)[64 * 8], float* red2, int tid, int nthreads)
+// LDS set-up shared by both forms of kernel W: group_sums' entries of absent
+// waves stay zero (ordered before use by the first barrier); group_sums_wide
+// (G > ONE_GROUP) reads present rows only.
+template <int MAXW, int G, int MAXB>
+__device__ __forceinline__ void wg_prologue(float* rows, float* red2, int tid, int nthreads)
 {
     const int nw = nthreads >> 6;
     if (tid < MAXW && tid >= nw)
         red2[tid] = 0.f;
-    for (int i = tid; i < 2 * 64 * 8; i += nthreads)
-        if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
-            rows[i >> 9][i & 511] = 0.f;
+    if constexpr (G <= ONE_GROUP) {
+        static_assert(row_slot<G, MAXB>() == 64 * 8, "group_sums' slot");
+        for (int i = tid; i < 2 * 64 * 8; i += nthreads)
+            if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
+                rows[i] = 0.f;
+    }
 }
 
 // A5 (and the optional mixture output) of one token from the running softmax
@@ -642,14 +711,15 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
     constexpr int S = NS + 1;
     constexpr int MAXW = MAXB / 64;
     static_assert(MAXB / 16 <= 64, "rows of one group slot");
-    __shared__ __align__(16) float rows[2][64 * 8];
-    __shared__ __align__(16) float tot[2][8];
+    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 32 rows");
+    __shared__ __align__(16) float rows[2][row_slot<G, MAXB>()];
+    __shared__ __align__(16) float tot[2][TOT_SLOT];
     __shared__ float red2[MAXW];
 
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int nvec = p.nvec;
-    wg_prologue<MAXW>(rows, red2, tid, nthreads);
+    wg_prologue<MAXW, G, MAXB>(&rows[0][0], red2, tid, nthreads);
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
         const int64_t row = t * (int64_t)nvec;
@@ -669,7 +739,7 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
         }
         // A1 (in step 0), A2-A4
         Mix<VPT> mx;
-        stream_batch<S, G, LA, true, true, ADD2, VPT>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot, tid,
+        stream_batch<S, G, LA, true, true, ADD2, VPT, MAXB>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot, tid,
                                                       nthreads);
         // A5
         wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
@@ -693,15 +763,16 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 {
     constexpr int B = MAX_SNAP;
     constexpr int MAXW = MAXB / 64;
-    __shared__ __align__(16) float rows[2][64 * 8];
-    __shared__ __align__(16) float tot[2][8];
+    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 32 rows");
+    __shared__ __align__(16) float rows[2][row_slot<G, MAXB>()];
+    __shared__ __align__(16) float tot[2][TOT_SLOT];
     __shared__ float red2[MAXW];
     const Params& p = pl.p;
 
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int nvec = p.nvec;
-    wg_prologue<MAXW>(rows, red2, tid, nthreads);
+    wg_prologue<MAXW, G, MAXB>(&rows[0][0], red2, tid, nthreads);
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
         const int64_t row = t * (int64_t)nvec;
@@ -723,17 +794,17 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
         uint4 a[VPT], b[VPT], c[VPT];
         {
             uint4 k[B + 1][VPT];
-            stream_batch<B + 1, G, LA, true, true, ADD2, VPT>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot,
+            stream_batch<B + 1, G, LA, true, true, ADD2, VPT, MAXB>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot,
                                                               tid, nthreads);
         }
         for (int bi = 0; bi < pl.n_full; ++bi) {
             uint4 k[B][VPT];
-            stream_batch<B, G, LA, false, false, ADD2, VPT>(p, pl.more + bi * B, row, vc, a, b, c, k, q, ok, mx,
+            stream_batch<B, G, LA, false, false, ADD2, VPT, MAXB>(p, pl.more + bi * B, row, vc, a, b, c, k, q, ok, mx,
                                                             rows, tot, tid, nthreads);
         }
         {
             uint4 k[NB_LAST][VPT];
-            stream_batch<NB_LAST, G, LA, false, false, ADD2, VPT>(p, pl.more + pl.n_full * B, row, vc, a, b, c, k,
+            stream_batch<NB_LAST, G, LA, false, false, ADD2, VPT, MAXB>(p, pl.more + pl.n_full * B, row, vc, a, b, c, k,
                                                                   q, ok, mx, rows, tot, tid, nthreads);
         }
         wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
@@ -967,11 +1038,20 @@ using Kernel = void (*)(Params);
 
 constexpr int WG_GROUP = 2;     // sources per reduction group in kernel W
 constexpr int WG_LOOKAHEAD = 1; // groups whose loads are in flight ahead of the one being mixed
+// Kernel W with at most SHORT_WG_THREADS threads of one vector each (H <=
+// 2048): a token's rows are short, every load is in flight at once, and the
+// time goes to the rounds of workgroup sums, so all sources of a pass form one
+// group with one round of group_sums_wide (H = 896, N = 12: 5.69 -> 4.26 us per
+// call for one token, 6.53 -> 5.28 for 256, against groups of two).  It holds
+// 128 VGPRs, so for large M (see Plan::single_group) the form with groups of
+// two, at 62, keeps more waves per CU and wins.
+constexpr int WG_SHORT_GROUP = MAX_SNAP + 1;
+constexpr int WG_SHORT_LOOKAHEAD = 1;
 
-template <bool A2, int VPT, int MAXB, int G, int... I>
+template <bool A2, int VPT, int MAXB, int G, int LA, int... I>
 constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I...>)
 {
-    return {{&fwd_wg<I, A2, VPT, MAXB, G, WG_LOOKAHEAD>...}};
+    return {{&fwd_wg<I, A2, VPT, MAXB, G, LA>...}};
 }
 
 template <bool A2, int MAXB, int MAXC, int WPE, int... I>
@@ -984,12 +1064,15 @@ using Seq = std::make_integer_sequence<int, MAX_SNAP + 1>;
 using SeqSplitSmall = std::make_integer_sequence<int, MAX_SPLIT_SNAP + 1>;
 
 // [add2][N]
-const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024, WG_GROUP>(Seq{}),
-                                                  wg_table<true, 1, 1024, WG_GROUP>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GROUP>(Seq{}),
-                                                  wg_table<true, 2, 512, WG_GROUP>(Seq{})};
-const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512, WG_GROUP>(Seq{}),
-                                                  wg_table<true, 4, 512, WG_GROUP>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg1[2] = {wg_table<false, 1, 1024, WG_GROUP, WG_LOOKAHEAD>(Seq{}),
+                                                  wg_table<true, 1, 1024, WG_GROUP, WG_LOOKAHEAD>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg1Small[2] = {
+    wg_table<false, 1, SHORT_WG_THREADS, WG_SHORT_GROUP, WG_SHORT_LOOKAHEAD>(Seq{}),
+    wg_table<true, 1, SHORT_WG_THREADS, WG_SHORT_GROUP, WG_SHORT_LOOKAHEAD>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg2[2] = {wg_table<false, 2, 512, WG_GROUP, WG_LOOKAHEAD>(Seq{}),
+                                                  wg_table<true, 2, 512, WG_GROUP, WG_LOOKAHEAD>(Seq{})};
+const std::array<Kernel, MAX_SNAP + 1> kWg4[2] = {wg_table<false, 4, 512, WG_GROUP, WG_LOOKAHEAD>(Seq{}),
+                                                  wg_table<true, 4, 512, WG_GROUP, WG_LOOKAHEAD>(Seq{})};
 // more than MAX_SNAP snapshots: [add2][size of the last batch - 1]
 using KernelLong = void (*)(ParamsLong);
 
@@ -1127,7 +1210,8 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
         p.timeouts = sc->timeouts;
         fn = pl.threads <= 128 ? kSpSmall[a2][n_snapshots] : kSpLarge[a2][n_snapshots];
     } else {
-        fn = (pl.vpt == 1 ? kWg1 : pl.vpt == 2 ? kWg2 : kWg4)[a2][n_snapshots];
+        const auto& wg1 = pl.single_group ? kWg1Small : kWg1;
+        fn = (pl.vpt == 1 ? wg1 : pl.vpt == 2 ? kWg2 : kWg4)[a2][n_snapshots];
     }
     void* args[] = {&p};
     if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)pl.grid), dim3(pl.threads),

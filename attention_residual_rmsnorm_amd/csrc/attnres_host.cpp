@@ -33,11 +33,13 @@ bool plan_wg(int64_t M, int nvec, int vpt, Plan& pl)
     const int threads = std::max(64, round_up64((nvec + vpt - 1) / vpt));
     if (threads > maxb)
         return false;
+    pl = Plan{};
     pl.variant = 1;
     pl.vpt = vpt;
     pl.threads = threads;
     pl.chunks = 1;
     pl.grid = std::min<int64_t>(M, int64_t(1) << 20);
+    pl.single_group = vpt == 1 && threads <= SHORT_WG_THREADS && M * threads <= SHORT_WG_MAX_THREADS_TOTAL;
     return true;
 }
 
@@ -55,6 +57,7 @@ bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
     const int chunks = (nvec + threads - 1) / threads;
     if (chunks > (waves <= 2 ? MAX_CHUNKS : 8) || M > MAX_SPLIT_TOKENS)
         return false;
+    pl = Plan{};
     pl.variant = 2;
     pl.vpt = 1;
     pl.threads = threads;
@@ -165,8 +168,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         return plan_split(M, nvec, many && force_param == 0 ? 2 : force_param, pl) ? ATTNRES_OK
                                                                                     : ATTNRES_EINVAL;
     }
-    // Automatic, from per-call times of every variant on MI355X at H = 7168
-    // (graph replay, inputs cold in HBM, M = 1..512, N = 1..12):
+    // Automatic, from per-call times of every variant on MI355X (graph
+    // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
     //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
     //  * N >= 3, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
     //    each token over the most CUs (one token: 2-wave chunks, whose
@@ -175,7 +178,20 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //  * M <= 64 with N >= 8: 4-wave chunks, or 2-wave chunks above 12
     //    sources (only that family holds them);
     //  * otherwise one workgroup per token.
-    if (n > 2) {
+    // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
+    // on one CU, and the exchange of a split costs more than it spreads.
+    //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
+    //    against 5.7 us for one token, 5.2 against 6.3 for 256);
+    //  * H = 3584 / 4096: with N >= 8 and M <= 64 the split still wins
+    //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us).
+    if (n > 2 && !many && nvec < LONG_ROW_VECTORS) {
+        if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP) {
+            if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
+                return ATTNRES_OK;
+            if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
+                return ATTNRES_OK;
+        }
+    } else if (n > 2) {
         if (!many && M >= 2 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
         const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_2WAVE_TOKENS) ||

@@ -22,6 +22,20 @@ constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_2WAVE_TOKENS = 24;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_MID_TOKENS = 64;
+// Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one
+// workgroup per token at every M and N <= 12; rows shorter than
+// LONG_ROW_VECTORS (H < 7168) are split only with N >= MID_SPLIT_MIN_SNAP and
+// M <= SPLIT_MID_TOKENS (1 wave per workgroup up to SPLIT_SMALL_TOKENS_WIDE
+// tokens); rows of LONG_ROW_VECTORS and more follow the rules above.
+constexpr int SHORT_ROW_VECTORS = 256;
+constexpr int LONG_ROW_VECTORS = 896;
+constexpr int MID_SPLIT_MIN_SNAP = 8;
+// Kernel W's single-group form (one vector per thread, at most
+// SHORT_WG_THREADS threads) while M * threads <= SHORT_WG_MAX_THREADS_TOTAL:
+// beyond that the form with groups of two keeps more waves per CU and streams
+// faster.
+constexpr int SHORT_WG_THREADS = 256;
+constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 65536;
 
 struct Plan {
     int variant = 0; // 1 = workgroup per token, 2 = split hidden
@@ -29,6 +43,7 @@ struct Plan {
     int threads = 0; // threads per workgroup
     int chunks = 1;  // workgroups per token
     int64_t grid = 0;
+    bool single_group = false; // kernel W: all sources of a pass in one group
 };
 
 // Full validation of a fused call; returns a status code (ATTNRES_*).

@@ -42,7 +42,9 @@ Also reported on the same JSON line:
   prefill       prefill-sized calls (M = 1,024 and 4,096, N = 12): µs per call
                 and the fraction of 8 TB/s
 
-Every timing follows a parity check against the CPU oracle.
+--mode grid prints µs per call and GB/s over a grid of token and source counts
+at H = 7168 ("grid") and at one tensor-parallel rank's 896 columns of it
+("tp8_share").  Every timing follows a parity check against the CPU oracle.
 """
 from __future__ import annotations
 
@@ -555,11 +557,12 @@ def fold_suite(launcher, cold_bytes=1.1e9):
 
 
 def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), Ns=(0, 1, 2, 4, 8, 12),
-               cold_bytes=1.1e9):
-    """The metric over a grid of token and source counts (H = 7168, add2,
-    automatic dispatch): µs per call with inputs cold in HBM (graph replay of
-    one launch per distinct buffer set over >= 1.1 GB of sets) and the
-    achieved GB/s of the algorithmic bytes."""
+               H=7168, cold_bytes=1.1e9, max_sets=20000):
+    """The metric over a grid of token and source counts (add2, automatic
+    dispatch): µs per call with inputs cold in HBM (graph replay of one launch
+    per distinct buffer set over >= 1.1 GB of sets, or over max_sets sets for
+    the smallest calls, still more than the 256 MB Infinity Cache holds) and
+    the achieved GB/s of the algorithmic bytes."""
     import torch
 
     from attention_residual_rmsnorm_amd import workloads as W
@@ -567,15 +570,16 @@ def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), Ns=(0
     out = []
     for N in Ns:
         for M in Ms:
-            case = W.make_case(cfg=93, M=M, N=N, add2=True)
+            case = W.make_case(cfg=93, M=M, N=N, add2=True, H=H)
             nbytes = call_bytes(M, case.H, N, True)
-            nsets = max(64, int(cold_bytes // nbytes) + 1)
+            nsets = min(max_sets, max(64, int(cold_bytes // nbytes) + 1))
             pool, sets = pool_sets(launcher, case, nsets)
             args = sets["fused"]
             sec, _ = graph_time(lambda s: [launcher.run_fused(a, s) for a in args], 3, 1)
             us = sec / nsets * 1e6
             plan = launcher.ar.attnres_plan(M, N, case.H)
-            row = {"M": M, "N": N, "us_per_call": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            row = {"M": M, "N": N, "H": H, "us_per_call": round(us, 3),
+                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                    "frac": round(nbytes / (us * 1e-6) / 8e12, 4),
                    "kernel": "W" if plan[0] == 1 else "S%dw" % (plan[2] // 64)}
             log("grid %s" % row)
@@ -660,7 +664,8 @@ def main():
                          "calibration kernel for the HBM byte counters; latency: the parity gate, "
                          "then only the small named calls and the per-config fold comparison "
                          "(for kernel-trace profiling of the latency workloads); grid: the parity "
-                         "gate, then µs per call and GB/s over a grid of token and source counts")
+                         "gate, then µs per call and GB/s over a grid of token and source counts, "
+                         "at H=7168 and at one tensor-parallel rank's share of it (H=896)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     args = ap.parse_args()
@@ -699,7 +704,9 @@ def main():
     parity_gate(chain, launcher, oracle.get())
 
     if args.mode == "grid":
-        res = {"mode": "grid", "grid": grid_suite(launcher)}
+        # the full hidden size, then one tensor-parallel rank's share of it (7168 / 8 columns)
+        res = {"mode": "grid", "grid": grid_suite(launcher),
+               "tp8_share": grid_suite(launcher, Ms=(1, 8, 16, 32, 256), Ns=(4, 12), H=896)}
         assert launcher.ar.attnres_debug_timeouts() == 0
         print(json.dumps(res))
         return

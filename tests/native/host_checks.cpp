@@ -76,8 +76,8 @@ int main()
                         continue;
                     for (int64_t m : {int64_t(1), int64_t(8), int64_t(64), int64_t(65), int64_t(512),
                                       int64_t(513), int64_t(1) << 21})
-                        for (int64_t h : {int64_t(8), int64_t(520), int64_t(7168), int64_t(8192),
-                                          int64_t(16384)}) {
+                        for (int64_t h : {int64_t(8), int64_t(520), int64_t(896), int64_t(2048),
+                                          int64_t(3584), int64_t(7168), int64_t(8192), int64_t(16384)}) {
                             const int rc = make_plan(m, n, h, fv, fp, pl);
                             if (rc == ATTNRES_OK) {
                                 EXPECT(pl.threads % 64 == 0 && pl.threads >= 64 && pl.threads <= 1024);
@@ -86,6 +86,10 @@ int main()
                                 if (n > MAX_SNAP)
                                     EXPECT((pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4)) ||
                                            (pl.variant == 2 && n <= MAX_SPLIT_SNAP && pl.threads <= 128));
+                                // the single-group table is built for at most SHORT_WG_THREADS
+                                if (pl.single_group)
+                                    EXPECT(pl.variant == 1 && pl.vpt == 1 && pl.threads <= SHORT_WG_THREADS &&
+                                           m * pl.threads <= SHORT_WG_MAX_THREADS_TOTAL);
                                 if (pl.variant == 2)
                                     EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
                                            pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&
@@ -97,6 +101,19 @@ int main()
                         }
                 }
         }
+    }
+    // kernel W's single-group form: short rows, up to 65536 threads per call
+    {
+        Plan pl;
+        EXPECT(make_plan(512, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && pl.threads == 128 &&
+               pl.single_group);
+        EXPECT(make_plan(513, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(256, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.threads == 256 && pl.single_group);
+        EXPECT(make_plan(257, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(1, 12, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 2);
+        EXPECT(make_plan(1, 4, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(1, 12, 7168, 1, 1, pl) == ATTNRES_OK && pl.threads == 896 && !pl.single_group);
+        EXPECT(make_plan(1, 13, 896, 1, 0, pl) == ATTNRES_OK && pl.vpt == 2 && !pl.single_group);
     }
     EXPECT(validate_fwd(nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr, 1e-6f, 0, H, nullptr,
                         nullptr) == ATTNRES_OK);

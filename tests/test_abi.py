@@ -186,6 +186,15 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(65, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
     assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
+    # shorter rows (a tensor-parallel rank's share of the hidden size)
+    assert ar.attnres_plan(1, 12, 896) == (1, 1, 128)      # H <= 2048: workgroup per token
+    assert ar.attnres_plan(256, 12, 896) == (1, 1, 128)
+    assert ar.attnres_plan(8, 12, 2048) == (1, 1, 256)
+    assert ar.attnres_plan(1, 12, 3584) == (2, 7, 64)      # H < 7168, N >= 8: 1-wave chunks up to 32 tokens
+    assert ar.attnres_plan(32, 8, 4096) == (2, 8, 64)
+    assert ar.attnres_plan(64, 12, 3584) == (2, 4, 128)    # then 2-wave chunks up to 64
+    assert ar.attnres_plan(65, 12, 3584)[0] == 1
+    assert ar.attnres_plan(1, 7, 3584)[0] == 1             # fewer sources: workgroup per token
     with pytest.raises(ar.AttnResError):
         ar.attnres_plan(1, 65, 7168)
     with pytest.raises(ar.AttnResError):

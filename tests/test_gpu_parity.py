@@ -204,6 +204,34 @@ def test_dispatch_boundaries(ar, orc, M, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
 
 
+# (M, H, N): kernel W's single-group form (rows of at most 256 vectors, up to
+# 65536 threads per call) on both sides of its bound, ragged short rows, and
+# the split bounds for rows of 257..895 vectors; H = 896 is a tensor-parallel
+# rank's share (1/8) of 7168
+SHORT_ROWS = [(1, 896, n) for n in (0, 1, 3, 4, 5, 8, 12)] + [
+    (7, 904, 2), (7, 904, 5), (7, 904, 12), (512, 896, 12), (513, 896, 12), (256, 2048, 8), (257, 2048, 8),
+    (33, 2048, 12), (1, 3584, 12), (32, 3584, 8), (33, 3584, 12), (65, 3584, 12), (3, 4096, 7)]
+
+
+@pytest.mark.parametrize("M,H,N", SHORT_ROWS)
+def test_short_rows(ar, orc, M, H, N):
+    """Rows shorter than 7168 under the automatic dispatch."""
+    case = case_for(("short", M, H, N), lambda: W.make_case(cfg=63, M=M, H=H, N=N, add2=(M % 2 == 1)))
+    say("short rows", M, H, N, ar.attnres_plan(M, N, H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+
+
+def test_short_rows_deterministic(ar):
+    """The single-group form's sums run in a fixed order: same bits every call."""
+    case = case_for(("short-det", 512, 896, 12), lambda: W.make_case(cfg=63, M=512, H=896, N=12, add2=True))
+    first = P.run_gpu(case)
+    for _ in range(10):
+        again = P.run_gpu(case)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
 def _random_cases(n=40, seed=2026):
     rng = np.random.default_rng(seed)
     out = []
