@@ -169,6 +169,37 @@ def test_golden_fold_add(ar, variant):
         assert np.all(gp1[k] == rows[i][3])
 
 
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+@pytest.mark.parametrize("add2", [True, False], ids=["add2", "no_add2"])
+def test_fold_every_bit_pattern(ar, orc, variant, add2):
+    """out_prefix is bit-exact for every input, special values included: each of
+    prefix, add and add2 holds every bf16 bit pattern once (NaN, +-Inf,
+    subnormals, +-0, sums that overflow to Inf), at different offsets, against
+    the oracle's two tensor additions; a NaN result only has to be a NaN.
+    (out_norm is outside the parity contract for non-finite inputs.)"""
+    import dataclasses
+
+    M, H = 10, 7168
+    rng = np.random.default_rng(91)
+    every = np.arange(1 << 16, dtype=np.uint16)
+
+    def field(shift):
+        v = rng.integers(0, 1 << 16, M * H).astype(np.uint16)
+        v[:1 << 16] = np.roll(every, shift)
+        return v.reshape(M, H)
+
+    prefix, add, add2v = field(0), field(12345), field(40000)
+    base = case_for(("fold-bits",), lambda: W.make_case(cfg=64, M=M, N=2, add2=True))
+    case = dataclasses.replace(base, prefix=prefix, add=add, add2=add2v if add2 else None)
+    say("fold bit patterns", variant, add2, ar.attnres_plan(M, 2, H))
+    gp, _ = P.run_gpu(case)
+    t = orc.add_tensor(add.ravel(), add2v.ravel()) if add2 else add.ravel()
+    want = orc.add_tensor(prefix.ravel(), t).reshape(M, H)
+    nan = P.is_nan16(want)
+    assert np.array_equal(gp[~nan], want[~nan]), "out_prefix differs at %d places" % int((gp[~nan] != want[~nan]).sum())
+    assert np.all(P.is_nan16(gp[nan]))
+
+
 # --- ragged, tiny and maximal shapes -----------------------------------------
 
 SHAPES = [
