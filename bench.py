@@ -42,6 +42,10 @@ Also reported on the same JSON line:
   prefill       prefill-sized calls (M = 1,024 and 4,096, N = 12): µs per call
                 and the fraction of 8 TB/s
 
+parity_after_timing: after the timed replays, every micro-batch instance's
+outputs on sampled token rows of every layer against the oracle chain, and
+the instances against each other bit for bit.
+
 --mode grid prints µs per call and GB/s over a grid of token and source counts
 at H = 7168 ("grid") and at one tensor-parallel rank's 896 columns of it
 ("tp8_share").  Every timing follows a parity check against the CPU oracle.
@@ -324,6 +328,31 @@ def parity_gate(chain, launcher, orc):
         if not norm_ok(gn, rn):
             raise SystemExit("parity gate: layer %d out_norm outside 2 ulps of the oracle" % l)
     log("parity gate: 25 layers, %d sampled tokens: ok" % len(idx))
+    return idx, ref
+
+
+def verify_instances(dc, idx, ref):
+    """After the timed graph replays: every micro-batch instance's outputs, on
+    the sampled token rows of every layer, against the oracle chain (bit-exact
+    prefixes, out_norm within 2 ulps), and the instances against each other
+    bit for bit (same inputs, same dispatch)."""
+    import numpy as np
+    import torch
+
+    torch.cuda.synchronize()
+    first = None
+    for i, c in enumerate(dc.inst):
+        got = [(host(c["out_prefix"][l])[idx], host(c["out_norm"][l])[idx]) for l in range(len(dc.layers))]
+        for l, ((gp, gn), (rp, rn)) in enumerate(zip(got, ref)):
+            if not np.array_equal(gp, rp):
+                raise SystemExit("after timing: instance %d layer %d out_prefix differs from the oracle" % (i, l))
+            if not norm_ok(gn, rn):
+                raise SystemExit("after timing: instance %d layer %d out_norm outside 2 ulps of the oracle" % (i, l))
+        if first is None:
+            first = got
+        elif not all(np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) for a, b in zip(got, first)):
+            raise SystemExit("after timing: instance %d differs from instance 0" % i)
+    return {"instances": len(dc.inst), "layers": len(dc.layers), "tokens_sampled": int(len(idx)), "ok": True}
 
 
 def cpu_baseline(chain, threads, min_cpu_seconds=12.0, max_passes=8):
@@ -701,7 +730,7 @@ def main():
 
     import oracle
 
-    parity_gate(chain, launcher, oracle.get())
+    gate_idx, gate_ref = parity_gate(chain, launcher, oracle.get())
 
     if args.mode == "grid":
         # the full hidden size, then one tensor-parallel rank's share of it (7168 / 8 columns)
@@ -733,6 +762,9 @@ def main():
     nbytes = dc.bytes_per_step()
     value = nbytes / sec / 1e9
     log("step: %.3f ms, %.1f GB/s" % (sec * 1e3, value))
+    # what the timed replays left in every instance's outputs
+    after_timing = verify_instances(dc, gate_idx, gate_ref)
+    log("after timing: %s" % after_timing)
 
     # the fused kernel's average launch duration over the timed region (the
     # replayed graph holds nothing but the step's fused launches)
@@ -779,6 +811,7 @@ def main():
                    "micro_batches": args.micro_batches, "calls_per_step": launches,
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": roofline,
+        "parity_after_timing": after_timing,
     }
 
     if args.mode == "full":
