@@ -48,6 +48,16 @@ namespace attnres {
 constexpr int REC_STRIDE = 64;           // records per (token, chunk) of the first exchange (>= 2*32)
 constexpr int STATE_STRIDE = 32;         // epoch word per token: one 128-byte line each
 constexpr unsigned SPIN_LIMIT = 1u << 20;
+// Kernel S with at most GRAM_MAX_SOURCES sources (attnres_host.hpp) takes one
+// exchange instead of two (the Gram form, see fwd_split).  Its sum of x^2,
+// alpha' G alpha, is used when GRAM_COND * (sum x^2 / H + eps) >=
+// (sum_s alpha_s |k_s|)^2 / H: then the rounding of G's entries, at most a few
+// binary32 ulps of |k_s||k_t| each, moves sum x^2 / H + eps by no more than
+// about GRAM_COND such ulps relative; when the sources cancel more than that,
+// the second exchange runs instead.
+constexpr float GRAM_COND = 64.f;
+static_assert(GRAM_MAX_SOURCES + GRAM_MAX_SOURCES * (GRAM_MAX_SOURCES + 1) / 2 <= REC_STRIDE,
+              "the Gram form's first exchange: one record per value");
 
 struct Params {
     const uint4* prefix;
@@ -178,6 +188,34 @@ __device__ __forceinline__ float2 source_partial(const uint4 (&x)[VPT], const ui
         qd += ok[j] ? qdj : 0.f;
     }
     return make_float2(ss, qd);
+}
+
+// Position of G_st (s <= t) among the S(S+1)/2 entries of the upper triangle
+// of the Gram matrix, row by row.
+__host__ __device__ constexpr int gram_index(int s, int t, int S) { return s * S - s * (s - 1) / 2 + (t - s); }
+
+// A2 of kernel S's Gram form: part[s] = q.k_s for s < S and
+// part[S + gram_index(s, t)] = k_s.k_t for s <= t (the diagonal is sum k_s^2,
+// summed in the same order as source_partial's).
+template <int S>
+__device__ __forceinline__ void gram_partials(const uint4 (&k)[S][1], const uint4* q, const bool* ok, float* part)
+{
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        float qd = dot2_bf16(q[0].x, k[s][0].x, 0.f);
+        qd = dot2_bf16(q[0].y, k[s][0].y, qd);
+        qd = dot2_bf16(q[0].z, k[s][0].z, qd);
+        qd = dot2_bf16(q[0].w, k[s][0].w, qd);
+        part[s] = ok[0] ? qd : 0.f;
+#pragma unroll
+        for (int t = s; t < S; ++t) {
+            float g = dot2_bf16(k[s][0].x, k[t][0].x, 0.f);
+            g = dot2_bf16(k[s][0].y, k[t][0].y, g);
+            g = dot2_bf16(k[s][0].z, k[t][0].z, g);
+            g = dot2_bf16(k[s][0].w, k[t][0].w, g);
+            part[S + gram_index(s, t, S)] = ok[0] ? g : 0.f;
+        }
+    }
 }
 
 // A2 for every source: part[2s] = sum k_s^2, part[2s+1] = q.k_s.
@@ -822,9 +860,16 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 // Exchanges (see attnres_device.hpp): the call's epoch E is read from the
 // token's state word at the start; the A2 partials travel with tag 2E+1, the
 // chunk sums of x^2 with tag 2E+2.  Chunk 0 advances the state word to E+1
-// after it has seen every chunk's second record, i.e. after every workgroup of
+// after it has seen every chunk's last record, i.e. after every workgroup of
 // the token has read E, so all workgroups of one call agree on E, and every
 // call (HIP-graph replays included) uses new tags.
+//
+// Gram form (S <= GRAM_MAX_SOURCES): the first exchange carries q.k_s and the
+// chunk's Gram entries k_s.k_t (s <= t) instead of q.k_s and sum k_s^2.  The
+// diagonal gives the logits as before, and sum_h x_h^2 = alpha' G alpha, so
+// the second exchange is needed only when that form is ill-conditioned
+// (GRAM_COND); every workgroup of the token takes the same decision, from the
+// same totals in the same order.
 //
 // Two families: MAXB = 128 (1-2 waves per workgroup, up to 32 chunks) and
 // MAXB = 512 (4-8 waves, at most 8 chunks; capped at 128 VGPRs so that two
@@ -833,7 +878,8 @@ template <int NS, bool ADD2, int MAXB, int MAXC, int WPE>
 __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
 {
     constexpr int S = NS + 1;
-    constexpr int NV = 2 * S;
+    constexpr bool GRAM = S <= GRAM_MAX_SOURCES;
+    constexpr int NV = GRAM ? S + S * (S + 1) / 2 : 2 * S; // values of the first exchange
     constexpr int NVP = (NV + 3) / 4 * 4;
     constexpr int MAXROWS = MAXB / 16;
     static_assert(S <= 32 && NV <= 64 && NV <= REC_STRIDE && MAXC <= 64, "one lane per value and per chunk");
@@ -845,6 +891,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     __shared__ float red2[MAXB / 64];
     __shared__ float alpha_sh[PERWAVE ? 1 : 32];
     __shared__ float ssum_sh;
+    __shared__ float gram_sh[2]; // Gram form, 4-8 waves: wave 0's sum of x^2 and decision
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -880,7 +927,10 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     // A2: this chunk's partials (row sums on DPP, rows through LDS); thread
     // v < NV adds the rows of value v and publishes it
     float part[NV];
-    source_partials<S, 1>(k, q, ok, part);
+    if constexpr (GRAM)
+        gram_partials<S>(k, q, ok, part);
+    else
+        source_partials<S, 1>(k, q, ok, part);
     fence_sources<S, 1>(k);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
@@ -920,6 +970,8 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     // whose logit, the wave's maximum and the exponentials' sum (DPP and
     // scalar reads, fixed order) give alpha_s in lane 2s.
     float alpha[S];
+    float gram_ssum = 0.f; // Gram form: alpha' G alpha
+    int use_gram = 0;      // Gram form: 1 when it is well-conditioned (same in every workgroup)
     if (PERWAVE || wave == 0) {
         const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
         float tv = 0.f;
@@ -949,19 +1001,58 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             for (int j = 0; j < 8; ++j)
                 tv += __uint_as_float((unsigned)r0[j]);
         }
-        const float qd = dpp<0xb1>(tv); // quad_perm [1,0,3,2]: lane 2s gets lane 2s+1's value
-        const bool src = (lane & 1) == 0 && lane < NV;
-        const float z = src ? rsqrtf(tv * p.inv_h + p.eps) * qd : -INFINITY;
-        const float zmax = wave_max(z);
-        const float e = src ? __expf(z - zmax) : 0.f;
-        const float den = wave_sum(e);
-        const float al = e * (1.0f / den);
-        if constexpr (PERWAVE) {
+        float al;
+        if constexpr (GRAM) {
+            // lane s < S holds q.k_s and fetches G_ss; alpha_s ends in lane s.
+            // Lane S + gram_index(s, t) holds G_st and fetches alpha_s, alpha_t.
+            const bool src = lane < S;
+            const float gss = __shfl(tv, src ? S + gram_index(lane, lane, S) : lane);
+            const float z = src ? rsqrtf(gss * p.inv_h + p.eps) * tv : -INFINITY;
+            const float zmax = wave_max(z);
+            const float e = src ? __expf(z - zmax) : 0.f;
+            const float den = wave_sum(e);
+            al = e * (1.0f / den);
+            int ps = 0, pt = 0, r = lane - S;
 #pragma unroll
-            for (int i = 0; i < S; ++i)
-                alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * i));
-        } else if (src) {
-            alpha_sh[lane >> 1] = al;
+            for (int s = 0; s < S; ++s) {
+                if (r >= 0 && r < S - s) {
+                    ps = s;
+                    pt = s + r;
+                }
+                r -= S - s;
+            }
+            const float as = __shfl(al, ps), at = __shfl(al, pt);
+            const bool entry = lane >= S && lane < NV;
+            gram_ssum = wave_sum(entry ? ((ps == pt ? 1.f : 2.f) * (as * at)) * tv : 0.f);
+            const float cs = wave_sum(src ? al * sqrtf(gss) : 0.f);
+            use_gram = GRAM_COND * (gram_ssum * p.inv_h + p.eps) >= (cs * cs) * p.inv_h ? 1 : 0;
+            if constexpr (PERWAVE) {
+#pragma unroll
+                for (int i = 0; i < S; ++i)
+                    alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), i));
+            } else {
+                if (src)
+                    alpha_sh[lane] = al;
+                if (lane == 0) {
+                    gram_sh[0] = gram_ssum;
+                    gram_sh[1] = use_gram ? 1.f : 0.f;
+                }
+            }
+        } else {
+            const float qd = dpp<0xb1>(tv); // quad_perm [1,0,3,2]: lane 2s gets lane 2s+1's value
+            const bool src = (lane & 1) == 0 && lane < NV;
+            const float z = src ? rsqrtf(tv * p.inv_h + p.eps) * qd : -INFINITY;
+            const float zmax = wave_max(z);
+            const float e = src ? __expf(z - zmax) : 0.f;
+            const float den = wave_sum(e);
+            al = e * (1.0f / den);
+            if constexpr (PERWAVE) {
+#pragma unroll
+                for (int i = 0; i < S; ++i)
+                    alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * i));
+            } else if (src) {
+                alpha_sh[lane >> 1] = al;
+            }
         }
     }
     if constexpr (!PERWAVE) {
@@ -969,45 +1060,59 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
 #pragma unroll
         for (int i = 0; i < S; ++i)
             alpha[i] = alpha_sh[i];
+        if constexpr (GRAM) {
+            gram_ssum = gram_sh[0];
+            use_gram = gram_sh[1] != 0.f ? 1 : 0;
+        }
     }
+    // the same value in every lane and wave of the workgroup: a scalar branch
+    use_gram = __builtin_amdgcn_readfirstlane(use_gram);
 
     // A4
     float x[1][8];
     const float sx = wave_sum(combine<S, 1>(k, alpha, ok, x));
-    if (lane == 0)
-        red2[wave] = sx;
-    __syncthreads();
-
-    // A5: the chunk's sum of x^2 (its waves in order) published by thread 0;
-    // every wave (PERWAVE) or wave 0 reads the C records (lane c: chunk c) and
-    // adds them on DPP
-    unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
-    if (tid == 0) {
-        float s2 = red2[0];
-        for (int w = 1; w < nw; ++w)
-            s2 += red2[w];
-        publish(&rec2[chunk], tag2, s2);
-    }
     float ssum = 0.f;
-    if (PERWAVE || wave == 0) {
-        unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
-        for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
-            if (polls >= p.spin_limit) {
-                atomicAdd(p.timeouts, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            w2 = peek(&rec2[lane]);
-        }
-        ssum = wave_sum(__uint_as_float((unsigned)w2));
-        if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
+    if (GRAM && use_gram) {
+        // A5 from alpha' G alpha: no second exchange.  Chunk 0 has seen every
+        // chunk's first record, so every workgroup of the token has read E.
+        ssum = gram_ssum;
+        if (chunk == 0 && tid == 0)
             __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!PERWAVE && lane == 0)
-            ssum_sh = ssum;
-    }
-    if constexpr (!PERWAVE) {
+    } else {
+        if (lane == 0)
+            red2[wave] = sx;
         __syncthreads();
-        ssum = ssum_sh;
+
+        // A5: the chunk's sum of x^2 (its waves in order) published by thread 0;
+        // every wave (PERWAVE) or wave 0 reads the C records (lane c: chunk c) and
+        // adds them on DPP
+        unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
+        if (tid == 0) {
+            float s2 = red2[0];
+            for (int w = 1; w < nw; ++w)
+                s2 += red2[w];
+            publish(&rec2[chunk], tag2, s2);
+        }
+        if (PERWAVE || wave == 0) {
+            unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
+            for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
+                if (polls >= p.spin_limit) {
+                    atomicAdd(p.timeouts, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                w2 = peek(&rec2[lane]);
+            }
+            ssum = wave_sum(__uint_as_float((unsigned)w2));
+            if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
+                __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!PERWAVE && lane == 0)
+                ssum_sh = ssum;
+        }
+        if constexpr (!PERWAVE) {
+            __syncthreads();
+            ssum = ssum_sh;
+        }
     }
     const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
     if (ok[0]) {

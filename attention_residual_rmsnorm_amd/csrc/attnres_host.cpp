@@ -170,8 +170,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     }
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
-    //  * N <= 2: one workgroup per token at every M (small rows, no exchange);
-    //  * N >= 3, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
+    //  * 1 <= N <= 6, M <= 32: 2-wave chunks, whose Gram form needs one
+    //    exchange (M = 1, N = 4: 4.94 against 5.61 us with two; M = 8, N = 2:
+    //    4.97 against 5.23 for one workgroup per token);
+    //  * N <= 2 otherwise, and N = 0: one workgroup per token;
+    //  * N >= 7, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
     //    each token over the most CUs (one token: 2-wave chunks, whose
     //    exchanges have half as many partners);
     //  * N >= 5: 2-wave chunks up to 24 tokens, and up to 32 with N < 8;
@@ -184,13 +187,17 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    against 5.7 us for one token, 5.2 against 6.3 for 256);
     //  * H = 3584 / 4096: with N >= 8 and M <= 64 the split still wins
     //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us).
-    if (n > 2 && !many && nvec < LONG_ROW_VECTORS) {
+    const bool long_rows = nvec >= LONG_ROW_VECTORS;
+    if (!long_rows && !many) {
         if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP) {
             if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
                 return ATTNRES_OK;
             if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
                 return ATTNRES_OK;
         }
+    } else if (long_rows && n >= 1 && n < GRAM_MAX_SOURCES && M <= SPLIT_SMALL_TOKENS_WIDE) {
+        if (plan_split(M, nvec, 2, pl))
+            return ATTNRES_OK;
     } else if (n > 2) {
         if (!many && M >= 2 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;

@@ -200,6 +200,49 @@ def test_fold_every_bit_pattern(ar, orc, variant, add2):
     assert np.all(P.is_nan16(gp[nan]))
 
 
+def _cancelling_case(N, noise=1e-3, M=3, H=7168, seed=5):
+    """Zero query (every logit 0, equal weights), p' = -snap_0 + noise, the
+    further snapshots in exactly opposite pairs and, if one is left, one of the
+    noise's size: the mixture is about `noise` of its terms."""
+    rng = np.random.default_rng(seed)
+    bf = lambda x: W.to_bf16_bits(np.asarray(x, np.float64))
+    f = lambda b: W.bf16_bits_to_f32(b).astype(np.float64)
+    s0 = bf(rng.standard_normal((M, H)))
+    snaps = [s0]
+    while N - len(snaps) >= 2:
+        s = bf(rng.standard_normal((M, H)))
+        snaps += [s, s ^ np.uint16(0x8000)]
+    if len(snaps) < N:
+        snaps.append(bf(noise * rng.standard_normal((M, H))))
+    assert len(snaps) == N
+    prefix = bf(-f(s0) + noise * rng.standard_normal((M, H)))
+    add = np.zeros((M, H), np.uint16)
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(H))
+    return W.Case("cancelling", M, H, prefix, add, None, snaps, np.zeros(H, np.uint16), gamma)
+
+
+@pytest.mark.parametrize("variant", [(0, 0), (2, 1), (2, 2), (2, 7)], ids=["auto", "S1w", "S2w", "S7w"],
+                         indirect=True)
+@pytest.mark.parametrize("noise", [1e-3, 0.15, 0.3, 0.6])
+@pytest.mark.parametrize("N", [1, 3, 4, 6])
+def test_cancelling_sources(ar, orc, variant, N, noise):
+    """Sources that nearly cancel.  The split kernel takes sum x^2 = alpha' G
+    alpha from its one exchange for few sources.  With noise 1e-3 that form
+    would lose most of sum x^2 to cancellation, so the kernel must detect it
+    and run the second exchange; with 0.15 the conditioning bound still sends
+    it there; with 0.6 (and 0.3 at N = 1) the sources cancel by a factor of
+    about 12 to 57, under the bound, so the form is accepted and its rounding
+    must stay far below the tolerance.  out_norm within the parity bound of
+    the oracle either way."""
+    case = case_for(("cancel", N, noise), lambda: _cancelling_case(N, noise))
+    say("cancelling sources", N, noise, variant, ar.attnres_plan(case.M, N, case.H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    x = np.abs(W.bf16_bits_to_f32(rn)).max()
+    assert x > 0.1, "the case must give a non-trivial normalised mixture"
+    P.assert_parity(gp, gn, rp, rn, "cancelling N=%d" % N)
+
+
 # --- ragged, tiny and maximal shapes -----------------------------------------
 
 SHAPES = [
@@ -221,13 +264,15 @@ def test_shapes(ar, orc, variant, M, H, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("N", [3, 4, 7, 8, 12])
+@pytest.mark.parametrize("N", [1, 3, 4, 6, 7, 8, 12])
 @pytest.mark.parametrize("M", [2, 16, 17, 24, 25, 32, 33, 64, 65])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
-    (1-wave chunks up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64,
-    then a workgroup per token) and source-count bounds (one group of up to four
-    sources in kernel W; the store policy changes at nine sources)."""
+    (2-wave chunks with one exchange up to 32 tokens for N <= 6; 1-wave chunks
+    up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64, then a workgroup
+    per token) and source-count bounds (the split kernel's single-exchange form
+    up to six snapshots; one group of up to four sources in kernel W; the store
+    policy changes at nine sources)."""
     case = case_for(("bound", M, N), lambda: W.make_case(cfg=62, M=M, N=N, add2=(M % 2 == 0)))
     say("boundary", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)
