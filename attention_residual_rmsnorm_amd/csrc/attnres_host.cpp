@@ -170,10 +170,13 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     }
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
-    //  * 1 <= N <= 6, M <= 32: 2-wave chunks, whose Gram form needs one
+    //  * 2 <= N <= 6, M <= 32: 2-wave chunks, whose Gram form needs one
     //    exchange (M = 1, N = 4: 4.94 against 5.61 us with two; M = 8, N = 2:
     //    4.97 against 5.23 for one workgroup per token);
-    //  * N <= 2 otherwise, and N = 0: one workgroup per token;
+    //  * N <= 2 otherwise, and N <= 1: one workgroup per token (at N = 1 the
+    //    split wins with add2 and loses without it, M = 1: 4.21 against 4.64
+    //    us and 4.37 against 4.30; the dispatch may not depend on add2, and
+    //    the named single-token call has none);
     //  * N >= 7, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
     //    each token over the most CUs (one token: 2-wave chunks, whose
     //    exchanges have half as many partners);
@@ -195,7 +198,7 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
             if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
                 return ATTNRES_OK;
         }
-    } else if (long_rows && n >= 1 && n < GRAM_MAX_SOURCES && M <= SPLIT_SMALL_TOKENS_WIDE) {
+    } else if (long_rows && n >= 2 && n < GRAM_MAX_SOURCES && M <= SPLIT_SMALL_TOKENS_WIDE) {
         if (plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
     } else if (n > 2) {

@@ -24,7 +24,7 @@ constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_MID_TOKENS = 64;
 // The split kernel's Gram form (one exchange instead of two) serves up to
 // GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).  With it, 2-wave
-// chunks win for 1 <= N <= GRAM_MAX_SOURCES - 1 up to SPLIT_SMALL_TOKENS_WIDE
+// chunks win for 2 <= N <= GRAM_MAX_SOURCES - 1 up to SPLIT_SMALL_TOKENS_WIDE
 // tokens (rows of LONG_ROW_VECTORS and more).
 constexpr int GRAM_MAX_SOURCES = 7;
 // Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one

@@ -175,7 +175,8 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(32, 4, 7168) == (2, 7, 128)
     assert ar.attnres_plan(33, 4, 7168)[0] == 1
     assert ar.attnres_plan(1, 2, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # no snapshot: workgroup per token
+    assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
+    assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(64, 2, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 2, 896) == (1, 1, 128)       # short rows stay on one workgroup per token
     assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks

@@ -264,11 +264,11 @@ def test_shapes(ar, orc, variant, M, H, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("N", [1, 3, 4, 6, 7, 8, 12])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 6, 7, 8, 12])
 @pytest.mark.parametrize("M", [2, 16, 17, 24, 25, 32, 33, 64, 65])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
-    (2-wave chunks with one exchange up to 32 tokens for N <= 6; 1-wave chunks
+    (2-wave chunks with one exchange up to 32 tokens for 2 <= N <= 6; 1-wave chunks
     up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64, then a workgroup
     per token) and source-count bounds (the split kernel's single-exchange form
     up to six snapshots; one group of up to four sources in kernel W; the store
