@@ -388,22 +388,44 @@ SYNC_VID = ["W", "S1w", "S2w", "S7w"]
 
 
 @pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
-def test_deterministic(ar, variant):
-    case = case_for("cfg4", lambda: W.config_case("cfg4"))
+@pytest.mark.parametrize("name", ["cfg4", "cfg2"])  # N = 12: two exchanges; N = 4: the Gram form's one
+def test_deterministic(ar, variant, name):
+    case = case_for(name, lambda: W.config_case(name))
     first = P.run_gpu(case)
     for _ in range(20):
         again = P.run_gpu(case)
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
+@pytest.mark.parametrize("variant", [(2, 1), (2, 2), (2, 7)], ids=["S1w", "S2w", "S7w"], indirect=True)
+def test_exchange_forms_alternate(ar, orc, variant):
+    """Calls with one exchange (the Gram form, N = 4), two exchanges (N = 8) and
+    the Gram form's fallback (cancelling sources, N = 4) in turn on the same
+    token slots: each form advances the per-token epoch at its own point, and
+    every call must still see only its own records (same bits as its first
+    run, within the bound of the oracle)."""
+    cases = [W.make_case(cfg=75, M=8, N=4, add2=True), W.make_case(cfg=76, M=8, N=8, add2=True),
+             _cancelling_case(4, 1e-3, M=8)]
+    first = [P.run_gpu(c) for c in cases]
+    for c, (gp, gn) in zip(cases, first):
+        rp, rn = P.run_oracle(orc, c)
+        P.assert_parity(gp, gn, rp, rn, c.name)
+    for rep in range(30):
+        i = (rep * 7) % 3
+        gp, gn = P.run_gpu(cases[i])
+        assert np.array_equal(gp, first[i][0]) and np.array_equal(gn, first[i][1]), "call %d (case %d)" % (rep, i)
+    assert ar.attnres_debug_timeouts() == 0
+
+
 @pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
-def test_graph_replay(ar, variant):
+@pytest.mark.parametrize("N", [8, 4])  # the split kernel's two exchanges, and its Gram form's one
+def test_graph_replay(ar, variant, N):
     """Capture one call into a HIP graph; replay it with fresh inputs copied
     in between (eager work and synchronisation between replays); every replay
     must equal the eager call on the same inputs, bit for bit."""
     import torch
 
-    cases = [W.make_case(cfg=70 + i, M=16, N=8, add2=True) for i in range(4)]
+    cases = [W.make_case(cfg=70 + i, M=16, N=N, add2=True) for i in range(4)]
     c0 = cases[0]
     d = P.dev
     ins = dict(prefix=d(c0.prefix), add=d(c0.add), add2=d(c0.add2), snaps=[d(s) for s in c0.snapshots],
