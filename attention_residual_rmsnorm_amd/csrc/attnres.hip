@@ -18,15 +18,19 @@
 //      the waves, and mixed two at a time as they arrive (up to four
 //      sources as one group), under a running softmax maximum and sum; each
 //      group's partials are summed on DPP within rows and by one wave across
-//      rows.  No inter-workgroup communication.  Used when there are many
-//      tokens, and for more than 12 sources (in batches of 12).
-// Outputs are written with the non-temporal hint in both kernels.
+//      rows.  With short rows (at most 256 threads of one vector) all sources
+//      form one group, summed in one round.  No inter-workgroup
+//      communication.  Used when there are many tokens, for short rows, and
+//      for more than 12 sources (in batches of 12).
 //   S  split hidden: C workgroups per token, each owning a contiguous chunk of
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
 //      chunk's share of sum x^2 are exchanged through tagged 64-bit records
-//      with relaxed device-scope atomics (no fences).  Spreads a few tokens
-//      over many CUs, which is what the latency-bound small-M calls need.
+//      with relaxed device-scope atomics (no fences); with at most seven
+//      sources the chunk's Gram matrix travels instead and one exchange gives
+//      both.  Spreads a few tokens over many CUs, which is what the
+//      latency-bound small-M calls need.
+// Outputs are written with the non-temporal hint in both kernels.
 // Both reduce in a fixed order: the same inputs give the same bits, and the
 // add2 / no-add2 instantiations share every line after A1.
 #include "attnres.h"
