@@ -173,15 +173,15 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //  * 2 <= N <= 6, M <= 32: 2-wave chunks, whose Gram form needs one
     //    exchange (M = 1, N = 4: 4.94 against 5.61 us with two; M = 8, N = 2:
     //    4.97 against 5.23 for one workgroup per token);
-    //  * N <= 2 otherwise, and N <= 1: one workgroup per token (at N = 1 the
-    //    split wins with add2 and loses without it, M = 1: 4.21 against 4.64
-    //    us and 4.37 against 4.30; the dispatch may not depend on add2, and
-    //    the named single-token call has none);
-    //  * N >= 7, 2 <= M <= 16: the call is latency-bound; 1-wave chunks spread
-    //    each token over the most CUs (one token: 2-wave chunks, whose
-    //    exchanges have half as many partners);
-    //  * N >= 5: 2-wave chunks up to 24 tokens, and up to 32 with N < 8;
-    //  * M <= 64 with N >= 8: 4-wave chunks, or 2-wave chunks above 12
+    //  * N <= 1 at every M, and N <= 6 above 32 tokens: one workgroup per
+    //    token (at N = 1 the split wins with add2 and loses without it, M = 1:
+    //    4.21 against 4.64 us and 4.37 against 4.30; the dispatch may not
+    //    depend on add2, and the named single-token call has none);
+    //  * N >= 7, the call latency-bound: one token takes 2-wave chunks (their
+    //    exchanges have half as many partners), 2..16 tokens 1-wave chunks
+    //    (spread over the most CUs), up to 24 tokens (N = 7: 32) 2-wave
+    //    chunks;
+    //  * N >= 8 up to 64 tokens: 4-wave chunks, or 2-wave chunks above 12
     //    sources (only that family holds them);
     //  * otherwise one workgroup per token.
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
