@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     attnres_add_rmsnorm_mix_fwd,
     attnres_bf16_add,
     attnres_debug_timeouts,
+    attnres_debug_set_spin_limit,
+    attnres_debug_reset_scratch,
     attnres_init,
     attnres_plan,
     attnres_selftest_rounding,

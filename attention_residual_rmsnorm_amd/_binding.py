@@ -62,6 +62,10 @@ def library():
         lib.attnres_set_variant.restype = ctypes.c_int
         lib.attnres_debug_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint)]
         lib.attnres_debug_timeouts.restype = ctypes.c_int
+        lib.attnres_debug_set_spin_limit.argtypes = [ctypes.c_uint]
+        lib.attnres_debug_set_spin_limit.restype = ctypes.c_int
+        lib.attnres_debug_reset_scratch.argtypes = []
+        lib.attnres_debug_reset_scratch.restype = ctypes.c_int
         lib.attnres_selftest_rounding.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
         lib.attnres_selftest_rounding.restype = ctypes.c_int
         lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -202,6 +206,14 @@ def attnres_debug_timeouts() -> int:
     out = ctypes.c_uint()
     _check(library().attnres_debug_timeouts(ctypes.byref(out)), "attnres_debug_timeouts")
     return out.value
+
+
+def attnres_debug_set_spin_limit(limit: int = 0) -> None:
+    _check(library().attnres_debug_set_spin_limit(limit), "attnres_debug_set_spin_limit")
+
+
+def attnres_debug_reset_scratch() -> None:
+    _check(library().attnres_debug_reset_scratch(), "attnres_debug_reset_scratch")
 
 
 def attnres_selftest_rounding() -> int:

@@ -1216,6 +1216,7 @@ constexpr int MAX_DEVICES = 64;
 std::mutex g_mutex;
 Scratch g_scratch[MAX_DEVICES];
 int g_force_variant = 0;
+unsigned g_spin_limit = SPIN_LIMIT;
 int g_force_param = 0;
 
 constexpr size_t REC1_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS * REC_STRIDE;
@@ -1287,7 +1288,7 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.nvec = (int)(H / 8);
     p.chunks = pl.chunks;
     p.M = M;
-    p.spin_limit = SPIN_LIMIT;
+    p.spin_limit = g_spin_limit;
 
     const int a2 = add2 ? 1 : 0;
     if (n_snapshots > MAX_SNAP && pl.variant == 1) {
@@ -1416,6 +1417,23 @@ extern "C" int attnres_debug_timeouts(unsigned* out)
     if (rc != ATTNRES_OK)
         return rc;
     if (hipMemcpy(out, sc->timeouts, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+        return ATTNRES_EHIP;
+    return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_set_spin_limit(unsigned limit)
+{
+    g_spin_limit = limit ? limit : SPIN_LIMIT;
+    return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_reset_scratch(void)
+{
+    Scratch* sc = nullptr;
+    const int rc = scratch_for_current_device(&sc);
+    if (rc != ATTNRES_OK)
+        return rc;
+    if (hipMemset(sc->base, 0, SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return ATTNRES_EHIP;
     return ATTNRES_OK;
 }

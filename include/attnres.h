@@ -191,6 +191,27 @@ int attnres_set_variant(int variant, int param);
 int attnres_debug_timeouts(unsigned* out);
 
 /*
+ * attnres_debug_set_spin_limit -- diagnostic, for tests of the bounded waits:
+ * every later split-hidden launch (process-wide) gives up a wait at a
+ * per-token barrier after `limit` re-polls instead of the default (limit = 0
+ * restores the default, about 2^20).  A wait that gives up counts a timeout
+ * (attnres_debug_timeouts) and the call's results are then unspecified; the
+ * kernel still finishes.  Records a timed-out call leaves behind can match a
+ * later call's tags, so clear them with attnres_debug_reset_scratch before
+ * trusting results again.  Not thread-safe with concurrent calls.  Returns
+ * ATTNRES_OK.
+ */
+int attnres_debug_set_spin_limit(unsigned limit);
+
+/*
+ * attnres_debug_reset_scratch -- diagnostic: clears the split-hidden scratch of
+ * the current device (records, epoch words, timeout counter) synchronously,
+ * allocating it first if needed.  No call may be in flight on the device.
+ * Not for use during HIP-graph capture.  Returns ATTNRES_OK or ATTNRES_EHIP.
+ */
+int attnres_debug_reset_scratch(void);
+
+/*
  * attnres_selftest_rounding -- diagnostic: checks on the current device that
  * the packed binary32 -> bf16 conversion the kernels use rounds every one of
  * the 2^32 binary32 inputs to nearest even exactly as rounding by definition

@@ -499,6 +499,39 @@ def test_no_barrier_timeouts(ar):
     assert ar.attnres_debug_timeouts() == 0
 
 
+def test_bounded_waits_give_up(ar, orc):
+    """The split kernel's waits at its per-token barriers are bounded.  With
+    the spin limit forced down to one re-poll from the host, calls of both
+    exchange forms still finish and the waits that give up are counted (the
+    results of those calls are unspecified and not checked); once the scratch
+    is cleared and the limit restored, a call is exact again."""
+    import torch
+
+    two = case_for("cfg4", lambda: W.config_case("cfg4"))  # two exchanges
+    one = case_for("cfg2", lambda: W.config_case("cfg2"))  # the Gram form's one
+    ar.attnres_set_variant(2, 1)
+    try:
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_debug_set_spin_limit(1)
+        for _ in range(10):
+            P.run_gpu(two)
+            P.run_gpu(one)
+        torch.cuda.synchronize()
+        forced = ar.attnres_debug_timeouts()
+    finally:
+        ar.attnres_debug_set_spin_limit(0)
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_set_variant(0, 0)
+    say("forced timeouts", forced)
+    assert forced > 0
+    assert ar.attnres_debug_timeouts() == 0
+    for case in (two, one):
+        gp, gn = P.run_gpu(case)
+        rp, rn = P.run_oracle(orc, case)
+        P.assert_parity(gp, gn, rp, rn, "after the reset")
+    assert ar.attnres_debug_timeouts() == 0
+
+
 # --- the standalone add ----------------------------------------------------------
 
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536, 65536 * 3 + 5])
