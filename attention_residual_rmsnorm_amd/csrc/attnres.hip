@@ -26,7 +26,7 @@
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
 //      chunk's share of sum x^2 are exchanged through tagged 64-bit records
-//      with relaxed device-scope atomics (no fences); with at most seven
+//      with relaxed device-scope atomics (no fences); with at most eight
 //      sources the chunk's Gram matrix travels instead and one exchange gives
 //      both.  Spreads a few tokens over many CUs, which is what the
 //      latency-bound small-M calls need.

@@ -170,17 +170,17 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     }
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
-    //  * 2 <= N <= 6, M <= 32: 2-wave chunks, whose Gram form needs one
+    //  * 2 <= N <= 7, M <= 32: 2-wave chunks, whose Gram form needs one
     //    exchange (M = 1, N = 4: 4.94 against 5.61 us with two; M = 8, N = 2:
-    //    4.97 against 5.23 for one workgroup per token);
-    //  * N <= 1 at every M, and N <= 6 above 32 tokens: one workgroup per
+    //    4.97 against 5.23 for one workgroup per token; M = 1, N = 7: 5.45
+    //    against 5.87);
+    //  * N <= 1 at every M, and N <= 7 above 32 tokens: one workgroup per
     //    token (at N = 1 the split wins with add2 and loses without it, M = 1:
     //    4.21 against 4.64 us and 4.37 against 4.30; the dispatch may not
     //    depend on add2, and the named single-token call has none);
-    //  * N >= 7, the call latency-bound: one token takes 2-wave chunks (their
+    //  * N >= 8, the call latency-bound: one token takes 2-wave chunks (their
     //    exchanges have half as many partners), 2..16 tokens 1-wave chunks
-    //    (spread over the most CUs), up to 24 tokens (N = 7: 32) 2-wave
-    //    chunks;
+    //    (spread over the most CUs), up to 24 tokens 2-wave chunks;
     //  * N >= 8 up to 64 tokens: 4-wave chunks, or 2-wave chunks above 12
     //    sources (only that family holds them);
     //  * otherwise one workgroup per token.
@@ -205,7 +205,7 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         if (!many && M >= 2 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
         const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_2WAVE_TOKENS) ||
-                           (n >= 5 && n < 8 && M <= SPLIT_SMALL_TOKENS_WIDE) || (many && M <= SPLIT_MID_TOKENS);
+                           (many && M <= SPLIT_MID_TOKENS);
         if (small && split_ok && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
         if (n >= 8 && !many && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))

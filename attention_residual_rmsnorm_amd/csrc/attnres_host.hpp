@@ -14,10 +14,11 @@ constexpr int MAX_SPLIT_SNAP = 31;       // split hidden, 1-2 waves per workgrou
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-// automatic dispatch (see make_plan), N >= 3: 1-wave split for 2 to
-// SPLIT_SMALL_TOKENS tokens (2-wave for one token); 2-wave split up to
-// SPLIT_2WAVE_TOKENS (N >= 5) or SPLIT_SMALL_TOKENS_WIDE (5 <= N < 8); 4-wave
-// split up to SPLIT_MID_TOKENS (N >= 8)
+// automatic dispatch (see make_plan) at H >= 7168: 2-wave split with one
+// exchange up to SPLIT_SMALL_TOKENS_WIDE tokens for 2 <= N < GRAM_MAX_SOURCES;
+// for more sources a 1-wave split for 2 to SPLIT_SMALL_TOKENS tokens (2-wave
+// for one token), 2-wave up to SPLIT_2WAVE_TOKENS, 4-wave up to
+// SPLIT_MID_TOKENS
 constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_2WAVE_TOKENS = 24;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
@@ -26,7 +27,7 @@ constexpr int SPLIT_MID_TOKENS = 64;
 // GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).  With it, 2-wave
 // chunks win for 2 <= N <= GRAM_MAX_SOURCES - 1 up to SPLIT_SMALL_TOKENS_WIDE
 // tokens (rows of LONG_ROW_VECTORS and more).
-constexpr int GRAM_MAX_SOURCES = 7;
+constexpr int GRAM_MAX_SOURCES = 8;
 // Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one
 // workgroup per token at every M and N <= 12; rows shorter than
 // LONG_ROW_VECTORS (H < 7168) are split only with N >= MID_SPLIT_MIN_SNAP and

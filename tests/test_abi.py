@@ -162,11 +162,14 @@ def test_bf16_add_validation():
 def test_plan_is_pure_and_sane():
     # the measured automatic dispatch at H = 7168
     assert ar.attnres_plan(1, 12, 7168) == (2, 7, 128)     # one token: 2-wave chunks
-    assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # N <= 6, M <= 32: 2-wave chunks (one exchange)
+    assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # N <= 7, M <= 32: 2-wave chunks (one exchange)
     assert ar.attnres_plan(16, 4, 7168) == (2, 7, 128)
     assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)
     assert ar.attnres_plan(33, 6, 7168)[0] == 1
-    assert ar.attnres_plan(2, 7, 7168) == (2, 14, 64)      # N >= 7, 2..16 tokens: 1-wave chunks
+    assert ar.attnres_plan(2, 7, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(32, 7, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(33, 7, 7168)[0] == 1
+    assert ar.attnres_plan(2, 8, 7168) == (2, 14, 64)      # N >= 8, 2..16 tokens: 1-wave chunks
     assert ar.attnres_plan(8, 12, 7168) == (2, 14, 64)
     assert ar.attnres_plan(24, 12, 7168) == (2, 7, 128)
     assert ar.attnres_plan(32, 5, 7168) == (2, 7, 128)

@@ -224,7 +224,7 @@ def _cancelling_case(N, noise=1e-3, M=3, H=7168, seed=5):
 @pytest.mark.parametrize("variant", [(0, 0), (2, 1), (2, 2), (2, 7)], ids=["auto", "S1w", "S2w", "S7w"],
                          indirect=True)
 @pytest.mark.parametrize("noise", [1e-3, 0.15, 0.3, 0.6])
-@pytest.mark.parametrize("N", [1, 3, 4, 6])
+@pytest.mark.parametrize("N", [1, 3, 4, 7])
 def test_cancelling_sources(ar, orc, variant, N, noise):
     """Sources that nearly cancel.  The split kernel takes sum x^2 = alpha' G
     alpha from its one exchange for few sources.  With noise 1e-3 that form
@@ -268,10 +268,10 @@ def test_shapes(ar, orc, variant, M, H, N):
 @pytest.mark.parametrize("M", [2, 16, 17, 24, 25, 32, 33, 64, 65])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
-    (2-wave chunks with one exchange up to 32 tokens for 2 <= N <= 6; 1-wave chunks
+    (2-wave chunks with one exchange up to 32 tokens for 2 <= N <= 7; 1-wave chunks
     up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64, then a workgroup
     per token) and source-count bounds (the split kernel's single-exchange form
-    up to six snapshots; one group of up to four sources in kernel W; the store
+    up to seven snapshots; one group of up to four sources in kernel W; the store
     policy changes at nine sources)."""
     case = case_for(("bound", M, N), lambda: W.make_case(cfg=62, M=M, N=N, add2=(M % 2 == 0)))
     say("boundary", M, N, ar.attnres_plan(M, N, case.H))
