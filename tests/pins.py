@@ -273,6 +273,166 @@ def check_two_source_closed_form(orc):
     assert_close(y[0], want, 1e-14, 0, "closed-form y")
 
 
+def check_two_source_eps_closed_form(orc):
+    """The same two sources with eps = 1 and a gamma that is not 1 at the
+    query's only nonzero column.  The key RMSNorm takes eps inside its square
+    root: the snapshot of ones (mean square 1) gets the logit
+    (1/2)/sqrt(1 + 1), the prefix [2,0,2,0,...] (mean square 2) gets
+    1/sqrt(2 + 1); the query enters the logits as it is (gamma belongs to the
+    final RMSNorm only).  The mixture is a0 + 2 a1 at even columns and a0 at
+    odd ones (a1 the prefix weight, a0 = 1 - a1), its mean square
+    ((a0 + 2 a1)^2 + a0^2)/2, and y = x / sqrt(that + 1) * gamma."""
+    H = 8
+    ones = np.full((1, H), 0x3F80, np.uint16)
+    prefix = np.array([[0x4000, 0x0000] * 4], np.uint16)
+    add = np.zeros((1, H), np.uint16)
+    q = np.zeros(H, np.uint16)
+    q[0] = 0x3F00  # 0.5
+    gamma = np.array([0x4000, 0x3F00, 0x3FC0, 0x3E80, 0x3F80, 0x4040, 0x3F40, 0x3FA0], np.uint16)
+    eps = 1.0
+    _, _, y, alpha = orc.fwd(prefix, add, None, [ones], q, gamma, eps, want_f64=True, want_alpha=True)
+    z0 = 0.5 / math.sqrt(1.0 + eps)
+    z1 = 1.0 / math.sqrt(2.0 + eps)
+    a1 = 1.0 / (1.0 + math.exp(z0 - z1))
+    a0 = 1.0 - a1
+    assert_close(alpha[0], [a0, a1], 1e-14, 0, "eps closed-form alpha")
+    x = np.array([a0 + 2 * a1, a0] * 4)
+    ms = ((a0 + 2 * a1) ** 2 + a0 ** 2) / 2
+    want = x / math.sqrt(ms + eps) * f64(gamma)
+    assert_close(y[0], want, 1e-14, 0, "eps closed-form y")
+
+
+# exact evaluation at tiny H (rationals, then 60 significant digits) ---------
+
+def _round_frac(x: Fraction, p: int, emin: int) -> Fraction:
+    """x rounded to the nearest floating-point value with p significand bits
+    (implicit bit included) and minimum normal exponent emin, ties to even,
+    gradual underflow.  (No overflow: the tiny-H cases stay far from it.)"""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:  # bring a into [2^E, 2^(E+1))
+        E -= 1
+    E = max(E, emin)
+    quantum = Fraction(2) ** (E - (p - 1))
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * quantum
+
+
+def _bf16_frac(bits) -> list:
+    return [Fraction(float(v)) for v in W.bf16_bits_to_f32(np.asarray(bits, np.uint16)).ravel()]
+
+
+def _frac_to_bf16_bits(v: Fraction) -> int:
+    """A Fraction that is a bf16 value -> its bit pattern (exact)."""
+    return int(W.to_bf16_bits(np.array([float(v)]))[0])
+
+
+def exact_attnres(prefix, add, add2, snapshots, query, gamma, eps):
+    """The operation on one token, evaluated from its definition without
+    binary64: the fold-add in exact rationals rounded to binary32 and then to
+    bf16 at each addition (round to nearest even, gradual underflow); the key
+    RMSNorm, the logits, the softmax, the mixture and the final RMSNorm in
+    exact rationals where they are rational and otherwise in 60-digit decimal
+    arithmetic (square roots and exponentials correctly rounded at that
+    precision).  Returns (out_prefix bits, y, alpha, x): y (the normalised
+    output), alpha (the weights) and x (the pre-norm mixture) as lists of
+    Decimal."""
+    from decimal import Decimal, localcontext
+
+    H = len(prefix)
+    p, a = _bf16_frac(prefix), _bf16_frac(add)
+    a2 = None if add2 is None else _bf16_frac(add2)
+    q, g = _bf16_frac(query), _bf16_frac(gamma)
+    e = Fraction(float(np.float32(eps)))
+    f32 = lambda v: _round_frac(v, 24, -126)
+    b16 = lambda v: _round_frac(v, 8, -126)
+    pp = []
+    for h in range(H):
+        t = a[h] if a2 is None else b16(f32(a[h] + a2[h]))
+        pp.append(b16(f32(p[h] + t)))
+    sources = [_bf16_frac(s) for s in snapshots] + [pp]
+    with localcontext() as ctx:
+        ctx.prec = 60
+        D = lambda fr: Decimal(fr.numerator) / Decimal(fr.denominator)
+        z = []
+        for k in sources:
+            ms = sum(v * v for v in k) / H + e
+            qk = sum(qh * v for qh, v in zip(q, k))
+            z.append(D(qk) / D(ms).sqrt())
+        zmax = max(z)
+        ex = [(zs - zmax).exp() for zs in z]
+        den = sum(ex)
+        alpha = [w / den for w in ex]
+        x = [sum(al * D(k[h]) for al, k in zip(alpha, sources)) for h in range(H)]
+        msx = sum(v * v for v in x) / H + D(e)
+        r = 1 / msx.sqrt()
+        y = [x[h] * r * D(g[h]) for h in range(H)]
+    return [_frac_to_bf16_bits(v) for v in pp], y, alpha, x
+
+
+def _tiny_h_cases(seed=41):
+    """Seeded one-token calls at H = 8, 16, 64: eps from 0 to 3, sources of
+    mean square 1e-4 .. 10 (so eps moves every logit and the final scale),
+    a query of logits O(1) on every column, gamma far from 1, with and without
+    the second addend, N from 0 to 12."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for H in (8, 16, 64):
+        for N, eps, add2 in ((0, 0.25, True), (1, 1e-3, False), (3, 0.25, True), (6, 3.0, True),
+                             (12, 1e-3, True), (4, 0.0, False), (2, 3.0, False)):
+            scale = lambda: 10.0 ** rng.uniform(-2.0, 0.5)
+            bf = lambda x: W.to_bf16_bits(np.asarray(x, np.float64))
+            s_p = scale()
+            prefix = bf(s_p * rng.standard_normal(H))
+            add = bf(0.5 * s_p * rng.standard_normal(H))
+            add2v = bf(0.5 * s_p * rng.standard_normal(H)) if add2 else None
+            snaps = [bf(scale() * rng.standard_normal(H)) for _ in range(N)]
+            query = bf(rng.standard_normal(H) * 2.0 / math.sqrt(H))
+            gamma = bf(1.0 + 0.4 * rng.standard_normal(H))
+            out.append((H, N, eps, prefix, add, add2v, snaps, query, gamma))
+    return out
+
+
+def check_exact_tiny_h(orc):
+    """The oracle's binary64 result against an exact evaluation of the same
+    definition (exact_attnres) on one-token calls at H = 8, 16 and 64:
+    out_prefix bit for bit, the weights and the unrounded out_norm to 1e-12
+    of the row's largest value (binary64 leaves about 1e-15; a changed term of
+    the key RMSNorm, the logits, the softmax or the final RMSNorm moves them
+    by far more), the same for the pre-norm mixture, and the bits of out_norm
+    and of the mixture output equal to the exact values rounded to nearest
+    even wherever those are not within 1e-12 of a tie."""
+    for H, N, eps, prefix, add, add2v, snaps, query, gamma in _tiny_h_cases():
+        what = "H=%d N=%d eps=%g" % (H, N, eps)
+        row = lambda v: None if v is None else v.reshape(1, H)
+        op, on, y, alpha, mix, mix64 = orc.fwd(row(prefix), row(add), row(add2v), [row(s) for s in snaps], query,
+                                               gamma, eps, want_f64=True, want_alpha=True, want_mix=True,
+                                               want_mix_f64=True)
+        xp, xy, xa, xx = exact_attnres(prefix, add, add2v, snaps, query, gamma, eps)
+        assert np.array_equal(op[0], np.array(xp, np.uint16)), what + ": out_prefix"
+        xa = np.array([float(v) for v in xa])
+        assert_close(alpha[0], xa, 0, 1e-12, what + ": alpha")
+        for name, got64, got16, exact in (("out_norm", y, on, xy), ("mixture", mix64, mix, xx)):
+            ex = np.array([float(v) for v in exact])
+            scale = np.max(np.abs(ex))
+            assert scale > 0.05 or name == "mixture", what + ": degenerate case"
+            assert_close(got64[0], ex, 0, 1e-12 * scale, "%s: %s before rounding" % (what, name))
+            for h in range(H):
+                want = _nearest_bf16_fraction(ex[h])
+                lo = _nearest_bf16_fraction(ex[h] * (1 - 1e-12))
+                hi = _nearest_bf16_fraction(ex[h] * (1 + 1e-12))
+                if lo == hi == want:
+                    assert got16[0, h] == want, "%s: %s[%d] %04x, exact rounds to %04x" % (
+                        what, name, h, got16[0, h], want)
+
+
 def check_token_permutation(orc):
     """Tokens are independent: permuting the rows of every [M,H] input
     permutes the outputs, bit for bit."""
@@ -391,6 +551,8 @@ QUICK = [
     check_identical_sources,
     check_mix_output,
     check_two_source_closed_form,
+    check_two_source_eps_closed_form,
+    check_exact_tiny_h,
     check_dominant_logit,
     check_token_permutation,
     check_snapshot_scale_invariance,

@@ -86,7 +86,34 @@ MUTANTS = {
     "snapshot_row_not_offset": (
         "            rows[s] = snapshots[s] + off;",
         "            rows[s] = snapshots[s];"),
+    # the key RMSNorm and the logits: eps, weight, temperature
+    "key_eps_dropped": (
+        "        double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n        z[s]",
+        "        double rstd = 1.0 / sqrt(sumsq / (double)H);\n        z[s]"),
+    "key_eps_outside_sqrt": (
+        "        double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n        z[s]",
+        "        double rstd = 1.0 / (sqrt(sumsq / (double)H) + eps);\n        z[s]"),
+    "query_times_gamma": (
+        "            qdot += oracle_bf16_to_f64(query[h]) * ks[h];",
+        "            qdot += oracle_bf16_to_f64(query[h]) * oracle_bf16_to_f64(gamma[h]) * ks[h];"),
+    "key_norm_weighted_by_gamma": (
+        "            sumsq += ks[h] * ks[h];",
+        "            sumsq += ks[h] * ks[h] * oracle_bf16_to_f64(gamma[h]) * oracle_bf16_to_f64(gamma[h]);"),
+    "logit_temperature": (
+        "        z[s] = rstd * qdot;",
+        "        z[s] = rstd * qdot / sqrt((double)H);"),
+    "final_eps_dropped": (
+        "    double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n    for",
+        "    double rstd = 1.0 / sqrt(sumsq / (double)H);\n    for"),
+    "final_norm_sum_not_mean": (
+        "    double rstd = 1.0 / sqrt(sumsq / (double)H + eps);\n    for",
+        "    double rstd = 1.0 / sqrt(sumsq + eps);\n    for"),
 }
+
+# A pin that compares the oracle with itself at a tolerance (the output under a
+# permutation of the snapshots) may fail for a mutant by accident, on a
+# near-zero element; it does not count as catching one.
+NOT_A_PIN = {"check_snapshot_permutation"}
 
 
 @pytest.fixture(scope="module")
@@ -105,9 +132,33 @@ def test_mutant_is_caught(name, mutant_dir):
     orc = oracle.Oracle(lib)
     caught = []
     for check in pins.QUICK + [pins.check_round_vs_fractions]:
+        if check.__name__ in NOT_A_PIN:
+            continue
         try:
             check(orc)
         except (AssertionError, RuntimeError, FloatingPointError) as exc:
             caught.append((check.__name__, str(exc)[:200]))
             break
     assert caught, "mutant %s passed every pin" % name
+    print("mutant", name, "caught by", caught[0][0])
+
+
+# Mistakes in the mixing formula, the key RMSNorm, the softmax, the final
+# RMSNorm or the mixture output: the exact tiny-H evaluation alone (rational and
+# 60-digit arithmetic, no binary64) must catch each of them.
+EXACT_ALONE = sorted(n for n in MUTANTS if n not in (
+    "denormals_are_zero", "flush_to_zero",  # no subnormal sums in its cases: the golden examples pin these
+    "no_max_subtraction",                    # logits O(1) there: the dominant-logit pin pins this
+    "snapshot_row_not_offset",               # one token per call there: the permutation pins pin this
+))
+
+
+@pytest.mark.parametrize("name", EXACT_ALONE)
+def test_exact_tiny_h_alone(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = os.path.join(str(mutant_dir), "exact_" + name + ".c")
+    with open(src, "w") as fh:
+        fh.write(SRC.replace(old, new))
+    lib = obuild.build(source=src, output=os.path.join(str(mutant_dir), "libexact_%s.so" % name))
+    with pytest.raises(AssertionError):
+        pins.check_exact_tiny_h(oracle.Oracle(lib))
