@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     ATTNRES_EALIAS,
     ATTNRES_EHIP,
     ATTNRES_EINVAL,
+    ATTNRES_ENOINIT,
     ATTNRES_EUNSUPPORTED,
     ATTNRES_MAX_HIDDEN,
     ATTNRES_MAX_SNAPSHOTS,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     attnres_debug_timeouts,
     attnres_debug_set_spin_limit,
     attnres_debug_reset_scratch,
+    attnres_debug_set_epoch,
     attnres_init,
     attnres_plan,
     attnres_selftest_rounding,

@@ -10,6 +10,7 @@ ATTNRES_EINVAL = -1
 ATTNRES_EUNSUPPORTED = -2
 ATTNRES_EALIAS = -3
 ATTNRES_EHIP = -4
+ATTNRES_ENOINIT = -5
 ATTNRES_MAX_SNAPSHOTS = 64
 ATTNRES_MAX_HIDDEN = 16384
 
@@ -66,6 +67,8 @@ def library():
         lib.attnres_debug_set_spin_limit.restype = ctypes.c_int
         lib.attnres_debug_reset_scratch.argtypes = []
         lib.attnres_debug_reset_scratch.restype = ctypes.c_int
+        lib.attnres_debug_set_epoch.argtypes = [ctypes.c_uint]
+        lib.attnres_debug_set_epoch.restype = ctypes.c_int
         lib.attnres_selftest_rounding.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
         lib.attnres_selftest_rounding.restype = ctypes.c_int
         lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -79,6 +82,22 @@ def library():
 def _check(rc: int, where: str) -> None:
     if rc != ATTNRES_OK:
         raise AttnResError(rc, where)
+
+
+_initialised = set()
+
+
+def _ensure_init() -> None:
+    """attnres_init() on the current device before the binding's first fused
+    call there (the library requires it; it allocates the device's scratch
+    and synchronises, once).  Callers that must not allocate at that point
+    (HIP-graph capture) call attnres_init() themselves beforehand."""
+    import torch
+
+    dev = torch.cuda.current_device()
+    if dev not in _initialised:
+        _check(library().attnres_init(), "attnres_init")
+        _initialised.add(dev)
 
 
 def _ptr(t) -> Optional[int]:
@@ -147,6 +166,7 @@ def attnres_add_rmsnorm_fwd(prefix, add, add2, snapshots: Sequence, query, gamma
     """
     M, H, n, arr, out_prefix, out_norm = _fwd_args(prefix, add, add2, snapshots, query, gamma,
                                                    out_prefix, out_norm)
+    _ensure_init()
     rc = library().attnres_add_rmsnorm_fwd(
         _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
         ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _stream(stream))
@@ -165,6 +185,7 @@ def attnres_add_rmsnorm_mix_fwd(prefix, add, add2, snapshots: Sequence, query, g
     if out_mix is None:
         out_mix = torch.empty_like(prefix)
     _check_tensor("out_mix", out_mix, (M, H))
+    _ensure_init()
     rc = library().attnres_add_rmsnorm_mix_fwd(
         _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
         ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _ptr(out_mix), _stream(stream))
@@ -187,7 +208,11 @@ def attnres_bf16_add(a, b, out=None, stream=None):
 
 
 def attnres_init() -> None:
+    """Allocate the current device's scratch (synchronously; once per device)."""
+    import torch
+
     _check(library().attnres_init(), "attnres_init")
+    _initialised.add(torch.cuda.current_device())
 
 
 def attnres_plan(M: int, n_snapshots: int, H: int):
@@ -214,6 +239,10 @@ def attnres_debug_set_spin_limit(limit: int = 0) -> None:
 
 def attnres_debug_reset_scratch() -> None:
     _check(library().attnres_debug_reset_scratch(), "attnres_debug_reset_scratch")
+
+
+def attnres_debug_set_epoch(epoch: int) -> None:
+    _check(library().attnres_debug_set_epoch(epoch), "attnres_debug_set_epoch")
 
 
 def attnres_selftest_rounding() -> int:

@@ -41,6 +41,7 @@
 
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -854,6 +855,44 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 }
 
 // ---------------------------------------------------------------------------
+// The split kernel's per-token epoch.  Epochs run through [0, EPOCH_PERIOD)
+// and wrap to 0, so the tags 2E+1 and 2E+2 are never 0, the tag of a record
+// that was never written (or was cleared).  A record from an earlier call
+// could match a later call's tag only if exactly a multiple of EPOCH_PERIOD
+// calls lay between the two; any such record sits at a chunk index the calls
+// in between did not use (each call rewrites the records of the chunks it
+// uses), and the call that wraps the epoch clears every record at chunk
+// indices it does not use.  The clearing runs in chunk 0 after every chunk of
+// its call has read the records it needs, and no chunk of this call reads
+// those indices; the next call on the token slot starts after this kernel
+// ends (calls on one device's scratch are ordered).
+constexpr unsigned EPOCH_PERIOD = 0x7fffffffu;
+
+__device__ __forceinline__ unsigned long long gave_up(unsigned tag)
+{
+    return ((unsigned long long)tag << 32) | 0x7fc00000u; // the tag, and a quiet NaN
+}
+
+__device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t t, int C)
+{
+    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
+    unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
+    for (int c = C; c < MAX_CHUNKS; ++c) {
+        for (int v = 0; v < REC_STRIDE; ++v)
+            __hip_atomic_store(&rec1[c * REC_STRIDE + v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&rec2[c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, unsigned epoch, int64_t t, int C)
+{
+    const unsigned next = epoch + 1u >= EPOCH_PERIOD ? 0u : epoch + 1u;
+    if (next == 0u)
+        clear_unused_chunks(p, t, C);
+    __hip_atomic_store(state, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel S: split hidden.  blockDim.x threads per workgroup, one 16-byte vector
 // each; C = p.chunks workgroups per token, chunk c owning vectors
 // [c*blockDim.x, (c+1)*blockDim.x).  Workgroup b serves token (b/8/C)*8 + b%8,
@@ -863,10 +902,14 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 //
 // Exchanges (see attnres_device.hpp): the call's epoch E is read from the
 // token's state word at the start; the A2 partials travel with tag 2E+1, the
-// chunk sums of x^2 with tag 2E+2.  Chunk 0 advances the state word to E+1
-// after it has seen every chunk's last record, i.e. after every workgroup of
-// the token has read E, so all workgroups of one call agree on E, and every
-// call (HIP-graph replays included) uses new tags.
+// chunk sums of x^2 with tag 2E+2.  Chunk 0 advances the state word (to E+1,
+// or to 0 at the end of the period, see advance_epoch) after it has seen
+// every chunk's last record, i.e. after every workgroup of the token has read
+// E, so all workgroups of one call agree on E, and every call (HIP-graph
+// replays included) uses new tags.  Every wait is bounded (Params::spin_limit
+// re-polls); a wait that gives up counts a timeout and takes NaN for each
+// missing value, so the outputs that depend on it are NaN, never silently
+// wrong (out_prefix does not depend on any exchange).
 //
 // Gram form (S <= GRAM_MAX_SOURCES): the first exchange carries q.k_s and the
 // chunk's Gram entries k_s.k_t (s <= t) instead of q.k_s and sum k_s^2.  The
@@ -992,7 +1035,13 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
                 if (ready)
                     break;
                 if (polls >= p.spin_limit) {
+                    // give up: a record still missing counts as NaN, so the weights, every
+                    // output of this wave and every sum of x^2 it publishes are NaN
                     atomicAdd(p.timeouts, 1u);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (tag_of(r0[j]) != tag1)
+                            r0[j] = gave_up(tag1);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -1081,7 +1130,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
         // chunk's first record, so every workgroup of the token has read E.
         ssum = gram_ssum;
         if (chunk == 0 && tid == 0)
-            __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            advance_epoch(p, state, epoch, t, C);
     } else {
         if (lane == 0)
             red2[wave] = sx;
@@ -1101,7 +1150,8 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
             for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
                 if (polls >= p.spin_limit) {
-                    atomicAdd(p.timeouts, 1u);
+                    atomicAdd(p.timeouts, 1u); // give up: the sum, hence this wave's outputs, is NaN
+                    w2 = gave_up(tag2);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -1109,7 +1159,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             }
             ssum = wave_sum(__uint_as_float((unsigned)w2));
             if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
-                __hip_atomic_store(state, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                advance_epoch(p, state, epoch, t, C);
             if (!PERWAVE && lane == 0)
                 ssum_sh = ssum;
         }
@@ -1213,8 +1263,9 @@ struct Scratch {
 };
 
 constexpr int MAX_DEVICES = 64;
-std::mutex g_mutex;
-Scratch g_scratch[MAX_DEVICES];
+std::mutex g_mutex;                          // serialises attnres_init
+Scratch g_scratch[MAX_DEVICES];              // written once per device, under g_mutex
+std::atomic<bool> g_ready[MAX_DEVICES];      // published after g_scratch[dev] is complete
 int g_force_variant = 0;
 unsigned g_spin_limit = SPIN_LIMIT;
 int g_force_param = 0;
@@ -1224,30 +1275,52 @@ constexpr size_t REC2_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MA
 constexpr size_t STATE_BYTES = sizeof(unsigned) * MAX_SPLIT_TOKENS * STATE_STRIDE;
 constexpr size_t SCRATCH_BYTES = REC1_BYTES + REC2_BYTES + STATE_BYTES + 256;
 
-// The scratch of the current device, allocated and cleared on first use.
+int current_device(int* dev)
+{
+    if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= MAX_DEVICES)
+        return ATTNRES_EHIP;
+    return ATTNRES_OK;
+}
+
+// Allocates and clears the scratch of the current device (once; attnres_init).
+int init_scratch()
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != ATTNRES_OK)
+        return rc;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_ready[dev].load(std::memory_order_acquire))
+        return ATTNRES_OK;
+    void* base = nullptr;
+    if (hipMalloc(&base, SCRATCH_BYTES) != hipSuccess)
+        return ATTNRES_EHIP;
+    if (hipMemset(base, 0, SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(base);
+        return ATTNRES_EHIP;
+    }
+    Scratch& s = g_scratch[dev];
+    char* c = static_cast<char*>(base);
+    s.rec1 = reinterpret_cast<unsigned long long*>(c);
+    s.rec2 = reinterpret_cast<unsigned long long*>(c + REC1_BYTES);
+    s.state = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES);
+    s.timeouts = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES + STATE_BYTES);
+    s.base = base;
+    g_ready[dev].store(true, std::memory_order_release);
+    return ATTNRES_OK;
+}
+
+// The scratch of the current device, or ATTNRES_ENOINIT when attnres_init has
+// not run there.  Never allocates, never synchronises.
 int scratch_for_current_device(Scratch** out)
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
-        return ATTNRES_EHIP;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    Scratch& s = g_scratch[dev];
-    if (!s.base) {
-        void* base = nullptr;
-        if (hipMalloc(&base, SCRATCH_BYTES) != hipSuccess)
-            return ATTNRES_EHIP;
-        if (hipMemset(base, 0, SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-            (void)hipFree(base);
-            return ATTNRES_EHIP;
-        }
-        char* c = static_cast<char*>(base);
-        s.rec1 = reinterpret_cast<unsigned long long*>(c);
-        s.rec2 = reinterpret_cast<unsigned long long*>(c + REC1_BYTES);
-        s.state = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES);
-        s.timeouts = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES + STATE_BYTES);
-        s.base = base;
-    }
-    *out = &s;
+    int rc = current_device(&dev);
+    if (rc != ATTNRES_OK)
+        return rc;
+    if (!g_ready[dev].load(std::memory_order_acquire))
+        return ATTNRES_ENOINIT;
+    *out = &g_scratch[dev];
     return ATTNRES_OK;
 }
 
@@ -1271,6 +1344,12 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
         return rc;
     if (M == 0)
         return ATTNRES_OK;
+    // every fused call needs attnres_init on its device (whichever kernel the
+    // plan picks, so that the rule does not depend on the sizes)
+    Scratch* sc = nullptr;
+    rc = scratch_for_current_device(&sc);
+    if (rc != ATTNRES_OK)
+        return rc;
 
     Params p{};
     p.prefix = static_cast<const uint4*>(prefix);
@@ -1310,10 +1389,6 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     }
     Kernel fn = nullptr;
     if (pl.variant == 2) {
-        Scratch* sc = nullptr;
-        rc = scratch_for_current_device(&sc);
-        if (rc != ATTNRES_OK)
-            return rc;
         p.rec1 = sc->rec1;
         p.rec2 = sc->rec2;
         p.state = sc->state;
@@ -1374,11 +1449,7 @@ extern "C" int attnres_bf16_add(const void* a, const void* b, void* out, int64_t
     return ATTNRES_OK;
 }
 
-extern "C" int attnres_init(void)
-{
-    Scratch* sc = nullptr;
-    return scratch_for_current_device(&sc);
-}
+extern "C" int attnres_init(void) { return init_scratch(); }
 
 extern "C" int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunks,
                             int* threads)
@@ -1433,7 +1504,28 @@ extern "C" int attnres_debug_reset_scratch(void)
     const int rc = scratch_for_current_device(&sc);
     if (rc != ATTNRES_OK)
         return rc;
-    if (hipMemset(sc->base, 0, SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    if (hipDeviceSynchronize() != hipSuccess || hipMemset(sc->base, 0, SCRATCH_BYTES) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+        return ATTNRES_EHIP;
+    return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_set_epoch(unsigned epoch)
+{
+    if (epoch >= EPOCH_PERIOD)
+        return ATTNRES_EINVAL;
+    Scratch* sc = nullptr;
+    const int rc = scratch_for_current_device(&sc);
+    if (rc != ATTNRES_OK)
+        return rc;
+    static unsigned words[MAX_SPLIT_TOKENS * STATE_STRIDE];
+    std::lock_guard<std::mutex> lock(g_mutex);
+    for (int t = 0; t < MAX_SPLIT_TOKENS; ++t)
+        for (int i = 0; i < STATE_STRIDE; ++i)
+            words[t * STATE_STRIDE + i] = i == 0 ? epoch : 0u;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(sc->state, words, sizeof(words), hipMemcpyHostToDevice) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
         return ATTNRES_EHIP;
     return ATTNRES_OK;
 }
@@ -1443,11 +1535,12 @@ extern "C" const char* attnres_status_string(int status)
     switch (status) {
     case ATTNRES_OK: return "ok";
     case ATTNRES_EINVAL: return "invalid argument";
-    case ATTNRES_EUNSUPPORTED: return "unsupported (more than 12 snapshots): add first, use the unfused route";
+    case ATTNRES_EUNSUPPORTED: return "unsupported (more than 64 snapshots): add first, use the unfused route";
     case ATTNRES_EALIAS: return "forbidden buffer overlap";
     case ATTNRES_EHIP: return "HIP error";
+    case ATTNRES_ENOINIT: return "attnres_init() has not run on the current device";
     default: return "unknown status";
     }
 }
 
-extern "C" int attnres_version(void) { return 101; }
+extern "C" int attnres_version(void) { return 20000; }

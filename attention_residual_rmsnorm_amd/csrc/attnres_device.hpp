@@ -137,11 +137,10 @@ __device__ __forceinline__ float wave_max(float v)
 // sees the expected tag also sees that call's value: no fence (and none of the
 // whole-cache writeback/invalidate that device-scope release/acquire costs on
 // gfx950) is needed.  Tags come from a per-token epoch word that advances once
-// per call (see fwd_split), so records left by earlier calls never match.
-// (The 32-bit tags repeat after 2^31 calls on one token slot.  Every call
-// rewrites the records of every chunk it uses, so an old record could match
-// only if a chunk index went unused for exactly that many calls and a later
-// call with more chunks then read it; this is not guarded against.)
+// per call (see fwd_split), so records left by earlier calls never match: tag
+// 0 (a record never written) is never expected, and the call that wraps the
+// epoch clears the records of every chunk index it does not use (see
+// advance_epoch).
 
 __device__ __forceinline__ void publish(unsigned long long* rec, unsigned tag, float v)
 {

@@ -766,8 +766,12 @@ def main():
     after_timing = verify_instances(dc, gate_idx, gate_ref)
     log("after timing: %s" % after_timing)
 
-    # the fused kernel's average launch duration over the timed region (the
-    # replayed graph holds nothing but the step's fused launches)
+    # the fused kernel's average launch duration over the timed region: HIP
+    # events around the replays on the launch stream, divided by the launches
+    # (the replayed graph holds nothing but the step's fused launches, back to
+    # back, so this is wall time per launch, gaps between launches included;
+    # rocprofv3's kernel trace of the same command gives the per-dispatch
+    # durations it is checked against)
     launches = dc.launches_per_step()
     per_launch_bytes = nbytes / launches
     avg_kernel = sec / launches
@@ -790,7 +794,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "attnres fused fwd, variant %s (%d threads/workgroup)" % (
                     "W" if plan[0] == 1 else "S", plan[2]),
-                "avg_kernel_us": round(avg_kernel * 1e6, 3),
+                "wall_us_per_launch": round(avg_kernel * 1e6, 3),
                 "algorithmic_bytes_per_launch": round(per_launch_bytes),
                 "n12_layer": {"kernel_us": round(t12 * 1e6, 3), "GBps": round(b12 / t12 / 1e9, 1),
                               "frac": round(b12 / t12 / 1e9 / HBM_PEAK_GBS, 4)},

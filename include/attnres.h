@@ -33,9 +33,12 @@
  * give the same bits, and the dispatch never depends on whether add2 is given,
  * so add2 = s yields the same bits as add = bf16(add + s), add2 = NULL.
  *
- * Execution: stream-ordered and asynchronous; no host synchronisation and no
- * printing.  Every argument is validated before any HIP call; an invalid call
- * launches nothing.
+ * Execution: stream-ordered and asynchronous.  The fused calls allocate
+ * nothing, never synchronise with the host and print nothing; they may be
+ * captured into a HIP graph.  The library's per-device scratch is allocated
+ * (synchronously) by attnres_init(), which must run once on a device before
+ * the first fused call there.  Every argument is validated before any HIP
+ * call; an invalid call launches nothing.
  */
 #ifndef ATTNRES_H
 #define ATTNRES_H
@@ -63,6 +66,8 @@ extern "C" {
                                      buffer */
 #define ATTNRES_EHIP (-4)         /* a HIP call failed (launch error, no device,
                                      out of memory for the scratch) */
+#define ATTNRES_ENOINIT (-5)      /* a fused call on a device where attnres_init()
+                                     has not run: nothing was launched */
 
 #define ATTNRES_MAX_SNAPSHOTS 64 /* up to 12 (the page's fused window, section "Model")
                                     the sources are taken in one pass; 13..64 are fused
@@ -101,12 +106,17 @@ extern "C" {
  * All device pointers must be 16-byte aligned.  The caller owns every buffer
  * and must keep it alive until the stream work completes.  The library owns a
  * per-device scratch buffer used by the split-hidden kernel (tagged partial
- * records and one epoch word per token slot; nothing needs clearing between
- * calls, HIP-graph replays included); it is allocated on the first call that
- * needs it on a device, or by attnres_init().  Calls that use it on the same
- * device must be ordered with respect to each other (same stream, or
- * synchronised): two overlapping calls on different streams of one device
- * race on it.
+ * records and one epoch word per token slot, 8.6 MB; nothing needs clearing
+ * between calls, HIP-graph replays included).  attnres_init() allocates it;
+ * the call itself never allocates or synchronises, and returns
+ * ATTNRES_ENOINIT (launching nothing) on a device where attnres_init() has
+ * not run, whatever kernel the sizes would select.  Calls on the same device
+ * must be ordered with respect to each other (same stream, or synchronised):
+ * two overlapping calls on different streams of one device race on the
+ * scratch.  The split-hidden kernel's waits for the other workgroups of a
+ * token are bounded; a wait that gives up (which a correct run never does:
+ * see attnres_debug_timeouts) makes that token's out_norm (and out_mix)
+ * elements that depend on it NaN instead of wrong; out_prefix is unaffected.
  *
  * Returns ATTNRES_OK or one of the negative codes above.
  */
@@ -154,11 +164,11 @@ int attnres_bf16_add(const void* a, const void* b, void* out, int64_t n,
                      hipStream_t stream);
 
 /*
- * attnres_init -- allocate the split-hidden scratch on the current device and
- * clear its counters (synchronously).  Optional: the first fused call on a
- * device does it too.  Call it before capturing calls into a HIP graph, since
- * allocation is not allowed during capture.  Returns ATTNRES_OK or
- * ATTNRES_EHIP.
+ * attnres_init -- allocate and clear the split-hidden scratch on the current
+ * device (synchronously: hipMalloc, hipMemset, hipDeviceSynchronize).  Must
+ * run once on each device before the first fused call there (those calls
+ * return ATTNRES_ENOINIT otherwise); later calls return at once.  Not for use
+ * during HIP-graph capture.  Thread-safe.  Returns ATTNRES_OK or ATTNRES_EHIP.
  */
 int attnres_init(void);
 
@@ -186,7 +196,8 @@ int attnres_set_variant(int variant, int param);
  * attnres_debug_timeouts -- diagnostic: *out = number of times a split-hidden
  * workgroup gave up waiting at a per-token barrier on the current device since
  * the scratch was created (0 in a correct run).  Synchronous (copies one word
- * to the host).  Returns ATTNRES_OK, ATTNRES_EINVAL (out NULL) or ATTNRES_EHIP.
+ * to the host).  Returns ATTNRES_OK, ATTNRES_EINVAL (out NULL), ATTNRES_ENOINIT
+ * or ATTNRES_EHIP.
  */
 int attnres_debug_timeouts(unsigned* out);
 
@@ -195,21 +206,33 @@ int attnres_debug_timeouts(unsigned* out);
  * every later split-hidden launch (process-wide) gives up a wait at a
  * per-token barrier after `limit` re-polls instead of the default (limit = 0
  * restores the default, about 2^20).  A wait that gives up counts a timeout
- * (attnres_debug_timeouts) and the call's results are then unspecified; the
- * kernel still finishes.  Records a timed-out call leaves behind can match a
- * later call's tags, so clear them with attnres_debug_reset_scratch before
- * trusting results again.  Not thread-safe with concurrent calls.  Returns
- * ATTNRES_OK.
+ * (attnres_debug_timeouts) and takes NaN for every value it did not receive,
+ * so each out_norm / out_mix element of the call is then either correct or
+ * NaN; the kernel still finishes.  Records a timed-out call leaves behind can
+ * match a later call's tags, so clear them with attnres_debug_reset_scratch
+ * before trusting results again.  Not thread-safe with concurrent calls.
+ * Returns ATTNRES_OK.
  */
 int attnres_debug_set_spin_limit(unsigned limit);
 
 /*
  * attnres_debug_reset_scratch -- diagnostic: clears the split-hidden scratch of
- * the current device (records, epoch words, timeout counter) synchronously,
- * allocating it first if needed.  No call may be in flight on the device.
- * Not for use during HIP-graph capture.  Returns ATTNRES_OK or ATTNRES_EHIP.
+ * the current device (records, epoch words, timeout counter) synchronously.
+ * No call may be in flight on the device.  Not for use during HIP-graph
+ * capture.  Returns ATTNRES_OK, ATTNRES_ENOINIT or ATTNRES_EHIP.
  */
 int attnres_debug_reset_scratch(void);
+
+/*
+ * attnres_debug_set_epoch -- diagnostic, for tests of the split kernel's epoch
+ * wrap: sets the epoch word of every token slot of the current device's
+ * scratch to `epoch` (synchronously; records are left as they are).  Epochs
+ * run through 0 .. 2^31 - 2 and wrap to 0; the call that wraps clears the
+ * records of the chunk indices it does not use.  No call may be in flight on
+ * the device.  Returns ATTNRES_OK, ATTNRES_EINVAL (epoch out of range),
+ * ATTNRES_ENOINIT or ATTNRES_EHIP.
+ */
+int attnres_debug_set_epoch(unsigned epoch);
 
 /*
  * attnres_selftest_rounding -- diagnostic: checks on the current device that

@@ -32,6 +32,8 @@ static int abi_checks(void)
     printf("version %d\n", attnres_version());
     CHECK(attnres_version() > 0, "bad version");
     CHECK(strlen(attnres_status_string(ATTNRES_EALIAS)) > 0, "empty status string");
+    CHECK(strstr(attnres_status_string(ATTNRES_ENOINIT), "attnres_init") != NULL, "ENOINIT status string");
+    CHECK(strstr(attnres_status_string(ATTNRES_EUNSUPPORTED), "64") != NULL, "EUNSUPPORTED status string");
     /* rejected before any HIP call: no GPU is touched */
     CHECK(attnres_add_rmsnorm_fwd(NULL, NULL, NULL, NULL, 65, NULL, NULL, 1e-6f, 1, 7168, NULL, NULL, 0) ==
               ATTNRES_EUNSUPPORTED,
@@ -86,8 +88,13 @@ static int run(const char* in_path, const char* out_path)
     const void* snaps[ATTNRES_MAX_SNAPSHOTS + 1];
     for (int s = 0; s < N; ++s)
         snaps[s] = dev_rows[2 + has_add2 + s];
-    const int rc = attnres_add_rmsnorm_fwd(dev_rows[0], dev_rows[1], has_add2 ? dev_rows[2] : NULL,
-                                           N ? snaps : NULL, N, dq, dg, eps, M, H, dop, don, 0);
+    /* before attnres_init the call launches nothing and says why */
+    int rc = attnres_add_rmsnorm_fwd(dev_rows[0], dev_rows[1], has_add2 ? dev_rows[2] : NULL, N ? snaps : NULL, N,
+                                     dq, dg, eps, M, H, dop, don, 0);
+    CHECK(rc == ATTNRES_ENOINIT, "call before attnres_init -> %d (%s)", rc, attnres_status_string(rc));
+    CHECK(attnres_init() == ATTNRES_OK && attnres_init() == ATTNRES_OK, "attnres_init");
+    rc = attnres_add_rmsnorm_fwd(dev_rows[0], dev_rows[1], has_add2 ? dev_rows[2] : NULL, N ? snaps : NULL, N, dq,
+                                 dg, eps, M, H, dop, don, 0);
     CHECK(rc == ATTNRES_OK, "attnres_add_rmsnorm_fwd -> %d (%s)", rc, attnres_status_string(rc));
     CHECK(hipDeviceSynchronize() == hipSuccess, "hipDeviceSynchronize");
 

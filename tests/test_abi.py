@@ -44,10 +44,13 @@ def test_status_codes_match_header():
     assert int(codes["ATTNRES_EUNSUPPORTED"]) == ar.ATTNRES_EUNSUPPORTED
     assert int(codes["ATTNRES_EALIAS"]) == ar.ATTNRES_EALIAS
     assert int(codes["ATTNRES_EHIP"]) == ar.ATTNRES_EHIP
+    assert int(codes["ATTNRES_ENOINIT"]) == ar.ATTNRES_ENOINIT
     assert int(codes["ATTNRES_MAX_SNAPSHOTS"]) == ar.ATTNRES_MAX_SNAPSHOTS
     assert int(codes["ATTNRES_MAX_HIDDEN"]) == ar.ATTNRES_MAX_HIDDEN
     assert ar.attnres_version() >= 100
     assert "overlap" in ar.attnres_status_string(ar.ATTNRES_EALIAS)
+    assert "attnres_init" in ar.attnres_status_string(ar.ATTNRES_ENOINIT)
+    assert "64" in ar.attnres_status_string(ar.ATTNRES_EUNSUPPORTED)
 
 
 # Validation: fake but plausible 16-byte-aligned addresses.  Every call below

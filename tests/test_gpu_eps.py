@@ -1,0 +1,148 @@
+"""GPU parity across eps: the kernels' eps arithmetic against the oracle.
+
+eps is an argument of the op: it enters both the key RMSNorm of every source
+(the logits) and the final RMSNorm, and kernel W folds the softmax's division
+into the latter (scale = 1/sqrt(sum x^2 / H + eps den^2)); the split kernel's
+Gram form also tests its conditioning against sum x^2 / H + eps.  With inputs of
+mean square near 1 an eps of 1e-6 moves nothing by a bf16 ulp, so here every
+source is scaled so that its mean square sits within a factor of about 3 of
+eps (from 1e-4 to 10 over the cases): eps then moves every logit and the final
+scale by far more than the tolerance, and the outputs stay of order one, so
+the 2-ulp bar is what decides (not the 1e-2 absolute clause).  Each case runs
+the plain call and the call with the pre-norm mixture, element by element
+against the oracle, and against the oracle's unrounded value (within 0.75 ulp
+where |value| >= 0.1).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import parity as P
+from attention_residual_rmsnorm_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+EPS = [0.0, 1e-3, 0.25, 3.0]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ar():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_residual_rmsnorm_amd as ar
+
+    ar.library()
+    ar.attnres_init()
+    yield ar
+    ar.attnres_set_variant(0, 0)
+
+
+def eps_case(M, N, eps, add2=True, H=7168, seed=0):
+    """Sources with mean squares near eps (near 10^U(-2, 1) when eps = 0),
+    a query giving logits of order one, gamma = 1 + N(0, 0.1)."""
+    rng = np.random.default_rng(1000 + 97 * seed + 13 * N + M + int(eps * 1000))
+    bf = lambda x: W.to_bf16_bits(np.asarray(x, np.float64))
+
+    def sigma():
+        if eps == 0.0:
+            return 10.0 ** rng.uniform(-2.0, 0.5)
+        return float(np.sqrt(eps * 10.0 ** rng.uniform(-0.5, 0.5)))
+
+    s_p = sigma()
+    prefix = bf(s_p * rng.standard_normal((M, H)))
+    add = bf(0.5 * s_p * rng.standard_normal((M, H)))
+    add2v = bf(0.5 * s_p * rng.standard_normal((M, H))) if add2 else None
+    snaps = [bf(sigma() * rng.standard_normal((M, H))) for _ in range(N)]
+    query = bf(2.0 / np.sqrt(H) * rng.standard_normal(H))
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(H))
+    return W.Case("eps%g" % eps, M, H, prefix, add, add2v, snaps, query, gamma, eps=eps)
+
+
+def cancelling_eps_case(N, eps, M=3, H=7168, noise=0.15):
+    """Zero query (equal weights), p' = -snap_0 + noise and further snapshots in
+    opposite pairs: the mixture is a few hundredths, of mean square near
+    1e-3, so eps = 0 and 1e-3 both matter and the split kernel's one-exchange
+    form must fall back to the second exchange."""
+    rng = np.random.default_rng(2000 + N)
+    bf = lambda x: W.to_bf16_bits(np.asarray(x, np.float64))
+    f = lambda b: W.bf16_bits_to_f32(b).astype(np.float64)
+    s0 = bf(rng.standard_normal((M, H)))
+    snaps = [s0]
+    while N - len(snaps) >= 2:
+        s = bf(rng.standard_normal((M, H)))
+        snaps += [s, s ^ np.uint16(0x8000)]
+    if len(snaps) < N:
+        snaps.append(bf(noise * rng.standard_normal((M, H))))
+    prefix = bf(-f(s0) + noise * rng.standard_normal((M, H)))
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(H))
+    return W.Case("cancel-eps%g" % eps, M, H, prefix, np.zeros((M, H), np.uint16), None, snaps,
+                  np.zeros(H, np.uint16), gamma, eps=eps)
+
+
+def check(ar, orc, case, what):
+    gp, gn, gm = P.run_gpu_mix(case)
+    gp2, gn2 = P.run_gpu(case)
+    assert np.array_equal(gp, gp2) and np.array_equal(gn, gn2), what + ": plain and mix calls differ"
+    rp, rn, rm = P.run_oracle_mix(orc, case)
+    P.assert_parity(gp, gn, rp, rn, what)
+    P.assert_mix_parity(gm, rm, what)
+    _, _, exact = orc.fwd(case.prefix, case.add, case.add2, case.snapshots, case.query, case.gamma, case.eps,
+                          want_f64=True)
+    got = W.bf16_bits_to_f32(gn).astype(np.float64)
+    big = np.abs(exact) >= 0.1
+    assert big.mean() > 0.5, what + ": outputs too small for the ulp bar to decide"
+    ulp = np.exp2(np.floor(np.log2(np.abs(exact[big]))) - 7)
+    err = np.abs(got[big] - exact[big]) / ulp
+    say(what, ar.attnres_plan(case.M, case.N, case.H), "max %.3f ulp" % err.max())
+    assert err.max() <= 0.75, "%s: %.3f ulp" % (what, err.max())
+
+
+# (forced variant, param, N): kernel W (one pass; batches of 12 above 12
+# sources), the split kernel's two exchanges (1, 2 and 7 waves per chunk) and
+# its Gram form (N <= 7)
+KERNELS = [((1, 0), 4, "W"), ((1, 0), 12, "W"), ((1, 0), 20, "W batched"), ((1, 4), 12, "W 4 vectors"),
+           ((2, 1), 12, "S1w"), ((2, 2), 12, "S2w"), ((2, 7), 12, "S7w"), ((2, 2), 4, "S2w Gram"),
+           ((2, 1), 7, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((0, 0), 1, "auto")]
+
+
+@pytest.mark.parametrize("eps", EPS)
+@pytest.mark.parametrize("variant,N,label", KERNELS, ids=[k[2] + " N=%d" % k[1] for k in KERNELS])
+def test_eps(ar, orc, variant, N, label, eps):
+    case = eps_case(5, N, eps, add2=(N % 2 == 0))
+    ar.attnres_set_variant(*variant)
+    try:
+        check(ar, orc, case, "%s N=%d eps=%g" % (label, N, eps))
+    finally:
+        ar.attnres_set_variant(0, 0)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-3])
+@pytest.mark.parametrize("variant", [(2, 1), (2, 2), (2, 7), (0, 0)], ids=["S1w", "S2w", "S7w", "auto"])
+def test_eps_gram_fallback(ar, orc, variant, eps):
+    """Cancelling sources at eps = 0 and 1e-3 through the Gram form's
+    conditioning test (N = 4: the fallback to the second exchange)."""
+    case = cancelling_eps_case(4, eps)
+    ar.attnres_set_variant(*variant)
+    try:
+        check(ar, orc, case, "cancelling N=4 eps=%g %s" % (eps, variant))
+    finally:
+        ar.attnres_set_variant(0, 0)
+
+
+@pytest.mark.parametrize("eps", EPS)
+@pytest.mark.parametrize("M,N", [(256, 12), (40, 12), (1, 12), (32, 3), (256, 1)])
+def test_eps_auto_dispatch(ar, orc, M, N, eps):
+    """The automatic dispatch at the named token and source counts."""
+    case = eps_case(M, N, eps, seed=1)
+    check(ar, orc, case, "auto M=%d N=%d eps=%g" % (M, N, eps))
+
+
+def test_eps_no_timeouts(ar):
+    assert ar.attnres_debug_timeouts() == 0

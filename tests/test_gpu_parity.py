@@ -502,27 +502,41 @@ def test_no_barrier_timeouts(ar):
 def test_bounded_waits_give_up(ar, orc):
     """The split kernel's waits at its per-token barriers are bounded.  With
     the spin limit forced down to one re-poll from the host, calls of both
-    exchange forms still finish and the waits that give up are counted (the
-    results of those calls are unspecified and not checked); once the scratch
-    is cleared and the limit restored, a call is exact again."""
+    exchange forms still finish and the waits that give up are counted; each
+    such call, run on a cleared scratch, leaves out_prefix exact and every
+    out_norm element either within the bar of the oracle or NaN (a wait that
+    gives up takes NaN for what it did not receive).  Once the scratch is
+    cleared and the limit restored, calls are exact again."""
     import torch
 
     two = case_for("cfg4", lambda: W.config_case("cfg4"))  # two exchanges
     one = case_for("cfg2", lambda: W.config_case("cfg2"))  # the Gram form's one
+    refs = [P.run_oracle(orc, c) for c in (two, one)]
+    forced = 0
+    nan_seen = 0
     ar.attnres_set_variant(2, 1)
     try:
-        ar.attnres_debug_reset_scratch()
-        ar.attnres_debug_set_spin_limit(1)
-        for _ in range(10):
-            P.run_gpu(two)
-            P.run_gpu(one)
-        torch.cuda.synchronize()
-        forced = ar.attnres_debug_timeouts()
+        for rep in range(6):
+            for case, (rp, rn) in zip((two, one), refs):
+                ar.attnres_debug_reset_scratch()
+                ar.attnres_debug_set_spin_limit(1)
+                try:
+                    gp, gn = P.run_gpu(case)
+                    torch.cuda.synchronize()
+                finally:
+                    ar.attnres_debug_set_spin_limit(0)
+                forced += ar.attnres_debug_timeouts()
+                assert np.array_equal(gp, rp), "out_prefix depends on no exchange"
+                nan = P.is_nan16(gn)
+                nan_seen += int(nan.sum())
+                bad = P.norm_mismatches(gn, rn) & ~nan
+                assert not bad.any(), "call %d M=%d N=%d: %d elements neither exact nor NaN" % (
+                    rep, case.M, case.N, int(bad.sum()))
     finally:
         ar.attnres_debug_set_spin_limit(0)
         ar.attnres_debug_reset_scratch()
         ar.attnres_set_variant(0, 0)
-    say("forced timeouts", forced)
+    say("forced timeouts", forced, "NaN elements", nan_seen)
     assert forced > 0
     assert ar.attnres_debug_timeouts() == 0
     for case in (two, one):
@@ -530,6 +544,43 @@ def test_bounded_waits_give_up(ar, orc):
         rp, rn = P.run_oracle(orc, case)
         P.assert_parity(gp, gn, rp, rn, "after the reset")
     assert ar.attnres_debug_timeouts() == 0
+
+
+EPOCH_PERIOD = 0x7FFFFFFF
+
+
+def test_epoch_wrap(ar, orc):
+    """The split kernel's per-token epoch wraps from 2^31 - 2 to 0, and the
+    wrapping call clears the records of the chunk indices it does not use.
+    A call with 14 chunks (one wave each) at epoch 5 leaves records at chunk
+    indices 7..13; calls with 7 chunks (two waves each) then run across the
+    wrap; another 14-chunk call on different inputs at epoch 5 again expects
+    the tags those old records carry, and must still be exact, because the
+    wrapping call cleared them.  Epochs are set from the host between calls."""
+    a = case_for(("wrap", 0), lambda: W.make_case(cfg=80, M=8, N=8, add2=True))
+    b = case_for(("wrap", 1), lambda: W.make_case(cfg=81, M=8, N=8, add2=True))
+    ra, rb = P.run_oracle(orc, a), P.run_oracle(orc, b)
+    try:
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_set_variant(2, 1)
+        assert ar.attnres_plan(8, 8, 7168)[1] == 14
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(a), *ra, "14 chunks at epoch 5")
+        ar.attnres_set_variant(2, 2)
+        assert ar.attnres_plan(8, 8, 7168)[1] == 7
+        ar.attnres_debug_set_epoch(EPOCH_PERIOD - 2)
+        for i in range(4):  # epochs 2^31 - 3 .. 2^31 - 2, then 0 and 1
+            say("wrap: 7-chunk call", i)
+            P.assert_parity(*P.run_gpu(b), *rb, "7 chunks, call %d across the wrap" % i)
+        ar.attnres_set_variant(2, 1)
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(b), *rb, "14 chunks at epoch 5 after the wrap")
+        assert ar.attnres_debug_timeouts() == 0
+        with pytest.raises(ar.AttnResError):
+            ar.attnres_debug_set_epoch(EPOCH_PERIOD)
+    finally:
+        ar.attnres_set_variant(0, 0)
+        ar.attnres_debug_reset_scratch()
 
 
 # --- the standalone add ----------------------------------------------------------
