@@ -12,12 +12,15 @@ from ._binding import (  # noqa: F401
     ATTNRES_EHIP,
     ATTNRES_EINVAL,
     ATTNRES_ENOINIT,
+    ATTNRES_ESCRATCH,
+    ATTNRES_NOALLOC_MAX_SPLIT_TOKENS,
     ATTNRES_EUNSUPPORTED,
     ATTNRES_MAX_HIDDEN,
     ATTNRES_MAX_SNAPSHOTS,
     ATTNRES_OK,
     AttnResError,
     attnres_add_rmsnorm_fwd,
+    attnres_add_rmsnorm_fwd_noalloc,
     attnres_add_rmsnorm_mix_fwd,
     attnres_bf16_add,
     attnres_debug_timeouts,

@@ -11,6 +11,8 @@ ATTNRES_EUNSUPPORTED = -2
 ATTNRES_EALIAS = -3
 ATTNRES_EHIP = -4
 ATTNRES_ENOINIT = -5
+ATTNRES_ESCRATCH = -6
+ATTNRES_NOALLOC_MAX_SPLIT_TOKENS = 64
 ATTNRES_MAX_SNAPSHOTS = 64
 ATTNRES_MAX_HIDDEN = 16384
 
@@ -51,6 +53,10 @@ def library():
             _vp, _vp, _vp, ctypes.POINTER(_vp), ctypes.c_int, _vp, _vp, ctypes.c_float,
             ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp, _vp]
         lib.attnres_add_rmsnorm_mix_fwd.restype = ctypes.c_int
+        lib.attnres_add_rmsnorm_fwd_noalloc.argtypes = [
+            _vp, _vp, _vp, ctypes.POINTER(_vp), ctypes.c_int, _vp, _vp, ctypes.c_float,
+            ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+        lib.attnres_add_rmsnorm_fwd_noalloc.restype = ctypes.c_int
         lib.attnres_bf16_add.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp]
         lib.attnres_bf16_add.restype = ctypes.c_int
         lib.attnres_init.argtypes = []
@@ -171,6 +177,21 @@ def attnres_add_rmsnorm_fwd(prefix, add, add2, snapshots: Sequence, query, gamma
         _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
         ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _stream(stream))
     _check(rc, "attnres_add_rmsnorm_fwd")
+    return out_prefix, out_norm
+
+
+def attnres_add_rmsnorm_fwd_noalloc(prefix, add, add2, snapshots: Sequence, query, gamma, eps: float,
+                                    out_prefix, out_norm, stream=None):
+    """attnres_add_rmsnorm_fwd for callers that cannot allocate: the library
+    allocates nothing (its split-kernel scratch is a static device array) and
+    needs no attnres_init.  The outputs must be given (this wrapper allocates
+    nothing either).  Returns ``(out_prefix, out_norm)``."""
+    M, H, n, arr, out_prefix, out_norm = _fwd_args(prefix, add, add2, snapshots, query, gamma,
+                                                   out_prefix, out_norm)
+    rc = library().attnres_add_rmsnorm_fwd_noalloc(
+        _ptr(prefix), _ptr(add), _ptr(add2), arr if n else None, n, _ptr(query), _ptr(gamma),
+        ctypes.c_float(eps), M, H, _ptr(out_prefix), _ptr(out_norm), _stream(stream))
+    _check(rc, "attnres_add_rmsnorm_fwd_noalloc")
     return out_prefix, out_norm
 
 

@@ -1324,15 +1324,90 @@ int scratch_for_current_device(Scratch** out)
     return ATTNRES_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The scratch of attnres_add_rmsnorm_fwd_noalloc: a file-scope device array,
+// so that entry point never allocates.  Same layout as the allocated scratch
+// (records [token][MAX_CHUNKS][REC_STRIDE], [token][MAX_CHUNKS], epoch words
+// [token][STATE_STRIDE], the timeout counter) for STATIC_SPLIT_TOKENS token
+// slots: every call the automatic dispatch sends to the split kernel (at most
+// 64 tokens) fits.  Each device holds its own copy, at its own address, for
+// the life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory: host code uses only the address hipGetSymbolAddress
+// returns for the current device (g_static below).
+constexpr int STATIC_SPLIT_TOKENS = 64;
+constexpr size_t STATIC_REC1_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS * REC_STRIDE;
+constexpr size_t STATIC_REC2_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS;
+constexpr size_t STATIC_STATE_BYTES = sizeof(unsigned) * STATIC_SPLIT_TOKENS * STATE_STRIDE;
+constexpr size_t STATIC_SCRATCH_BYTES = STATIC_REC1_BYTES + STATIC_REC2_BYTES + STATIC_STATE_BYTES + 256;
+static_assert(STATIC_SCRATCH_BYTES % 16 == 0, "cleared in 16-byte vectors");
+
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+std::mutex g_static_mutex;
+std::atomic<unsigned char*> g_static[MAX_DEVICES]; // device address of `scratch`, per device
+
+// Clears n 16-byte vectors (the static scratch, once per device, on the
+// caller's stream: a kernel rather than a memset, so a HIP graph may hold it).
+__global__ __launch_bounds__(256) void clear_vectors(uint4* p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The static scratch of the current device: its address from
+// hipGetSymbolAddress (no allocation, no synchronisation), resolved on first
+// use on the device or in attnres_init.  On first use the array is also
+// cleared on `stream` (ordered before the call's own kernel); `clear` is false
+// only from attnres_init, which clears it synchronously instead.
+int static_scratch_for_current_device(Scratch* out, hipStream_t stream, bool clear)
+{
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc != ATTNRES_OK)
+        return rc;
+    unsigned char* base = g_static[dev].load(std::memory_order_acquire);
+    if (!base) {
+        std::lock_guard<std::mutex> lock(g_static_mutex);
+        base = g_static[dev].load(std::memory_order_acquire);
+        if (!base) {
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+                return ATTNRES_EHIP;
+            const int64_t nvec = (int64_t)(STATIC_SCRATCH_BYTES / 16);
+            if (clear) {
+                uint4* pv = static_cast<uint4*>(ptr);
+                void* args[] = {&pv, (void*)&nvec};
+                if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_vectors), dim3(256), dim3(256), args, 0,
+                                    stream) != hipSuccess)
+                    return ATTNRES_EHIP;
+            } else if (hipMemset(ptr, 0, STATIC_SCRATCH_BYTES) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+                return ATTNRES_EHIP;
+            }
+            base = static_cast<unsigned char*>(ptr);
+            g_static[dev].store(base, std::memory_order_release);
+        }
+    }
+    out->base = base;
+    out->rec1 = reinterpret_cast<unsigned long long*>(base);
+    out->rec2 = reinterpret_cast<unsigned long long*>(base + STATIC_REC1_BYTES);
+    out->state = reinterpret_cast<unsigned*>(base + STATIC_REC1_BYTES + STATIC_REC2_BYTES);
+    out->timeouts = reinterpret_cast<unsigned*>(base + STATIC_REC1_BYTES + STATIC_REC2_BYTES + STATIC_STATE_BYTES);
+    return ATTNRES_OK;
+}
+
 } // namespace attnres
 
 using namespace attnres;
 
 namespace attnres {
 
+// The fused call.  static_scratch: the split kernel's scratch is the static
+// array (attnres_add_rmsnorm_fwd_noalloc: no attnres_init needed, at most
+// STATIC_SPLIT_TOKENS tokens in the split kernel); otherwise the allocated
+// one, which attnres_init must have set up on the device.
 int launch_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
                int n_snapshots, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
-               void* out_prefix, void* out_norm, void* out_mix, hipStream_t stream)
+               void* out_prefix, void* out_norm, void* out_mix, hipStream_t stream, bool static_scratch = false)
 {
     int rc = validate_fwd(prefix, add, add2, snapshots, n_snapshots, query, gamma, eps, M, H,
                           out_prefix, out_norm, out_mix);
@@ -1344,10 +1419,17 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
         return rc;
     if (M == 0)
         return ATTNRES_OK;
-    // every fused call needs attnres_init on its device (whichever kernel the
-    // plan picks, so that the rule does not depend on the sizes)
-    Scratch* sc = nullptr;
-    rc = scratch_for_current_device(&sc);
+    Scratch static_view;
+    Scratch* sc = &static_view;
+    if (static_scratch) {
+        if (pl.variant == 2 && M > STATIC_SPLIT_TOKENS)
+            return ATTNRES_ESCRATCH;
+        rc = pl.variant == 2 ? static_scratch_for_current_device(&static_view, stream, true) : ATTNRES_OK;
+    } else {
+        // every fused call needs attnres_init on its device (whichever kernel
+        // the plan picks, so that the rule does not depend on the sizes)
+        rc = scratch_for_current_device(&sc);
+    }
     if (rc != ATTNRES_OK)
         return rc;
 
@@ -1427,6 +1509,15 @@ extern "C" int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, 
                       out_norm, out_mix, stream);
 }
 
+extern "C" int attnres_add_rmsnorm_fwd_noalloc(const void* prefix, const void* add, const void* add2,
+                                               const void* const* snapshots, int n_snapshots,
+                                               const void* query, const void* gamma, float eps, int64_t M,
+                                               int64_t H, void* out_prefix, void* out_norm, hipStream_t stream)
+{
+    return launch_fwd(prefix, add, add2, snapshots, n_snapshots, query, gamma, eps, M, H, out_prefix,
+                      out_norm, nullptr, stream, true);
+}
+
 extern "C" int attnres_bf16_add(const void* a, const void* b, void* out, int64_t n, hipStream_t stream)
 {
     const int rc = validate_add(a, b, out, n);
@@ -1449,7 +1540,14 @@ extern "C" int attnres_bf16_add(const void* a, const void* b, void* out, int64_t
     return ATTNRES_OK;
 }
 
-extern "C" int attnres_init(void) { return init_scratch(); }
+extern "C" int attnres_init(void)
+{
+    const int rc = init_scratch();
+    if (rc != ATTNRES_OK)
+        return rc;
+    Scratch view;
+    return static_scratch_for_current_device(&view, nullptr, false);
+}
 
 extern "C" int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunks,
                             int* threads)
@@ -1539,6 +1637,8 @@ extern "C" const char* attnres_status_string(int status)
     case ATTNRES_EALIAS: return "forbidden buffer overlap";
     case ATTNRES_EHIP: return "HIP error";
     case ATTNRES_ENOINIT: return "attnres_init() has not run on the current device";
+    case ATTNRES_ESCRATCH:
+        return "the call needs more than the static scratch holds (split-hidden kernel for more than 64 tokens)";
     default: return "unknown status";
     }
 }

@@ -68,6 +68,10 @@ extern "C" {
                                      out of memory for the scratch) */
 #define ATTNRES_ENOINIT (-5)      /* a fused call on a device where attnres_init()
                                      has not run: nothing was launched */
+#define ATTNRES_ESCRATCH (-6)     /* attnres_add_rmsnorm_fwd_noalloc: the call would
+                                     need more token slots than its static scratch
+                                     holds (ATTNRES_NOALLOC_MAX_SPLIT_TOKENS): nothing
+                                     was launched */
 
 #define ATTNRES_MAX_SNAPSHOTS 64 /* up to 12 (the page's fused window, section "Model")
                                     the sources are taken in one pass; 13..64 are fused
@@ -77,6 +81,7 @@ extern "C" {
                                     up to 31 at once), so the page's N > 12 fallback is
                                     not needed below 65 */
 #define ATTNRES_MAX_HIDDEN 16384
+#define ATTNRES_NOALLOC_MAX_SPLIT_TOKENS 64 /* token slots of the no-allocation scratch */
 
 /*
  * attnres_add_rmsnorm_fwd -- the fused decode step described above.
@@ -150,6 +155,36 @@ int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void*
                                 void* out_mix, hipStream_t stream);
 
 /*
+ * attnres_add_rmsnorm_fwd_noalloc -- attnres_add_rmsnorm_fwd for callers that
+ * cannot allocate device memory: code under HIP-graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing and needs no
+ * attnres_init(): the split-hidden kernel's scratch is a static device array
+ * of the library (about 1.05 MB per device, held until the process ends),
+ * with ATTNRES_NOALLOC_MAX_SPLIT_TOKENS token slots.
+ *
+ * Arguments, accuracy, dispatch and results are those of
+ * attnres_add_rmsnorm_fwd (the same kernels, bit for bit the same outputs).
+ * A call whose sizes select the split-hidden kernel for more than
+ * ATTNRES_NOALLOC_MAX_SPLIT_TOKENS tokens (only possible through
+ * attnres_set_variant: the automatic dispatch splits at most 64 tokens)
+ * returns ATTNRES_ESCRATCH and launches nothing.  The first call on a device
+ * that uses the static scratch looks up its address (hipGetSymbolAddress; no
+ * allocation, no synchronisation) and enqueues one kernel on `stream` that
+ * clears it, ordered before the call's own kernel; attnres_init(), if called
+ * on the device, does both beforehand.  Every call on a device shares that
+ * device's array: calls on one device that overlap in time (different
+ * streams, not synchronised) race on it, as for attnres_add_rmsnorm_fwd.
+ *
+ * Returns ATTNRES_OK, ATTNRES_ESCRATCH or one of the codes of
+ * attnres_add_rmsnorm_fwd other than ATTNRES_ENOINIT.
+ */
+int attnres_add_rmsnorm_fwd_noalloc(const void* prefix, const void* add, const void* add2,
+                                    const void* const* snapshots, int n_snapshots,
+                                    const void* query, const void* gamma, float eps,
+                                    int64_t M, int64_t H, void* out_prefix, void* out_norm,
+                                    hipStream_t stream);
+
+/*
  * attnres_bf16_add -- the unfused MoE-tail addition: out = bf16(a + b)
  * elementwise (binary32 round-to-nearest add, subnormals kept), n elements.
  * This is the standalone kernel the fold replaces (page "[#20545][perf] Kimi
@@ -165,10 +200,12 @@ int attnres_bf16_add(const void* a, const void* b, void* out, int64_t n,
 
 /*
  * attnres_init -- allocate and clear the split-hidden scratch on the current
- * device (synchronously: hipMalloc, hipMemset, hipDeviceSynchronize).  Must
- * run once on each device before the first fused call there (those calls
- * return ATTNRES_ENOINIT otherwise); later calls return at once.  Not for use
- * during HIP-graph capture.  Thread-safe.  Returns ATTNRES_OK or ATTNRES_EHIP.
+ * device (synchronously: hipMalloc, hipMemset, hipDeviceSynchronize), and
+ * look up and clear the static scratch of attnres_add_rmsnorm_fwd_noalloc.
+ * Must run once on each device before the first attnres_add_rmsnorm_fwd /
+ * _mix_fwd call there (those return ATTNRES_ENOINIT otherwise); later calls
+ * return at once.  Not for use during HIP-graph capture.  Thread-safe.
+ * Returns ATTNRES_OK or ATTNRES_EHIP.
  */
 int attnres_init(void);
 
