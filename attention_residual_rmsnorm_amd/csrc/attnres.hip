@@ -30,7 +30,8 @@
 //      sources the chunk's Gram matrix travels instead and one exchange gives
 //      both.  Spreads a few tokens over many CUs, which is what the
 //      latency-bound small-M calls need.
-// Outputs are written with the non-temporal hint in both kernels.
+// Outputs are written with the non-temporal hint in both kernels; kernel W
+// writes out_prefix after the token's last group, right before out_norm.
 // Both reduce in a fixed order: the same inputs give the same bits, and the
 // add2 / no-add2 instantiations share every line after A1.
 #include "attnres.h"
@@ -112,19 +113,13 @@ __device__ __forceinline__ void store_stream(uint4* p, const uint4& v)
     __builtin_nontemporal_store(v.w, &p->w);
 }
 
-// Kernel W's out_prefix, written right after the first group arrives: in a
-// call with many sources (S >= 9) a plain store does better, because its
-// lines leave L2 in the background while the remaining sources stream in
-// instead of competing with them (M = 256, N = 10: 11.84 -> 11.54 us; with
-// N <= 7 the streamed store wins, N = 5: 8.46 against 8.97 us).
-template <int S>
-__device__ __forceinline__ void store_prefix(uint4* p, const uint4& v)
-{
-    if constexpr (S >= 9)
-        *p = v;
-    else
-        store_stream(p, v);
-}
+// Kernel W's out_prefix is held in registers and written after the token's
+// last group is mixed, just before A5, next to out_norm: the [M,H] rows of a
+// call are then written in one burst at the end of each token instead of in
+// the middle of its read stream.  Written early (non-temporal, or plain from
+// nine sources on) the 25-layer M = 256 chain took 9.92 us per launch; written
+// late, 9.20 (bench.py's chain: 4,467 -> 4,830 GB/s).  Reads and writes
+// interleaved on the same HBM channels cost far more than their bytes.
 
 // Loads of vector v of one token's rows (16 bytes = 8 bf16 each).  The loads
 // are unconditional: a lane past the end of the row reads the row's last
@@ -639,9 +634,9 @@ constexpr int group_start(int i)
 }
 
 // Kernel W's pipeline over one batch of S sources, step GI: issue the loads of
-// group GI + LA, then (batch with p', step 0) apply A1 and store out_prefix,
-// then mix group GI.  Group gi uses LDS slot gi % 2.  Any reuse of a slot is
-// ordered by the two barriers of every group: a thread writes a group's rows
+// group GI + LA, then (batch with p', step 0) apply A1, then mix group GI.
+// Group gi uses LDS slot gi % 2.  Any reuse of a slot is ordered by the two
+// barriers of every group: a thread writes a group's rows
 // only after the previous group's second barrier (wave 0 has read that
 // group's rows), and wave 0 writes a group's totals only after its first
 // barrier (every thread has read the previous totals).  FIRSTBATCH: the first
@@ -658,14 +653,8 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
         if constexpr (GI + LA < NG)
             issue_range<group_start<S, G>(GI + LA), group_start<S, G>(GI + LA + 1), HASP, ADD2, VPT, S>(
                 p, snap, row, vc, a, b, c, k);
-        if constexpr (HASP && GI == 0) {
-            // A1
-            fold_add<ADD2, VPT>(a, b, c, k[0]);
-#pragma unroll
-            for (int j = 0; j < VPT; ++j)
-                if (ok[j])
-                    store_prefix<S>(&p.out_prefix[row + tid + j * nthreads], k[0][j]);
-        }
+        if constexpr (HASP && GI == 0)
+            fold_add<ADD2, VPT>(a, b, c, k[0]); // A1 (p' stored after the batch, see stream_batch)
         constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
         constexpr int wide_rows = G > ONE_GROUP ? MAXB / 16 : 0;
         mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, wide_rows>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p,
@@ -676,7 +665,7 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
 }
 
 // One batch of S sources through the pipeline: the first LA groups' loads,
-// then the steps.
+// then the steps; a batch that starts with p' then writes out_prefix.
 template <int S, int G, int LA, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT, int MAXB>
 __device__ __forceinline__ void stream_batch(const Params& p, const uint4* const* snap, int64_t row,
                                              const int (&vc)[VPT], uint4 (&a)[VPT], uint4 (&b)[VPT],
@@ -688,6 +677,12 @@ __device__ __forceinline__ void stream_batch(const Params& p, const uint4* const
     issue_range<0, group_start<S, G>(LA < NG ? LA : NG), HASP, ADD2, VPT, S>(p, snap, row, vc, a, b, c, k);
     stream_groups<S, G, LA, 0, HASP, FIRSTBATCH, ADD2, VPT, MAXB>(p, snap, row, vc, a, b, c, k, q, ok, mx, rows,
                                                                   tot, tid, nthreads);
+    if constexpr (HASP) { // out_prefix (p', source 0) once the batch's sources are all in
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+            if (ok[j])
+                store_stream(&p.out_prefix[row + tid + j * nthreads], k[0][j]);
+    }
 }
 
 // LDS set-up shared by both forms of kernel W: group_sums' entries of absent
