@@ -80,7 +80,10 @@ struct Params {
     int nvec;           // H / 8 (16-byte vectors per row)
     int chunks;         // split hidden: workgroups per token
     int64_t M;
-    unsigned long long* rec1; // split hidden: [token][MAX_CHUNKS][REC_STRIDE] tagged A2 partials
+    int64_t split_base;       // split hidden: first token it serves (the hybrid's W part takes [0, split_base))
+    int split_threads;        // split hidden: threads per chunk (the workgroup's others exit at once)
+    int wg_blocks;            // hybrid: workgroups of its W part
+    unsigned long long* rec1; // split hidden: [token slot][MAX_CHUNKS][REC_STRIDE] tagged A2 partials
     unsigned long long* rec2; // split hidden: [token][MAX_CHUNKS] tagged chunk sums of x^2
     unsigned* state;          // split hidden: [token][STATE_STRIDE] epoch word (index 0)
     unsigned* timeouts;       // split hidden: exchange waits that gave up
@@ -743,8 +746,9 @@ __device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, co
     __syncthreads(); // LDS reuse by the next token
 }
 
+// Kernel W's body: tokens t0, t0 + stride, ... below tend, one at a time.
 template <int NS, bool ADD2, int VPT, int MAXB, int G, int LA>
-__global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
+__device__ __forceinline__ void wg_tokens(const Params& p, int64_t t0, int64_t tend, int64_t stride)
 {
     constexpr int S = NS + 1;
     constexpr int MAXW = MAXB / 64;
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
     const int nvec = p.nvec;
     wg_prologue<MAXW, G, MAXB>(&rows[0][0], red2, tid, nthreads);
 
-    for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
+    for (int64_t t = t0; t < tend; t += stride) {
         const int64_t row = t * (int64_t)nvec;
         uint4 k[S][VPT], q[VPT], g[VPT], a[VPT], b[VPT], c[VPT];
         bool ok[VPT];
@@ -782,6 +786,12 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
         // A5
         wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
     }
+}
+
+template <int NS, bool ADD2, int VPT, int MAXB, int G, int LA>
+__global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg(Params p)
+{
+    wg_tokens<NS, ADD2, VPT, MAXB, G, LA>(p, blockIdx.x, p.M, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -868,10 +878,10 @@ __device__ __forceinline__ unsigned long long gave_up(unsigned tag)
     return ((unsigned long long)tag << 32) | 0x7fc00000u; // the tag, and a quiet NaN
 }
 
-__device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t t, int C)
+__device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t slot, int C)
 {
-    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
-    unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC_STRIDE;
+    unsigned long long* rec2 = p.rec2 + (size_t)slot * MAX_CHUNKS;
     for (int c = C; c < MAX_CHUNKS; ++c) {
         for (int v = 0; v < REC_STRIDE; ++v)
             __hip_atomic_store(&rec1[c * REC_STRIDE + v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -879,11 +889,11 @@ __device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t t, int
     }
 }
 
-__device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, unsigned epoch, int64_t t, int C)
+__device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, unsigned epoch, int64_t slot, int C)
 {
     const unsigned next = epoch + 1u >= EPOCH_PERIOD ? 0u : epoch + 1u;
     if (next == 0u)
-        clear_unused_chunks(p, t, C);
+        clear_unused_chunks(p, slot, C);
     __hip_atomic_store(state, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -916,8 +926,12 @@ __device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, 
 // Two families: MAXB = 128 (1-2 waves per workgroup, up to 32 chunks) and
 // MAXB = 512 (4-8 waves, at most 8 chunks; capped at 128 VGPRs so that two
 // workgroups share a CU).
-template <int NS, bool ADD2, int MAXB, int MAXC, int WPE>
-__global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
+// Kernel S's body for workgroup b of its part of the grid, nthreads threads
+// per chunk (threads beyond exit at once, before any barrier); its tokens are
+// split_base + 0, 1, ..., and token slot t - split_base of the scratch serves
+// token t.
+template <int NS, bool ADD2, int MAXB, int MAXC>
+__device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads)
 {
     constexpr int S = NS + 1;
     constexpr bool GRAM = S <= GRAM_MAX_SOURCES;
@@ -936,19 +950,20 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
     __shared__ float gram_sh[2]; // Gram form, 4-8 waves: wave 0's sum of x^2 and decision
 
     const int tid = threadIdx.x;
+    if (tid >= nthreads)
+        return;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nthreads = blockDim.x;
     const int nw = nthreads >> 6;
     const int C = p.chunks;
-    const int b = blockIdx.x;
     const int ib = b >> 3;
-    const int64_t t = (int64_t)(ib / C) * 8 + (b & 7);
+    const int64_t slot = (int64_t)(ib / C) * 8 + (b & 7);
+    const int64_t t = p.split_base + slot;
     const int chunk = ib - (ib / C) * C;
     if (t >= p.M)
         return;
 
-    unsigned* state = p.state + (size_t)t * STATE_STRIDE;
+    unsigned* state = p.state + (size_t)slot * STATE_STRIDE;
     const unsigned epoch = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned tag1 = 2u * epoch + 1u, tag2 = 2u * epoch + 2u;
 
@@ -987,7 +1002,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
                                4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
     }
     __syncthreads();
-    unsigned long long* rec1 = p.rec1 + (size_t)t * MAX_CHUNKS * REC_STRIDE;
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC_STRIDE;
     if (tid < NV) { // rows in order, loaded 8 at a time so the loads overlap
         const int nrows = nthreads >> 4;
         float acc = rows[tid];
@@ -1125,7 +1140,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
         // chunk's first record, so every workgroup of the token has read E.
         ssum = gram_ssum;
         if (chunk == 0 && tid == 0)
-            advance_epoch(p, state, epoch, t, C);
+            advance_epoch(p, state, epoch, slot, C);
     } else {
         if (lane == 0)
             red2[wave] = sx;
@@ -1134,7 +1149,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
         // A5: the chunk's sum of x^2 (its waves in order) published by thread 0;
         // every wave (PERWAVE) or wave 0 reads the C records (lane c: chunk c) and
         // adds them on DPP
-        unsigned long long* rec2 = p.rec2 + (size_t)t * MAX_CHUNKS;
+        unsigned long long* rec2 = p.rec2 + (size_t)slot * MAX_CHUNKS;
         if (tid == 0) {
             float s2 = red2[0];
             for (int w = 1; w < nw; ++w)
@@ -1154,7 +1169,7 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
             }
             ssum = wave_sum(__uint_as_float((unsigned)w2));
             if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
-                advance_epoch(p, state, epoch, t, C);
+                advance_epoch(p, state, epoch, slot, C);
             if (!PERWAVE && lane == 0)
                 ssum_sh = ssum;
         }
@@ -1169,6 +1184,12 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
         if (p.out_mix) // the pre-norm mixture (the weights sum to one here)
             store_stream(&p.out_mix[row + v], pack_scaled(x[0], 1.0f));
     }
+}
+
+template <int NS, bool ADD2, int MAXB, int MAXC, int WPE>
+__global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
+{
+    split_chunk<NS, ADD2, MAXB, MAXC>(p, blockIdx.x, blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1201,6 +1222,31 @@ constexpr int WG_LOOKAHEAD = 1; // groups whose loads are in flight ahead of the
 // two, at 62, keeps more waves per CU and wins.
 constexpr int WG_SHORT_GROUP = MAX_SNAP + 1;
 constexpr int WG_SHORT_LOOKAHEAD = 1;
+
+// ---------------------------------------------------------------------------
+// The hybrid launch (H of 4104..8192, a few more tokens than CUs, one pass of
+// sources): workgroups [0, wg_blocks) run kernel W on tokens [0, split_base),
+// the rest run kernel S's chunks of split_threads threads (4 to 8 waves; the
+// workgroup's other waves exit at once) on tokens [split_base, M).  With
+// split_base = the CU count each CU holds one W token and about one chunk,
+// instead of some CUs holding two whole tokens and the others one.
+constexpr int HYBRID_WG_THREADS_MAX = 512;
+
+template <int NS, bool ADD2>
+__global__ __launch_bounds__(HYBRID_WG_THREADS_MAX, 4) void fwd_hybrid(Params p)
+{
+    if ((int)blockIdx.x < p.wg_blocks) // uniform over the workgroup
+        wg_tokens<NS, ADD2, 2, HYBRID_WG_THREADS_MAX, WG_GROUP, WG_LOOKAHEAD>(p, blockIdx.x, p.split_base,
+                                                                             p.wg_blocks);
+    else
+        split_chunk<NS, ADD2, HYBRID_WG_THREADS_MAX, 8>(p, (int)blockIdx.x - p.wg_blocks, p.split_threads);
+}
+
+template <bool A2, int... I>
+constexpr std::array<Kernel, sizeof...(I)> hybrid_table(std::integer_sequence<int, I...>)
+{
+    return {{&fwd_hybrid<I, A2>...}};
+}
 
 template <bool A2, int VPT, int MAXB, int G, int LA, int... I>
 constexpr std::array<Kernel, sizeof...(I)> wg_table(std::integer_sequence<int, I...>)
@@ -1248,6 +1294,8 @@ const std::array<Kernel, MAX_SPLIT_SNAP + 1> kSpSmall[2] = {
 // split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
 const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8, 4>(Seq{}),
                                                       split_table<true, 512, 8, 4>(Seq{})};
+// the hybrid of the two
+const std::array<Kernel, MAX_SNAP + 1> kHybrid[2] = {hybrid_table<false>(Seq{}), hybrid_table<true>(Seq{})};
 
 struct Scratch {
     void* base = nullptr;
@@ -1324,8 +1372,8 @@ int scratch_for_current_device(Scratch** out)
 // so that entry point never allocates.  Same layout as the allocated scratch
 // (records [token][MAX_CHUNKS][REC_STRIDE], [token][MAX_CHUNKS], epoch words
 // [token][STATE_STRIDE], the timeout counter) for STATIC_SPLIT_TOKENS token
-// slots: every call the automatic dispatch sends to the split kernel (at most
-// 64 tokens) fits.  Each device holds its own copy, at its own address, for
+// slots: every call the automatic dispatch makes fits (the split kernel takes
+// at most 64 tokens, the hybrid's split part at most 64).  Each device holds its own copy, at its own address, for
 // the life of the process.  In host code `scratch` names a host-side stand-in,
 // not device memory: host code uses only the address hipGetSymbolAddress
 // returns for the current device (g_static below).
@@ -1398,8 +1446,8 @@ namespace attnres {
 
 // The fused call.  static_scratch: the split kernel's scratch is the static
 // array (attnres_add_rmsnorm_fwd_noalloc: no attnres_init needed, at most
-// STATIC_SPLIT_TOKENS tokens in the split kernel); otherwise the allocated
-// one, which attnres_init must have set up on the device.
+// STATIC_SPLIT_TOKENS token slots); otherwise the allocated one, which
+// attnres_init must have set up on the device.
 int launch_fwd(const void* prefix, const void* add, const void* add2, const void* const* snapshots,
                int n_snapshots, const void* query, const void* gamma, float eps, int64_t M, int64_t H,
                void* out_prefix, void* out_norm, void* out_mix, hipStream_t stream, bool static_scratch = false)
@@ -1417,9 +1465,9 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     Scratch static_view;
     Scratch* sc = &static_view;
     if (static_scratch) {
-        if (pl.variant == 2 && M > STATIC_SPLIT_TOKENS)
+        if (pl.split_slots > STATIC_SPLIT_TOKENS)
             return ATTNRES_ESCRATCH;
-        rc = pl.variant == 2 ? static_scratch_for_current_device(&static_view, stream, true) : ATTNRES_OK;
+        rc = pl.split_slots > 0 ? static_scratch_for_current_device(&static_view, stream, true) : ATTNRES_OK;
     } else {
         // every fused call needs attnres_init on its device (whichever kernel
         // the plan picks, so that the rule does not depend on the sizes)
@@ -1444,6 +1492,9 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.nvec = (int)(H / 8);
     p.chunks = pl.chunks;
     p.M = M;
+    p.split_base = pl.split_base;
+    p.split_threads = pl.variant == 3 ? pl.split_threads : pl.threads;
+    p.wg_blocks = pl.wg_blocks;
     p.spin_limit = g_spin_limit;
 
     const int a2 = add2 ? 1 : 0;
@@ -1465,12 +1516,15 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
         return ATTNRES_OK;
     }
     Kernel fn = nullptr;
-    if (pl.variant == 2) {
+    if (pl.variant == 2 || pl.variant == 3) {
         p.rec1 = sc->rec1;
         p.rec2 = sc->rec2;
         p.state = sc->state;
         p.timeouts = sc->timeouts;
-        fn = pl.threads <= 128 ? kSpSmall[a2][n_snapshots] : kSpLarge[a2][n_snapshots];
+        if (pl.variant == 3)
+            fn = kHybrid[a2][n_snapshots];
+        else
+            fn = pl.threads <= 128 ? kSpSmall[a2][n_snapshots] : kSpLarge[a2][n_snapshots];
     } else {
         const auto& wg1 = pl.single_group ? kWg1Small : kWg1;
         fn = (pl.vpt == 1 ? wg1 : pl.vpt == 2 ? kWg2 : kWg4)[a2][n_snapshots];

@@ -63,7 +63,37 @@ bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
     pl.threads = threads;
     pl.chunks = chunks;
     pl.grid = 8 * (int64_t)chunks * ((M + 7) / 8);
+    pl.split_threads = threads;
+    pl.split_slots = M;
     return true;
+}
+
+// Hybrid: kernel W (two vectors per thread) on the first nw tokens, one
+// workgroup each, then 4-wave split chunks (a quarter of a row at H = 7168) on
+// the other M - nw; nw is a multiple of 8 so the chunks of a token keep one
+// workgroup id mod 8.
+bool plan_hybrid(int64_t M, int nvec, Plan& pl)
+{
+    if (nvec <= 512 || nvec > 1024 || M < 1)
+        return false;
+    const int64_t nw = M > HYBRID_WG_TOKENS ? HYBRID_WG_TOKENS : (M / 2) / 8 * 8;
+    const int64_t rest = M - nw;
+    if (rest > MAX_SPLIT_TOKENS)
+        return false;
+    const int threads = round_up64((nvec + 1) / 2);
+    const int chunk_threads = HYBRID_CHUNK_THREADS;
+    const int chunks = (nvec + chunk_threads - 1) / chunk_threads;
+    pl = Plan{};
+    pl.variant = 3;
+    pl.vpt = 2;
+    pl.threads = threads;
+    pl.chunks = chunks;
+    pl.split_base = nw;
+    pl.split_threads = chunk_threads;
+    pl.wg_blocks = (int)nw;
+    pl.grid = nw + 8 * (int64_t)chunks * ((rest + 7) / 8);
+    pl.split_slots = rest;
+    return threads >= HYBRID_CHUNK_THREADS && chunks <= 8;
 }
 
 } // namespace
@@ -144,6 +174,7 @@ bool valid_override(int variant, int param)
     case 0: return param == 0;
     case 1: return param == 0 || param == 1 || param == 2 || param == 4;
     case 2: return param >= 0 && param <= 8 && param != 3;
+    case 3: return param == 0;
     default: return false;
     }
 }
@@ -168,6 +199,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         return plan_split(M, nvec, many && force_param == 0 ? 2 : force_param, pl) ? ATTNRES_OK
                                                                                     : ATTNRES_EINVAL;
     }
+    if (force_variant == 3)
+        return !many && plan_hybrid(M, nvec, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
     //  * 2 <= N <= 7, M <= 32: 2-wave chunks, whose Gram form needs one
@@ -211,6 +244,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         if (n >= 8 && !many && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;
     }
+    // Just past the CU count, kernel W would give some CUs two whole tokens
+    // and the others one; the hybrid gives every CU one W token and a few
+    // split chunks of the rest.
+    if (long_rows && !many && M > HYBRID_WG_TOKENS && M <= HYBRID_MAX_TOKENS && plan_hybrid(M, nvec, pl))
+        return ATTNRES_OK;
     if (plan_wg(M, nvec, wg_vpt, pl))
         return ATTNRES_OK;
     return split_ok && plan_split(M, nvec, many ? 2 : 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;

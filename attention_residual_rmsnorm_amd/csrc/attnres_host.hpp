@@ -43,13 +43,28 @@ constexpr int MID_SPLIT_MIN_SNAP = 8;
 constexpr int SHORT_WG_THREADS = 256;
 constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 65536;
 
+// The hybrid launch (kernel W's workgroups for the first HYBRID_WG_TOKENS
+// tokens, one token each, and 4-wave split chunks of HYBRID_CHUNK_THREADS
+// threads for the rest), automatic for rows of LONG_ROW_VECTORS..1024 vectors,
+// one pass of sources and HYBRID_WG_TOKENS < M <= HYBRID_MAX_TOKENS: one chunk
+// per CU at most next to its W token.  (Beyond, chunks either queue for a CU's
+// second workgroup slot or, as wide as half a row, lose to kernel W: M = 321,
+// N = 12: 19.65 against 18.79 us.)
+constexpr int HYBRID_WG_TOKENS = 256;
+constexpr int HYBRID_MAX_TOKENS = 320;
+constexpr int HYBRID_CHUNK_THREADS = 256;
+
 struct Plan {
-    int variant = 0; // 1 = workgroup per token, 2 = split hidden
+    int variant = 0; // 1 = workgroup per token, 2 = split hidden, 3 = hybrid
     int vpt = 0;     // 16-byte vectors per thread
     int threads = 0; // threads per workgroup
-    int chunks = 1;  // workgroups per token
+    int chunks = 1;  // workgroups per token (split part)
     int64_t grid = 0;
     bool single_group = false; // kernel W: all sources of a pass in one group
+    int64_t split_base = 0;    // first token of the split part (hybrid: tokens before it are W's)
+    int split_threads = 0;     // threads per split chunk
+    int wg_blocks = 0;         // hybrid: workgroups of the W part
+    int64_t split_slots = 0;   // scratch token slots the call uses (0: no scratch)
 };
 
 // Full validation of a fused call; returns a status code (ATTNRES_*).

@@ -164,10 +164,10 @@ int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void*
  *
  * Arguments, accuracy, dispatch and results are those of
  * attnres_add_rmsnorm_fwd (the same kernels, bit for bit the same outputs).
- * A call whose sizes select the split-hidden kernel for more than
+ * A call whose sizes give the split-hidden kernel more than
  * ATTNRES_NOALLOC_MAX_SPLIT_TOKENS tokens (only possible through
- * attnres_set_variant: the automatic dispatch splits at most 64 tokens)
- * returns ATTNRES_ESCRATCH and launches nothing.  The first call on a device
+ * attnres_set_variant: the automatic dispatch splits at most 64) returns
+ * ATTNRES_ESCRATCH and launches nothing.  The first call on a device
  * that uses the static scratch looks up its address (hipGetSymbolAddress; no
  * allocation, no synchronisation) and enqueues one kernel on `stream` that
  * clears it, ordered before the call's own kernel; attnres_init(), if called
@@ -211,8 +211,10 @@ int attnres_init(void);
 
 /*
  * attnres_plan -- the launch the fused call would make for (M, N, H), without
- * any HIP call.  *variant: 1 = workgroup per token, 2 = split hidden;
- * *chunks: workgroups per token; *threads: threads per workgroup.  Any output
+ * any HIP call.  *variant: 1 = workgroup per token, 2 = split hidden, 3 =
+ * hybrid (one workgroup per token for the first 256 tokens, split-hidden
+ * chunks for the rest, in one launch); *chunks: workgroups per token (of the
+ * split part); *threads: threads per workgroup.  Any output
  * pointer may be NULL.  Returns ATTNRES_OK or the status the call would return
  * for these sizes.
  */
@@ -223,8 +225,10 @@ int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunk
  * attnres_set_variant -- process-wide dispatch override for tests and
  * benchmarks: variant 0 = automatic (param 0); 1 = workgroup per token, param =
  * 16-byte vectors per thread (0 automatic, or 1, 2, 4); 2 = split hidden, param
- * = waves per workgroup (0 automatic, or 1, 2, 4..8).  A size the forced variant
- * cannot serve makes the fused call return ATTNRES_EINVAL.  Not thread-safe
+ * = waves per workgroup (0 automatic, or 1, 2, 4..8); 3 = hybrid, param 0
+ * (rows of 4104..8192 elements, at most 12 snapshots; below 257 tokens the
+ * workgroup-per-token part takes about half of them).  A size the forced
+ * variant cannot serve makes the fused call return ATTNRES_EINVAL.  Not thread-safe
  * with concurrent calls.  Returns ATTNRES_OK or ATTNRES_EINVAL.
  */
 int attnres_set_variant(int variant, int param);

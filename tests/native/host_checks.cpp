@@ -70,7 +70,7 @@ int main()
                                         snaps[n - 1]) == ATTNRES_EALIAS);
             }
             Plan pl;
-            for (int fv = 0; fv <= 2; ++fv)
+            for (int fv = 0; fv <= 3; ++fv)
                 for (int fp = 0; fp <= 9; ++fp) {
                     if (!valid_override(fv, fp))
                         continue;
@@ -93,8 +93,24 @@ int main()
                                 if (pl.variant == 2)
                                     EXPECT(m <= MAX_SPLIT_TOKENS && pl.chunks <= MAX_CHUNKS &&
                                            pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&
-                                           pl.threads <= 512 &&
+                                           pl.threads <= 512 && pl.split_slots == m &&
+                                           pl.split_threads == pl.threads &&
                                            pl.chunks <= (pl.threads <= 128 ? MAX_CHUNKS : 8));
+                                // the hybrid: W on [0, split_base), one workgroup per token, 4-wave
+                                // chunks on the rest (the split family of up to 8 chunks, one pass of
+                                // sources), chunks of a token on one workgroup id mod 8
+                                if (pl.variant == 3)
+                                    EXPECT(n <= MAX_SNAP && pl.vpt == 2 && pl.threads <= 512 &&
+                                           pl.threads >= HYBRID_CHUNK_THREADS &&
+                                           (int64_t)pl.threads * 2 * 8 >= h && pl.split_base % 8 == 0 &&
+                                           pl.wg_blocks == pl.split_base && pl.split_base <= HYBRID_WG_TOKENS &&
+                                           pl.split_base < m && m - pl.split_base <= MAX_SPLIT_TOKENS &&
+                                           pl.split_slots == m - pl.split_base &&
+                                           pl.split_threads == HYBRID_CHUNK_THREADS && pl.chunks <= 8 &&
+                                           (int64_t)pl.chunks * pl.split_threads * 8 >= h &&
+                                           pl.grid == pl.split_base + 8 * pl.chunks * ((pl.split_slots + 7) / 8));
+                                if (pl.variant == 1)
+                                    EXPECT(pl.split_slots == 0);
                             } else {
                                 EXPECT(fv != 0 || h > 8192); // automatic always finds a plan
                             }
@@ -114,6 +130,22 @@ int main()
         EXPECT(make_plan(1, 4, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
         EXPECT(make_plan(1, 12, 7168, 1, 1, pl) == ATTNRES_OK && pl.threads == 896 && !pl.single_group);
         EXPECT(make_plan(1, 13, 896, 1, 0, pl) == ATTNRES_OK && pl.vpt == 2 && !pl.single_group);
+    }
+    // the hybrid just past the CU count, automatic at H = 7168 for one pass of sources
+    {
+        Plan pl;
+        EXPECT(make_plan(256, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
+        EXPECT(make_plan(257, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 && pl.split_base == 256 &&
+               pl.chunks == 4 && pl.grid == 256 + 32);
+        EXPECT(make_plan(HYBRID_MAX_TOKENS, 1, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 &&
+               pl.chunks == 4 && pl.split_threads == 256);
+        EXPECT(make_plan(HYBRID_MAX_TOKENS + 1, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
+        EXPECT(make_plan(300, 13, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
+        EXPECT(make_plan(300, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
+        EXPECT(make_plan(20, 5, 7168, 3, 0, pl) == ATTNRES_OK && pl.variant == 3 && pl.split_base == 8);
+        EXPECT(make_plan(15, 5, 7168, 3, 0, pl) == ATTNRES_OK && pl.split_base == 0 && pl.wg_blocks == 0);
+        EXPECT(make_plan(20, 13, 7168, 3, 0, pl) == ATTNRES_EINVAL);
+        EXPECT(make_plan(20, 5, 896, 3, 0, pl) == ATTNRES_EINVAL);
     }
     EXPECT(validate_fwd(nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr, 1e-6f, 0, H, nullptr,
                         nullptr) == ATTNRES_OK);

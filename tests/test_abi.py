@@ -187,7 +187,12 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(1, 2, 896) == (1, 1, 128)       # short rows stay on one workgroup per token
     assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks
     assert ar.attnres_plan(65, 12, 7168)[0] == 1
+    assert ar.attnres_plan(256, 1, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(257, 12, 7168) == (3, 4, 448)   # just past the CU count: the hybrid
+    assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # up to 64 left-over tokens
+    assert ar.attnres_plan(321, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(384, 12, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(300, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
@@ -217,7 +222,8 @@ def test_plan_is_pure_and_sane():
 
 def test_set_variant_validation():
     lib = ar.library()
-    assert lib.attnres_set_variant(3, 0) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(4, 0) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(3, 1) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(1, 3) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(2, 9) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(2, 3) == ar.ATTNRES_EINVAL
@@ -240,6 +246,12 @@ def test_set_variant_validation():
         ar.attnres_set_variant(2, 4)
         with pytest.raises(ar.AttnResError):  # more than 12 only in the 1-2-wave family
             ar.attnres_plan(1, 13, 7168)
+        ar.attnres_set_variant(3, 0)
+        assert ar.attnres_plan(20, 12, 7168) == (3, 4, 448)  # the hybrid, forced at a small M
+        with pytest.raises(ar.AttnResError):  # its split part: one pass of sources
+            ar.attnres_plan(20, 13, 7168)
+        with pytest.raises(ar.AttnResError):  # rows of 513..1024 vectors only
+            ar.attnres_plan(20, 4, 3584)
     finally:
         ar.attnres_set_variant(0, 0)
 

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 # (variant, param): 0 = automatic; W = workgroup per token with param vectors
 # per thread; S = split hidden with param waves per workgroup
-VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7)]
-VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w"]
+VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7), (3, 0)]
+VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w", "hybrid"]
 
 
 def say(*a):
@@ -148,8 +148,10 @@ def test_add2_equals_presummed(ar, variant, M):
 @pytest.mark.parametrize("variant", VARIANTS, ids=VID, indirect=True)
 def test_golden_fold_add(ar, variant):
     rows = pins.read_golden_fold()
-    H = 64
+    H = 64 if variant != (3, 0) else 7168  # the hybrid serves rows of 4104..8192 elements
     M = len(rows)
+    if not supported(ar, M, 0, H):
+        pytest.skip("variant not available for this size")
     prefix = np.array([[r[0]] * H for r in rows], np.uint16)
     add = np.array([[r[1]] * H for r in rows], np.uint16)
     add2_rows = [r for r in rows if r[2] is not None]
@@ -280,6 +282,19 @@ def test_dispatch_boundaries(ar, orc, M, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
 
 
+@pytest.mark.parametrize("N", [0, 1, 3, 4, 7, 8, 12])
+@pytest.mark.parametrize("M", [256, 257, 264, 288, 319, 320, 321])
+def test_hybrid_boundaries(ar, orc, M, N):
+    """Just past the CU count: the automatic dispatch's hybrid launch (kernel W
+    on the first 256 tokens, 4-wave split chunks on the rest) at its bounds,
+    every output element against the oracle."""
+    case = case_for(("hybrid", M, N), lambda: W.make_case(cfg=67, M=M, N=N, add2=(N % 2 == 0)))
+    say("hybrid", M, N, ar.attnres_plan(M, N, case.H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
+
+
 # (M, H, N): kernel W's single-group form (rows of at most 256 vectors, up to
 # 65536 threads per call) on both sides of its bound, ragged short rows, and
 # the split bounds for rows of 257..895 vectors; H = 896 is a tensor-parallel
@@ -390,8 +405,9 @@ def test_in_place_prefix(ar, orc, variant):
 
 # --- determinism, graphs, canaries ---------------------------------------------
 
-SYNC_VARIANTS = [(1, 0), (2, 1), (2, 2), (2, 7)]  # W; split with 1, 2 (gather in every wave), 7 waves (wave 0)
-SYNC_VID = ["W", "S1w", "S2w", "S7w"]
+# W; split with 1, 2 (gather in every wave), 7 waves (wave 0); the hybrid of W and 4-wave chunks
+SYNC_VARIANTS = [(1, 0), (2, 1), (2, 2), (2, 7), (3, 0)]
+SYNC_VID = ["W", "S1w", "S2w", "S7w", "hybrid"]
 
 
 @pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
@@ -473,13 +489,14 @@ def test_graph_replay(ar, variant, N):
     assert ar.attnres_debug_timeouts() == 0
 
 
-@pytest.mark.parametrize("variant", [(1, 0), (2, 0)], ids=["W", "S"], indirect=True)
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0), (3, 0)], ids=["W", "S", "hybrid"], indirect=True)
 def test_canaries(ar, orc, variant):
     """Outputs live inside larger buffers filled with a canary pattern: nothing
     outside [M,H] may change."""
     import torch
 
-    case = W.make_case(cfg=63, M=7, H=1000, N=3, add2=True)
+    case = W.make_case(cfg=63, M=7, H=1000, N=3, add2=True) if variant != (3, 0) else \
+        W.make_case(cfg=63, M=21, H=7176, N=3, add2=True)
     n = case.M * case.H
     pad = 4096
     canary = 0x7E57

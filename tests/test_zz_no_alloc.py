@@ -63,9 +63,11 @@ def out_pair(M, H):
 
 
 # (M, N): split kernel with 4-wave chunks and two exchanges, then a smaller
-# call (2-wave chunks, Gram form), one token, the most tokens and sources the
-# static scratch takes, and a call kernel W serves (no scratch)
-CALLS = [(48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0)]
+# call (2-wave chunks, Gram form), one token, the most sources the split
+# kernel takes, calls kernel W serves (no scratch), and the hybrid of W and
+# split chunks just past the CU count (its split part at the most tokens the
+# automatic dispatch gives it)
+CALLS = [(48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4)]
 
 
 def test_noalloc_matches_fwd(ar, orc):
@@ -90,7 +92,9 @@ def test_noalloc_matches_fwd(ar, orc):
 
 def test_noalloc_rejects_beyond_static_scratch(ar):
     """The split kernel forced on 65 tokens: the allocating entry point serves
-    it (512 slots), the no-allocation one returns ATTNRES_ESCRATCH."""
+    it (512 slots), the no-allocation one (64 slots) returns ATTNRES_ESCRATCH;
+    64 tokens it serves."""
+    assert ar.ATTNRES_NOALLOC_MAX_SPLIT_TOKENS == 64
     case = W.make_case(cfg=86, M=65, N=8, add2=True)
     ar.attnres_set_variant(2, 2)
     try:
