@@ -1019,10 +1019,11 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
         publish(&rec1[chunk * REC_STRIDE + tid], tag1, acc);
     }
 
-    // A3 in every wave (PERWAVE) or in wave 0: lane v < NV adds value v (2s:
-    // sum k_s^2, 2s+1: q.k_s) over the chunks in chunk order, 8 chunks' records
-    // in flight at a time (those not yet tagged read again; bounded wait), so
-    // it holds the same bits in every wave of every workgroup of the token.  A
+    // A3 in every wave (PERWAVE) or in wave 0: lane v < NV ends with value v
+    // (2s: sum k_s^2, 2s+1: q.k_s) summed over the chunks in a fixed order, up
+    // to 16 chunks' records in flight at a time (those not yet tagged read
+    // again; bounded wait), so it holds the same bits in every wave of every
+    // workgroup of the token.  A
     // DPP swap of neighbouring lanes puts q.k_s beside sum k_s^2 in lane 2s,
     // whose logit, the wave's maximum and the exponentials' sum (DPP and
     // scalar reads, fixed order) give alpha_s in lane 2s.
@@ -1031,12 +1032,22 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
     int use_gram = 0;      // Gram form: 1 when it is well-conditioned (same in every workgroup)
     if (PERWAVE || wave == 0) {
         const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
+        // With at most 32 values, lanes v and v + 32 both take value v, from
+        // alternate chunks (c0 + h, c0 + h + 2, ...), so 16 chunks' records are
+        // in flight at once (one round trip for 14 one-wave chunks instead of
+        // two: M = 1, N = 12: 6.32 -> 5.81 us), and the two halves' sums are
+        // added at the end (the same bits in both lanes).
+        constexpr int HALVES = NV <= 32 ? 2 : 1;
+        const int hh = HALVES == 2 ? lane >> 5 : 0;
+        const int vv = HALVES == 2 ? lane & 31 : lane;
         float tv = 0.f;
-        for (int c0 = 0; c0 < C; c0 += 8) {
+        for (int c0 = 0; c0 < C; c0 += 8 * HALVES) {
             unsigned long long r0[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                r0[j] = c0 + j < C && lane < NV ? peek(&rec1[(c0 + j) * REC_STRIDE + lane]) : ready_zero;
+            for (int j = 0; j < 8; ++j) {
+                const int cj = c0 + hh + HALVES * j;
+                r0[j] = cj < C && vv < NV ? peek(&rec1[cj * REC_STRIDE + vv]) : ready_zero;
+            }
             for (unsigned polls = 0;; ++polls) {
                 bool ready = true;
 #pragma unroll
@@ -1056,14 +1067,18 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
                 }
                 __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (c0 + j < C && lane < NV && tag_of(r0[j]) != tag1)
-                        r0[j] = peek(&rec1[(c0 + j) * REC_STRIDE + lane]);
+                for (int j = 0; j < 8; ++j) {
+                    const int cj = c0 + hh + HALVES * j;
+                    if (cj < C && vv < NV && tag_of(r0[j]) != tag1)
+                        r0[j] = peek(&rec1[cj * REC_STRIDE + vv]);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 tv += __uint_as_float((unsigned)r0[j]);
         }
+        if constexpr (HALVES == 2)
+            tv = tv + __shfl_xor(tv, 32);
         float al;
         if constexpr (GRAM) {
             // lane s < S holds q.k_s and fetches G_ss; alpha_s ends in lane s.

@@ -202,21 +202,25 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     if (force_variant == 3)
         return !many && plan_hybrid(M, nvec, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     // Automatic, from per-call times of every variant on MI355X (graph
-    // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168:
-    //  * 2 <= N <= 7, M <= 32: 2-wave chunks, whose Gram form needs one
-    //    exchange (M = 1, N = 4: 4.94 against 5.61 us with two; M = 8, N = 2:
-    //    4.97 against 5.23 for one workgroup per token; M = 1, N = 7: 5.45
-    //    against 5.87);
-    //  * N <= 1 at every M, and N <= 7 above 32 tokens: one workgroup per
-    //    token (at N = 1 the split wins with add2 and loses without it, M = 1:
-    //    4.21 against 4.64 us and 4.37 against 4.30; the dispatch may not
-    //    depend on add2, and the named single-token call has none);
-    //  * N >= 8, the call latency-bound: one token takes 2-wave chunks (their
-    //    exchanges have half as many partners), 2..16 tokens 1-wave chunks
-    //    (spread over the most CUs), up to 24 tokens 2-wave chunks;
-    //  * N >= 8 up to 64 tokens: 4-wave chunks, or 2-wave chunks above 12
-    //    sources (only that family holds them);
-    //  * otherwise one workgroup per token.
+    // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168, one
+    // pass of sources:
+    //  * N >= 8: 1-wave chunks (14 per token, every chunk's records in flight
+    //    at once) up to 32 tokens, 4-wave chunks up to 64 (M = 1, N = 12: 5.49
+    //    against 6.07 us for 2-wave chunks and 9.40 for one workgroup per
+    //    token; M = 16: 6.43 against 7.21; M = 48: 4-wave 7.84 against 1-wave
+    //    8.34);
+    //  * 2 <= N <= 7 (the Gram form's one exchange): 2-wave chunks up to 16
+    //    tokens, up to 32 from N = 4 on, then 4-wave chunks up to 64 (M = 1,
+    //    N = 7: 5.58 against 5.93 for 1-wave chunks, whose 35 values do not fit
+    //    one round of polling; M = 64, N = 7: 7.24 against 7.91 for W; N = 2
+    //    from 24 tokens: W 5.29 against 5.32);
+    //  * N <= 1 at every M: one workgroup per token (at N = 1 the split wins
+    //    with add2 and loses without it, M = 1: 4.21 against 4.64 us and 4.37
+    //    against 4.30; the dispatch may not depend on add2, and the named
+    //    single-token call has none);
+    //  * otherwise one workgroup per token (or the hybrid, below).
+    // More than one pass of sources: 2-wave chunks (the family that holds up
+    // to 31 snapshots) up to 64 tokens, else W's batches.
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
@@ -224,24 +228,26 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //  * H = 3584 / 4096: with N >= 8 and M <= 64 the split still wins
     //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
-    if (!long_rows && !many) {
+    if (many) {
+        if (M <= SPLIT_MID_TOKENS && split_ok && plan_split(M, nvec, 2, pl))
+            return ATTNRES_OK;
+    } else if (!long_rows) {
         if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP) {
             if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
                 return ATTNRES_OK;
             if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
                 return ATTNRES_OK;
         }
-    } else if (long_rows && n >= 2 && n < GRAM_MAX_SOURCES && M <= SPLIT_SMALL_TOKENS_WIDE) {
-        if (plan_split(M, nvec, 2, pl))
+    } else if (n >= GRAM_MAX_SOURCES) {
+        if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
-    } else if (n > 2) {
-        if (!many && M >= 2 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
+        if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;
-        const bool small = M <= SPLIT_SMALL_TOKENS || (n >= 5 && M <= SPLIT_2WAVE_TOKENS) ||
-                           (many && M <= SPLIT_MID_TOKENS);
-        if (small && split_ok && plan_split(M, nvec, 2, pl))
+    } else if (n >= 2) {
+        const bool two_wave = M <= SPLIT_SMALL_TOKENS || (n >= 4 && M <= SPLIT_SMALL_TOKENS_WIDE);
+        if (two_wave && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
-        if (n >= 8 && !many && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
+        if (n >= 4 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;
     }
     // Just past the CU count, kernel W would give some CUs two whole tokens

@@ -14,19 +14,16 @@ constexpr int MAX_SPLIT_SNAP = 31;       // split hidden, 1-2 waves per workgrou
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-// automatic dispatch (see make_plan) at H >= 7168: 2-wave split with one
-// exchange up to SPLIT_SMALL_TOKENS_WIDE tokens for 2 <= N < GRAM_MAX_SOURCES;
-// for more sources a 1-wave split for 2 to SPLIT_SMALL_TOKENS tokens (2-wave
-// for one token), 2-wave up to SPLIT_2WAVE_TOKENS, 4-wave up to
-// SPLIT_MID_TOKENS
+// automatic dispatch (see make_plan) at H >= 7168, one pass of sources:
+// N >= 8: 1-wave split chunks up to SPLIT_SMALL_TOKENS_WIDE tokens, 4-wave up
+// to SPLIT_MID_TOKENS; 2 <= N < GRAM_MAX_SOURCES: 2-wave chunks up to
+// SPLIT_SMALL_TOKENS tokens (up to SPLIT_SMALL_TOKENS_WIDE from N = 4 on),
+// then 4-wave up to SPLIT_MID_TOKENS from N = 4 on
 constexpr int SPLIT_SMALL_TOKENS = 16;
-constexpr int SPLIT_2WAVE_TOKENS = 24;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_MID_TOKENS = 64;
 // The split kernel's Gram form (one exchange instead of two) serves up to
-// GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).  With it, 2-wave
-// chunks win for 2 <= N <= GRAM_MAX_SOURCES - 1 up to SPLIT_SMALL_TOKENS_WIDE
-// tokens (rows of LONG_ROW_VECTORS and more).
+// GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).
 constexpr int GRAM_MAX_SOURCES = 8;
 // Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one
 // workgroup per token at every M and N <= 12; rows shorter than

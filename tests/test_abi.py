@@ -164,22 +164,27 @@ def test_bf16_add_validation():
 
 def test_plan_is_pure_and_sane():
     # the measured automatic dispatch at H = 7168
-    assert ar.attnres_plan(1, 12, 7168) == (2, 7, 128)     # one token: 2-wave chunks
-    assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # N <= 7, M <= 32: 2-wave chunks (one exchange)
+    assert ar.attnres_plan(1, 12, 7168) == (2, 14, 64)     # N >= 8: 1-wave chunks up to 32 tokens
+    assert ar.attnres_plan(2, 8, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(8, 12, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(24, 12, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(32, 8, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(33, 8, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
+    assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # 2 <= N <= 7: 2-wave chunks (one exchange)
     assert ar.attnres_plan(16, 4, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 6, 7168)[0] == 1
+    assert ar.attnres_plan(16, 3, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(17, 3, 7168)[0] == 1            # N < 4: up to 16 tokens
+    assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)     # N >= 4: up to 32 tokens
+    assert ar.attnres_plan(33, 6, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
     assert ar.attnres_plan(2, 7, 7168) == (2, 7, 128)
     assert ar.attnres_plan(32, 7, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 7, 7168)[0] == 1
-    assert ar.attnres_plan(2, 8, 7168) == (2, 14, 64)      # N >= 8, 2..16 tokens: 1-wave chunks
-    assert ar.attnres_plan(8, 12, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(24, 12, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(33, 7, 7168) == (2, 4, 256)
+    assert ar.attnres_plan(64, 7, 7168) == (2, 4, 256)
+    assert ar.attnres_plan(65, 7, 7168)[0] == 1
     assert ar.attnres_plan(32, 5, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(32, 8, 7168) == (2, 4, 256)
     assert ar.attnres_plan(16, 13, 7168) == (2, 7, 128)    # above 12 sources: 2-wave family
     assert ar.attnres_plan(32, 4, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 4, 7168)[0] == 1
+    assert ar.attnres_plan(33, 4, 7168) == (2, 4, 256)
     assert ar.attnres_plan(1, 2, 7168) == (2, 7, 128)
     assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
     assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)

@@ -267,14 +267,15 @@ def test_shapes(ar, orc, variant, M, H, N):
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 6, 7, 8, 12])
-@pytest.mark.parametrize("M", [2, 16, 17, 24, 25, 32, 33, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 16, 17, 24, 32, 33, 48, 64, 65])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
-    (2-wave chunks with one exchange up to 32 tokens for 2 <= N <= 7; 1-wave chunks
-    up to 16 tokens, 2-wave up to 24 or 32, 4-wave up to 64, then a workgroup
-    per token) and source-count bounds (the split kernel's single-exchange form
-    up to seven snapshots; one group of up to four sources in kernel W; the store
-    policy changes at nine sources)."""
+    (for N >= 8 1-wave chunks up to 32 tokens, then 4-wave up to 64; for
+    2 <= N <= 7, the one-exchange form, 2-wave chunks up to 16 tokens, up to 32
+    from N = 4, then 4-wave up to 64; then a workgroup per token) and
+    source-count bounds (the split kernel's single-exchange form up to seven
+    snapshots, and the halved polling of up to 32 values; one group of up to
+    four sources in kernel W)."""
     case = case_for(("bound", M, N), lambda: W.make_case(cfg=62, M=M, N=N, add2=(M % 2 == 0)))
     say("boundary", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)
