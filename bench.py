@@ -585,7 +585,7 @@ def fold_suite(launcher, cold_bytes=1.1e9):
     return out
 
 
-def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), Ns=(0, 1, 2, 4, 8, 12),
+def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 288, 320, 384, 512, 1024), Ns=(0, 1, 2, 4, 8, 12),
                H=7168, cold_bytes=1.1e9, max_sets=20000):
     """The metric over a grid of token and source counts (add2, automatic
     dispatch): µs per call with inputs cold in HBM (graph replay of one launch
@@ -610,7 +610,7 @@ def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024), Ns=(0
             row = {"M": M, "N": N, "H": H, "us_per_call": round(us, 3),
                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                    "frac": round(nbytes / (us * 1e-6) / 8e12, 4),
-                   "kernel": "W" if plan[0] == 1 else "S%dw" % (plan[2] // 64)}
+                   "kernel": {1: "W", 3: "hybrid"}.get(plan[0], "S%dw" % (plan[2] // 64))}
             log("grid %s" % row)
             out.append(row)
             del pool, sets, args
