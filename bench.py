@@ -686,7 +686,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--micro-batches", type=int, default=16)
-    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy", "latency", "grid"], default="full",
+    ap.add_argument("--mode", choices=["full", "chain", "eager", "copy", "latency", "grid", "single"], default="full",
                     help="full: everything; chain: the timed chain only (for kernel-trace "
                          "profiling); eager: --steps eager steps of the chain, no graph and no "
                          "timing (for counter collection); copy: a plain 1 GiB device copy, the "
@@ -694,7 +694,8 @@ def main():
                          "then only the small named calls and the per-config fold comparison "
                          "(for kernel-trace profiling of the latency workloads); grid: the parity "
                          "gate, then µs per call and GB/s over a grid of token and source counts, "
-                         "at H=7168 and at one tensor-parallel rank's share of it (H=896)")
+                         "at H=7168 and at one tensor-parallel rank's share of it (H=896); single: "
+                         "the parity gate, then µs per call of one token at N = 1..12 (H=7168)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     args = ap.parse_args()
@@ -736,6 +737,12 @@ def main():
         # the full hidden size, then one tensor-parallel rank's share of it (7168 / 8 columns)
         res = {"mode": "grid", "grid": grid_suite(launcher),
                "tp8_share": grid_suite(launcher, Ms=(1, 8, 16, 32, 256), Ns=(4, 12), H=896)}
+        assert launcher.ar.attnres_debug_timeouts() == 0
+        print(json.dumps(res))
+        return
+
+    if args.mode == "single":
+        res = {"mode": "single", "single_token": grid_suite(launcher, Ms=(1,), Ns=tuple(range(1, 13)))}
         assert launcher.ar.attnres_debug_timeouts() == 0
         print(json.dumps(res))
         return
