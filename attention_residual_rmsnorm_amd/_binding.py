@@ -75,6 +75,8 @@ def library():
         lib.attnres_debug_reset_scratch.restype = ctypes.c_int
         lib.attnres_debug_set_epoch.argtypes = [ctypes.c_uint]
         lib.attnres_debug_set_epoch.restype = ctypes.c_int
+        lib.attnres_debug_set_exchange.argtypes = [ctypes.c_int]
+        lib.attnres_debug_set_exchange.restype = ctypes.c_int
         lib.attnres_selftest_rounding.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
         lib.attnres_selftest_rounding.restype = ctypes.c_int
         lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -256,6 +258,10 @@ def attnres_debug_timeouts() -> int:
 
 def attnres_debug_set_spin_limit(limit: int = 0) -> None:
     _check(library().attnres_debug_set_spin_limit(limit), "attnres_debug_set_spin_limit")
+
+
+def attnres_debug_set_exchange(mode: int = 0) -> None:
+    _check(library().attnres_debug_set_exchange(mode), "attnres_debug_set_exchange")
 
 
 def attnres_debug_reset_scratch() -> None:

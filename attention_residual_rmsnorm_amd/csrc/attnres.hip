@@ -52,6 +52,14 @@
 namespace attnres {
 
 constexpr int REC_STRIDE = 64;           // records per (token, chunk) of the first exchange (>= 2*32)
+// Each record has two copies (see publish): per (token, chunk), the first
+// exchange's L2 copies are records [0, REC_STRIDE) and the device-scope copies
+// [REC_STRIDE, 2 REC_STRIDE); per token, the second exchange's are [0,
+// MAX_CHUNKS) and [MAX_CHUNKS, 2 MAX_CHUNKS).
+constexpr int REC1_CHUNK = 2 * REC_STRIDE;
+constexpr int REC2_SLOT = 2 * MAX_CHUNKS;
+// re-polls of a record's L2 copy before its device-scope copy is read instead
+constexpr unsigned L2_POLLS = 64;
 constexpr int STATE_STRIDE = 32;         // epoch word per token: one 128-byte line each
 constexpr unsigned SPIN_LIMIT = 1u << 20;
 // Kernel S with at most GRAM_MAX_SOURCES sources (attnres_host.hpp) takes one
@@ -83,11 +91,13 @@ struct Params {
     int64_t split_base;       // split hidden: first token it serves (the hybrid's W part takes [0, split_base))
     int split_threads;        // split hidden: threads per chunk (the workgroup's others exit at once)
     int wg_blocks;            // hybrid: workgroups of its W part
-    unsigned long long* rec1; // split hidden: [token slot][MAX_CHUNKS][REC_STRIDE] tagged A2 partials
-    unsigned long long* rec2; // split hidden: [token][MAX_CHUNKS] tagged chunk sums of x^2
+    unsigned long long* rec1; // split hidden: [token slot][MAX_CHUNKS][REC1_CHUNK] tagged A2 partials
+    unsigned long long* rec2; // split hidden: [token][REC2_SLOT] tagged chunk sums of x^2
     unsigned* state;          // split hidden: [token][STATE_STRIDE] epoch word (index 0)
     unsigned* timeouts;       // split hidden: exchange waits that gave up
     unsigned spin_limit;
+    unsigned l2_polls;        // split hidden: re-polls of the L2 copies (0: device-scope copies only)
+    int xcd_skew;             // split hidden: 1 places a token's chunks on different XCDs (tests only)
 };
 
 // A 16-byte load with the non-temporal hint, for the [M,H] streams: a decode
@@ -880,12 +890,13 @@ __device__ __forceinline__ unsigned long long gave_up(unsigned tag)
 
 __device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t slot, int C)
 {
-    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC_STRIDE;
-    unsigned long long* rec2 = p.rec2 + (size_t)slot * MAX_CHUNKS;
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
+    unsigned long long* rec2 = p.rec2 + (size_t)slot * REC2_SLOT;
     for (int c = C; c < MAX_CHUNKS; ++c) {
-        for (int v = 0; v < REC_STRIDE; ++v)
-            __hip_atomic_store(&rec1[c * REC_STRIDE + v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int v = 0; v < REC1_CHUNK; ++v) // both copies
+            __hip_atomic_store(&rec1[c * REC1_CHUNK + v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&rec2[c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&rec2[MAX_CHUNKS + c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -901,8 +912,12 @@ __device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, 
 // Kernel S: split hidden.  blockDim.x threads per workgroup, one 16-byte vector
 // each; C = p.chunks workgroups per token, chunk c owning vectors
 // [c*blockDim.x, (c+1)*blockDim.x).  Workgroup b serves token (b/8/C)*8 + b%8,
-// chunk (b/8)%C, so every chunk of a token has the same b mod 8 (the XCD the
-// dispatcher assigns it to); grid = 8*C*ceil(M/8) and workgroups past the last
+// chunk (b/8)%C, so every chunk of a token has the same b mod 8, hence the
+// same XCD: the dispatcher deals workgroups to the XCDs in turn, so the
+// records' L2 copies reach the token's other chunks (Params::xcd_skew, for
+// tests only, adds the chunk index to b mod 8 instead, which spreads a
+// token's chunks over several XCDs and makes the readers fall back to the
+// device-scope copies); grid = 8*C*ceil(M/8) and workgroups past the last
 // token exit at once.
 //
 // Exchanges (see attnres_device.hpp): the call's epoch E is read from the
@@ -957,9 +972,9 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
     const int nw = nthreads >> 6;
     const int C = p.chunks;
     const int ib = b >> 3;
-    const int64_t slot = (int64_t)(ib / C) * 8 + (b & 7);
-    const int64_t t = p.split_base + slot;
     const int chunk = ib - (ib / C) * C;
+    const int64_t slot = (int64_t)(ib / C) * 8 + ((b + p.xcd_skew * chunk) & 7);
+    const int64_t t = p.split_base + slot;
     if (t >= p.M)
         return;
 
@@ -1002,7 +1017,7 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
                                4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
     }
     __syncthreads();
-    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC_STRIDE;
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
     if (tid < NV) { // rows in order, loaded 8 at a time so the loads overlap
         const int nrows = nthreads >> 4;
         float acc = rows[tid];
@@ -1016,7 +1031,7 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
                 if (r0 + r < nrows)
                     acc += vr[r];
         }
-        publish(&rec1[chunk * REC_STRIDE + tid], tag1, acc);
+        publish(&rec1[chunk * REC1_CHUNK + tid], REC_STRIDE, tag1, acc);
     }
 
     // A3 in every wave (PERWAVE) or in wave 0: lane v < NV ends with value v
@@ -1043,10 +1058,11 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
         float tv = 0.f;
         for (int c0 = 0; c0 < C; c0 += 8 * HALVES) {
             unsigned long long r0[8];
+            int off = p.l2_polls ? 0 : REC_STRIDE; // the L2 copies first (see publish)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int cj = c0 + hh + HALVES * j;
-                r0[j] = cj < C && vv < NV ? peek(&rec1[cj * REC_STRIDE + vv]) : ready_zero;
+                r0[j] = cj < C && vv < NV ? peek(&rec1[cj * REC1_CHUNK + off + vv]) : ready_zero;
             }
             for (unsigned polls = 0;; ++polls) {
                 bool ready = true;
@@ -1065,12 +1081,14 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
                             r0[j] = gave_up(tag1);
                     break;
                 }
+                if (polls >= p.l2_polls)
+                    off = REC_STRIDE; // then the device-scope copies
                 __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int cj = c0 + hh + HALVES * j;
                     if (cj < C && vv < NV && tag_of(r0[j]) != tag1)
-                        r0[j] = peek(&rec1[cj * REC_STRIDE + vv]);
+                        r0[j] = peek(&rec1[cj * REC1_CHUNK + off + vv]);
                 }
             }
 #pragma unroll
@@ -1164,23 +1182,26 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
         // A5: the chunk's sum of x^2 (its waves in order) published by thread 0;
         // every wave (PERWAVE) or wave 0 reads the C records (lane c: chunk c) and
         // adds them on DPP
-        unsigned long long* rec2 = p.rec2 + (size_t)slot * MAX_CHUNKS;
+        unsigned long long* rec2 = p.rec2 + (size_t)slot * REC2_SLOT;
         if (tid == 0) {
             float s2 = red2[0];
             for (int w = 1; w < nw; ++w)
                 s2 += red2[w];
-            publish(&rec2[chunk], tag2, s2);
+            publish(&rec2[chunk], MAX_CHUNKS, tag2, s2);
         }
         if (PERWAVE || wave == 0) {
-            unsigned long long w2 = lane < C ? peek(&rec2[lane]) : (unsigned long long)tag2 << 32;
+            int off = p.l2_polls ? 0 : MAX_CHUNKS; // the L2 copies first, as above
+            unsigned long long w2 = lane < C ? peek(&rec2[off + lane]) : (unsigned long long)tag2 << 32;
             for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
                 if (polls >= p.spin_limit) {
                     atomicAdd(p.timeouts, 1u); // give up: the sum, hence this wave's outputs, is NaN
                     w2 = gave_up(tag2);
                     break;
                 }
+                if (polls >= p.l2_polls)
+                    off = MAX_CHUNKS;
                 __builtin_amdgcn_s_sleep(1);
-                w2 = peek(&rec2[lane]);
+                w2 = peek(&rec2[off + lane]);
             }
             ssum = wave_sum(__uint_as_float((unsigned)w2));
             if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
@@ -1326,10 +1347,12 @@ Scratch g_scratch[MAX_DEVICES];              // written once per device, under g
 std::atomic<bool> g_ready[MAX_DEVICES];      // published after g_scratch[dev] is complete
 int g_force_variant = 0;
 unsigned g_spin_limit = SPIN_LIMIT;
+unsigned g_l2_polls = L2_POLLS;
+int g_xcd_skew = 0;
 int g_force_param = 0;
 
-constexpr size_t REC1_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS * REC_STRIDE;
-constexpr size_t REC2_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS;
+constexpr size_t REC1_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * MAX_CHUNKS * REC1_CHUNK;
+constexpr size_t REC2_BYTES = sizeof(unsigned long long) * MAX_SPLIT_TOKENS * REC2_SLOT;
 constexpr size_t STATE_BYTES = sizeof(unsigned) * MAX_SPLIT_TOKENS * STATE_STRIDE;
 constexpr size_t SCRATCH_BYTES = REC1_BYTES + REC2_BYTES + STATE_BYTES + 256;
 
@@ -1385,16 +1408,16 @@ int scratch_for_current_device(Scratch** out)
 // ---------------------------------------------------------------------------
 // The scratch of attnres_add_rmsnorm_fwd_noalloc: a file-scope device array,
 // so that entry point never allocates.  Same layout as the allocated scratch
-// (records [token][MAX_CHUNKS][REC_STRIDE], [token][MAX_CHUNKS], epoch words
+// (records [token][MAX_CHUNKS][REC1_CHUNK], [token][REC2_SLOT], epoch words
 // [token][STATE_STRIDE], the timeout counter) for STATIC_SPLIT_TOKENS token
 // slots: every call the automatic dispatch makes fits (the split kernel takes
-// at most 64 tokens, the hybrid's split part at most 64).  Each device holds its own copy, at its own address, for
-// the life of the process.  In host code `scratch` names a host-side stand-in,
+// at most 64 tokens, the hybrid's split part at most 64).  Each device holds
+// its own copy, at its own address, for the life of the process.  In host code `scratch` names a host-side stand-in,
 // not device memory: host code uses only the address hipGetSymbolAddress
 // returns for the current device (g_static below).
 constexpr int STATIC_SPLIT_TOKENS = 64;
-constexpr size_t STATIC_REC1_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS * REC_STRIDE;
-constexpr size_t STATIC_REC2_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS;
+constexpr size_t STATIC_REC1_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS * REC1_CHUNK;
+constexpr size_t STATIC_REC2_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * REC2_SLOT;
 constexpr size_t STATIC_STATE_BYTES = sizeof(unsigned) * STATIC_SPLIT_TOKENS * STATE_STRIDE;
 constexpr size_t STATIC_SCRATCH_BYTES = STATIC_REC1_BYTES + STATIC_REC2_BYTES + STATIC_STATE_BYTES + 256;
 static_assert(STATIC_SCRATCH_BYTES % 16 == 0, "cleared in 16-byte vectors");
@@ -1511,6 +1534,8 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.split_threads = pl.variant == 3 ? pl.split_threads : pl.threads;
     p.wg_blocks = pl.wg_blocks;
     p.spin_limit = g_spin_limit;
+    p.l2_polls = g_l2_polls;
+    p.xcd_skew = g_xcd_skew;
 
     const int a2 = add2 ? 1 : 0;
     if (n_snapshots > MAX_SNAP && pl.variant == 1) {
@@ -1657,6 +1682,15 @@ extern "C" int attnres_debug_timeouts(unsigned* out)
 extern "C" int attnres_debug_set_spin_limit(unsigned limit)
 {
     g_spin_limit = limit ? limit : SPIN_LIMIT;
+    return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_set_exchange(int mode)
+{
+    if (mode < 0 || mode > 2)
+        return ATTNRES_EINVAL;
+    g_l2_polls = mode == 1 ? 0u : L2_POLLS;
+    g_xcd_skew = mode == 2 ? 1 : 0;
     return ATTNRES_OK;
 }
 

@@ -133,19 +133,32 @@ __device__ __forceinline__ float wave_max(float v)
 //
 // Workgroups that share a token exchange binary32 partial sums through 64-bit
 // records: the upper word is a tag, the lower word the value.  A record is
-// written and read with single relaxed device-scope atomics, so a reader that
-// sees the expected tag also sees that call's value: no fence (and none of the
-// whole-cache writeback/invalidate that device-scope release/acquire costs on
-// gfx950) is needed.  Tags come from a per-token epoch word that advances once
-// per call (see fwd_split), so records left by earlier calls never match: tag
-// 0 (a record never written) is never expected, and the call that wraps the
-// epoch clears the records of every chunk index it does not use (see
-// advance_epoch).
+// written with single 8-byte atomic stores and read with relaxed device-scope
+// atomic loads, so a reader that sees the expected tag also sees that call's
+// value: no fence (and none of the whole-cache writeback/invalidate that
+// device-scope release/acquire costs on gfx950) is needed.  Tags come from a
+// per-token epoch word that advances once per call (see fwd_split), so records
+// left by earlier calls never match: tag 0 (a record never written) is never
+// expected, and the call that wraps the epoch clears the records of every
+// chunk index it does not use (see advance_epoch).
+//
+// Every record is written twice.  The first copy, at `rec`, takes a
+// workgroup-scope store: it goes no further than the L2 of the writer's XCD,
+// where the device-scope loads of the other CUs of that XCD see it (one hop
+// of about 190 ns on an idle device against 292 for a device-scope store, and
+// it does not queue behind the whole chip's memory traffic when the other CUs
+// stream).  The second, at rec + dev_off, takes a device-scope store and is
+// seen from every XCD.  Readers poll the first copy for a bounded number of
+// re-polls, then the second (see fwd_split): the chunks of a token are placed
+// on one XCD, so the first copy is the one that arrives, but the result never
+// depends on where the workgroups run, since a record with the expected tag
+// is taken from either copy and both hold the same bits.
 
-__device__ __forceinline__ void publish(unsigned long long* rec, unsigned tag, float v)
+__device__ __forceinline__ void publish(unsigned long long* rec, int dev_off, unsigned tag, float v)
 {
     const unsigned long long w = ((unsigned long long)tag << 32) | __float_as_uint(v);
-    __hip_atomic_store(rec, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(rec, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(rec + dev_off, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ unsigned long long peek(const unsigned long long* rec)

@@ -111,7 +111,7 @@ extern "C" {
  * All device pointers must be 16-byte aligned.  The caller owns every buffer
  * and must keep it alive until the stream work completes.  The library owns a
  * per-device scratch buffer used by the split-hidden kernel (tagged partial
- * records and one epoch word per token slot, 8.6 MB; nothing needs clearing
+ * records and one epoch word per token slot, 17 MB; nothing needs clearing
  * between calls, HIP-graph replays included).  attnres_init() allocates it;
  * the call itself never allocates or synchronises, and returns
  * ATTNRES_ENOINIT (launching nothing) on a device where attnres_init() has
@@ -159,7 +159,7 @@ int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void*
  * cannot allocate device memory: code under HIP-graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  It allocates nothing and needs no
  * attnres_init(): the split-hidden kernel's scratch is a static device array
- * of the library (about 1.05 MB per device, held until the process ends),
+ * of the library (about 2.1 MB per device, held until the process ends),
  * with ATTNRES_NOALLOC_MAX_SPLIT_TOKENS token slots.
  *
  * Arguments, accuracy, dispatch and results are those of
@@ -255,6 +255,20 @@ int attnres_debug_timeouts(unsigned* out);
  * Returns ATTNRES_OK.
  */
 int attnres_debug_set_spin_limit(unsigned limit);
+
+/*
+ * attnres_debug_set_exchange -- diagnostic, for tests of the split-hidden
+ * kernel's exchange: mode 0 (the default) reads the records' L2 copies first
+ * (the copy the other workgroups of a token, placed on one XCD, see at once)
+ * and their device-scope copies after a bounded number of re-polls; mode 1
+ * reads the device-scope copies only; mode 2 reads as mode 0 but places the
+ * chunks of a token on different XCDs, so that the L2 copies are not seen and
+ * every wait falls back to the device-scope copies.  Outputs are the same bits
+ * in every mode; modes 1 and 2 are slower.  Applies to later launches,
+ * process-wide.  Not thread-safe with concurrent calls.  Returns ATTNRES_OK
+ * or ATTNRES_EINVAL (mode outside 0..2).
+ */
+int attnres_debug_set_exchange(int mode);
 
 /*
  * attnres_debug_reset_scratch -- diagnostic: clears the split-hidden scratch of

@@ -225,6 +225,14 @@ def test_plan_is_pure_and_sane():
         ar.attnres_plan(1, 4, 7170)
 
 
+def test_set_exchange_validation():
+    lib = ctypes.CDLL(ar.library_path)
+    for mode in (0, 1, 2, 0):
+        assert lib.attnres_debug_set_exchange(mode) == ar.ATTNRES_OK
+    assert lib.attnres_debug_set_exchange(3) == ar.ATTNRES_EINVAL
+    assert lib.attnres_debug_set_exchange(-1) == ar.ATTNRES_EINVAL
+
+
 def test_set_variant_validation():
     lib = ar.library()
     assert lib.attnres_set_variant(4, 0) == ar.ATTNRES_EINVAL

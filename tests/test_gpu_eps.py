@@ -138,7 +138,8 @@ def test_eps_gram_fallback(ar, orc, variant, eps):
 
 
 @pytest.mark.parametrize("eps", EPS)
-@pytest.mark.parametrize("M,N", [(256, 12), (40, 12), (1, 12), (32, 3), (256, 1), (300, 12), (300, 3)])
+@pytest.mark.parametrize("M,N", [(256, 12), (40, 12), (1, 12), (32, 3), (256, 1), (300, 12), (300, 3),
+                                 (270, 12), (350, 12), (350, 5)])
 def test_eps_auto_dispatch(ar, orc, M, N, eps):
     """The automatic dispatch at the named token and source counts."""
     case = eps_case(M, N, eps, seed=1)

@@ -284,11 +284,12 @@ def test_dispatch_boundaries(ar, orc, M, N):
 
 
 @pytest.mark.parametrize("N", [0, 1, 3, 4, 7, 8, 12])
-@pytest.mark.parametrize("M", [256, 257, 264, 288, 319, 320, 321])
+@pytest.mark.parametrize("M", [256, 257, 264, 288, 289, 319, 320, 321, 352, 383, 384, 385, 511])
 def test_hybrid_boundaries(ar, orc, M, N):
-    """Just past the CU count: the automatic dispatch's hybrid launch (kernel W
-    on the first 256 tokens, 4-wave split chunks on the rest) at its bounds,
-    every output element against the oracle."""
+    """Past the CU count: the automatic dispatch's hybrid launch (kernel W on
+    the first 256 tokens, 4-wave split chunks on the rest) at its bounds, and
+    kernel W beyond it (two tokens on some CUs), every output element against
+    the oracle."""
     case = case_for(("hybrid", M, N), lambda: W.make_case(cfg=67, M=M, N=N, add2=(N % 2 == 0)))
     say("hybrid", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)
@@ -561,6 +562,44 @@ def test_bounded_waits_give_up(ar, orc):
         gp, gn = P.run_gpu(case)
         rp, rn = P.run_oracle(orc, case)
         P.assert_parity(gp, gn, rp, rn, "after the reset")
+    assert ar.attnres_debug_timeouts() == 0
+
+
+# (forced variant, case): kernel S's two exchanges (1 and 7 waves per chunk),
+# its Gram form, the automatic single-token call (14 one-wave chunks), and the
+# hybrid's split part
+EXCHANGE_CASES = [((2, 1), "cfg4"), ((2, 7), "cfg4"), ((2, 2), "cfg2"), ((0, 0), "cfg4b"), ((3, 0), "hybrid21")]
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["device-copies", "chunks-on-other-XCDs"])
+def test_exchange_copies(ar, orc, mode):
+    """The exchange's two copies of every record: the device-scope copies read
+    alone (mode 1), and the chunks of each token placed on different XCDs, so
+    that their L2 copies stay unseen and every wait falls back to the
+    device-scope copies (mode 2).  Each call against the default mode's bits
+    and against the oracle, with no wait given up."""
+    import torch
+
+    for variant, name in EXCHANGE_CASES:
+        if name == "hybrid21":
+            case = case_for(name, lambda: W.make_case(cfg=68, M=21, H=7176, N=12, add2=True))
+        else:
+            case = case_for(name, lambda: W.config_case(name))
+        ar.attnres_set_variant(*variant)
+        try:
+            say("exchange mode", mode, variant, name, ar.attnres_plan(case.M, case.N, case.H))
+            ep, en = P.run_gpu(case)
+            ar.attnres_debug_set_exchange(mode)
+            try:
+                gp, gn = P.run_gpu(case)
+                torch.cuda.synchronize()
+            finally:
+                ar.attnres_debug_set_exchange(0)
+        finally:
+            ar.attnres_set_variant(0, 0)
+        assert np.array_equal(gp, ep) and np.array_equal(gn, en), "%s %s: modes differ" % (variant, name)
+        rp, rn = P.run_oracle(orc, case)
+        P.assert_parity(gp, gn, rp, rn, "mode %d %s %s" % (mode, variant, name))
     assert ar.attnres_debug_timeouts() == 0
 
 
