@@ -12,7 +12,7 @@ ATTNRES_EALIAS = -3
 ATTNRES_EHIP = -4
 ATTNRES_ENOINIT = -5
 ATTNRES_ESCRATCH = -6
-ATTNRES_NOALLOC_MAX_SPLIT_TOKENS = 64
+ATTNRES_NOALLOC_MAX_SPLIT_TOKENS = 96
 ATTNRES_MAX_SNAPSHOTS = 64
 ATTNRES_MAX_HIDDEN = 16384
 

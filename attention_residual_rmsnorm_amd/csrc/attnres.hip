@@ -1411,11 +1411,15 @@ int scratch_for_current_device(Scratch** out)
 // (records [token][MAX_CHUNKS][REC1_CHUNK], [token][REC2_SLOT], epoch words
 // [token][STATE_STRIDE], the timeout counter) for STATIC_SPLIT_TOKENS token
 // slots: every call the automatic dispatch makes fits (the split kernel takes
-// at most 64 tokens, the hybrid's split part at most 64).  Each device holds
-// its own copy, at its own address, for the life of the process.  In host code `scratch` names a host-side stand-in,
+// at most SPLIT_WIDE_TOKENS tokens, the hybrid's split part at most
+// HYBRID_MAX_TOKENS - HYBRID_WG_TOKENS).  Each device holds its own copy, at
+// its own address, for the life of the process.  In host code `scratch` names a host-side stand-in,
 // not device memory: host code uses only the address hipGetSymbolAddress
 // returns for the current device (g_static below).
-constexpr int STATIC_SPLIT_TOKENS = 64;
+constexpr int STATIC_SPLIT_TOKENS = 96;
+static_assert(STATIC_SPLIT_TOKENS >= SPLIT_WIDE_TOKENS && STATIC_SPLIT_TOKENS >= SPLIT_MID_TOKENS &&
+                  STATIC_SPLIT_TOKENS >= HYBRID_MAX_TOKENS - HYBRID_WG_TOKENS,
+              "every automatic plan fits the static scratch");
 constexpr size_t STATIC_REC1_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * MAX_CHUNKS * REC1_CHUNK;
 constexpr size_t STATIC_REC2_BYTES = sizeof(unsigned long long) * STATIC_SPLIT_TOKENS * REC2_SLOT;
 constexpr size_t STATIC_STATE_BYTES = sizeof(unsigned) * STATIC_SPLIT_TOKENS * STATE_STRIDE;
@@ -1736,7 +1740,7 @@ extern "C" const char* attnres_status_string(int status)
     case ATTNRES_EHIP: return "HIP error";
     case ATTNRES_ENOINIT: return "attnres_init() has not run on the current device";
     case ATTNRES_ESCRATCH:
-        return "the call needs more than the static scratch holds (split-hidden kernel for more than 64 tokens)";
+        return "the call needs more than the static scratch holds (split-hidden kernel for more than 96 tokens)";
     default: return "unknown status";
     }
 }

@@ -205,10 +205,13 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168, one
     // pass of sources:
     //  * N >= 8: 1-wave chunks (14 per token, every chunk's records in flight
-    //    at once) up to 32 tokens, 4-wave chunks up to 64 (M = 1, N = 12: 5.49
-    //    against 6.07 us for 2-wave chunks and 9.40 for one workgroup per
-    //    token; M = 16: 6.43 against 7.21; M = 48: 4-wave 7.84 against 1-wave
-    //    8.34);
+    //    at once) up to 48 tokens, 4-wave chunks up to 64, 2-wave chunks up to
+    //    96 (M = 1, N = 12: 5.49 against 6.07 us for 2-wave chunks and 9.40
+    //    for one workgroup per token; M = 16: 6.43 against 7.21; M = 48: 7.48
+    //    against 7.67 for 4-wave chunks; M = 64: 4-wave 7.96 against 8.64 for
+    //    2-wave; M = 80 and 96: 2-wave 9.15 and 9.54 against 10.13 and 10.35
+    //    for W, N = 8 7.97 and 8.14 against 8.26 and 8.50; from 112 tokens
+    //    within 0.1-0.4 us of W);
     //  * 2 <= N <= 7 (the Gram form's one exchange): 2-wave chunks up to 16
     //    tokens, up to 32 from N = 4 on, then 4-wave chunks up to 64 (M = 1,
     //    N = 7: 5.58 against 5.93 for 1-wave chunks, whose 35 values do not fit
@@ -239,9 +242,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
                 return ATTNRES_OK;
         }
     } else if (n >= GRAM_MAX_SOURCES) {
-        if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
+        if (M <= SPLIT_ONE_WAVE_TOKENS && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
         if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
+            return ATTNRES_OK;
+        if (M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
     } else if (n >= 2) {
         const bool two_wave = M <= SPLIT_SMALL_TOKENS || (n >= 4 && M <= SPLIT_SMALL_TOKENS_WIDE);

@@ -15,13 +15,16 @@ constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
 // automatic dispatch (see make_plan) at H >= 7168, one pass of sources:
-// N >= 8: 1-wave split chunks up to SPLIT_SMALL_TOKENS_WIDE tokens, 4-wave up
-// to SPLIT_MID_TOKENS; 2 <= N < GRAM_MAX_SOURCES: 2-wave chunks up to
-// SPLIT_SMALL_TOKENS tokens (up to SPLIT_SMALL_TOKENS_WIDE from N = 4 on),
-// then 4-wave up to SPLIT_MID_TOKENS from N = 4 on
+// N >= 8: 1-wave split chunks up to SPLIT_ONE_WAVE_TOKENS tokens, 4-wave up
+// to SPLIT_MID_TOKENS, 2-wave up to SPLIT_WIDE_TOKENS; 2 <= N <
+// GRAM_MAX_SOURCES: 2-wave chunks up to SPLIT_SMALL_TOKENS tokens (up to
+// SPLIT_SMALL_TOKENS_WIDE from N = 4 on), then 4-wave up to SPLIT_MID_TOKENS
+// from N = 4 on
 constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
+constexpr int SPLIT_ONE_WAVE_TOKENS = 48;
 constexpr int SPLIT_MID_TOKENS = 64;
+constexpr int SPLIT_WIDE_TOKENS = 96;
 // The split kernel's Gram form (one exchange instead of two) serves up to
 // GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).
 constexpr int GRAM_MAX_SOURCES = 8;

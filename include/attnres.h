@@ -81,7 +81,7 @@ extern "C" {
                                     up to 31 at once), so the page's N > 12 fallback is
                                     not needed below 65 */
 #define ATTNRES_MAX_HIDDEN 16384
-#define ATTNRES_NOALLOC_MAX_SPLIT_TOKENS 64 /* token slots of the no-allocation scratch */
+#define ATTNRES_NOALLOC_MAX_SPLIT_TOKENS 96 /* token slots of the no-allocation scratch */
 
 /*
  * attnres_add_rmsnorm_fwd -- the fused decode step described above.
@@ -159,14 +159,14 @@ int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void*
  * cannot allocate device memory: code under HIP-graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  It allocates nothing and needs no
  * attnres_init(): the split-hidden kernel's scratch is a static device array
- * of the library (about 2.1 MB per device, held until the process ends),
+ * of the library (about 3.2 MB per device, held until the process ends),
  * with ATTNRES_NOALLOC_MAX_SPLIT_TOKENS token slots.
  *
  * Arguments, accuracy, dispatch and results are those of
  * attnres_add_rmsnorm_fwd (the same kernels, bit for bit the same outputs).
  * A call whose sizes give the split-hidden kernel more than
  * ATTNRES_NOALLOC_MAX_SPLIT_TOKENS tokens (only possible through
- * attnres_set_variant: the automatic dispatch splits at most 64) returns
+ * attnres_set_variant: the automatic dispatch splits at most 96) returns
  * ATTNRES_ESCRATCH and launches nothing.  The first call on a device
  * that uses the static scratch looks up its address (hipGetSymbolAddress; no
  * allocation, no synchronisation) and enqueues one kernel on `stream` that

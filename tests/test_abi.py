@@ -164,12 +164,17 @@ def test_bf16_add_validation():
 
 def test_plan_is_pure_and_sane():
     # the measured automatic dispatch at H = 7168
-    assert ar.attnres_plan(1, 12, 7168) == (2, 14, 64)     # N >= 8: 1-wave chunks up to 32 tokens
+    assert ar.attnres_plan(1, 12, 7168) == (2, 14, 64)     # N >= 8: 1-wave chunks up to 48 tokens
     assert ar.attnres_plan(2, 8, 7168) == (2, 14, 64)
     assert ar.attnres_plan(8, 12, 7168) == (2, 14, 64)
     assert ar.attnres_plan(24, 12, 7168) == (2, 14, 64)
     assert ar.attnres_plan(32, 8, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(33, 8, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
+    assert ar.attnres_plan(48, 8, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(49, 8, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
+    assert ar.attnres_plan(64, 12, 7168) == (2, 4, 256)
+    assert ar.attnres_plan(65, 12, 7168) == (2, 7, 128)    # then 2-wave chunks up to 96
+    assert ar.attnres_plan(96, 8, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(97, 8, 7168)[0] == 1
     assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # 2 <= N <= 7: 2-wave chunks (one exchange)
     assert ar.attnres_plan(16, 4, 7168) == (2, 7, 128)
     assert ar.attnres_plan(16, 3, 7168) == (2, 7, 128)
@@ -191,7 +196,7 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(64, 2, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 2, 896) == (1, 1, 128)       # short rows stay on one workgroup per token
     assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks
-    assert ar.attnres_plan(65, 12, 7168)[0] == 1
+    assert ar.attnres_plan(97, 12, 7168)[0] == 1
     assert ar.attnres_plan(256, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(257, 12, 7168) == (3, 4, 448)   # just past the CU count: the hybrid
     assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # up to 64 left-over tokens

@@ -1,7 +1,7 @@
 """attnres_add_rmsnorm_fwd_noalloc: the fused call for callers that cannot
 allocate, through the C ABI, against attnres_add_rmsnorm_fwd.
 
-Its split-kernel scratch is a static device array (64 token slots) instead of
+Its split-kernel scratch is a static device array (96 token slots) instead of
 the allocated one, so it needs no attnres_init.  The first test calls it before
 anything in the process has called attnres_init (when the file runs alone),
 two calls in a row with the second smaller, and then compares with the
@@ -62,12 +62,13 @@ def out_pair(M, H):
             torch.empty((M, H), dtype=torch.bfloat16, device="cuda"))
 
 
-# (M, N): split kernel with 4-wave chunks and two exchanges, then a smaller
-# call (2-wave chunks, Gram form), one token, the most sources the split
-# kernel takes, calls kernel W serves (no scratch), and the hybrid of W and
-# split chunks just past the CU count (its split part at the most tokens the
-# automatic dispatch gives it)
-CALLS = [(48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4)]
+# (M, N): the split kernel at the most tokens the automatic dispatch gives it
+# (2-wave chunks, two exchanges), then smaller calls (1-wave chunks; 2-wave
+# chunks in the Gram form), one token, the most sources the split kernel
+# takes, calls kernel W serves (no scratch), the hybrid of W and split chunks
+# just past the CU count (its split part at the most tokens the automatic
+# dispatch gives it), and 2-wave chunks again
+CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (80, 8)]
 
 
 def test_noalloc_matches_fwd(ar, orc):
@@ -91,11 +92,11 @@ def test_noalloc_matches_fwd(ar, orc):
 
 
 def test_noalloc_rejects_beyond_static_scratch(ar):
-    """The split kernel forced on 65 tokens: the allocating entry point serves
-    it (512 slots), the no-allocation one (64 slots) returns ATTNRES_ESCRATCH;
-    64 tokens it serves."""
-    assert ar.ATTNRES_NOALLOC_MAX_SPLIT_TOKENS == 64
-    case = W.make_case(cfg=86, M=65, N=8, add2=True)
+    """The split kernel forced on 97 tokens: the allocating entry point serves
+    it (512 slots), the no-allocation one (96 slots) returns ATTNRES_ESCRATCH;
+    96 tokens it serves."""
+    assert ar.ATTNRES_NOALLOC_MAX_SPLIT_TOKENS == 96
+    case = W.make_case(cfg=86, M=97, N=8, add2=True)
     ar.attnres_set_variant(2, 2)
     try:
         op, on = out_pair(case.M, case.H)
@@ -104,7 +105,7 @@ def test_noalloc_rejects_beyond_static_scratch(ar):
         P.run_gpu(case)
     finally:
         ar.attnres_set_variant(0, 0)
-    case = W.make_case(cfg=86, M=64, N=8, add2=True)
+    case = W.make_case(cfg=86, M=96, N=8, add2=True)
     ar.attnres_set_variant(2, 2)
     try:
         op, on = out_pair(case.M, case.H)
