@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     attnres_debug_reset_scratch,
     attnres_debug_set_epoch,
     attnres_debug_set_exchange,
+    attnres_debug_set_slot_rotation,
     attnres_init,
     attnres_plan,
     attnres_selftest_rounding,

@@ -77,6 +77,8 @@ def library():
         lib.attnres_debug_set_epoch.restype = ctypes.c_int
         lib.attnres_debug_set_exchange.argtypes = [ctypes.c_int]
         lib.attnres_debug_set_exchange.restype = ctypes.c_int
+        lib.attnres_debug_set_slot_rotation.argtypes = [ctypes.c_int]
+        lib.attnres_debug_set_slot_rotation.restype = ctypes.c_int
         lib.attnres_selftest_rounding.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
         lib.attnres_selftest_rounding.restype = ctypes.c_int
         lib.attnres_status_string.argtypes = [ctypes.c_int]
@@ -262,6 +264,10 @@ def attnres_debug_set_spin_limit(limit: int = 0) -> None:
 
 def attnres_debug_set_exchange(mode: int = 0) -> None:
     _check(library().attnres_debug_set_exchange(mode), "attnres_debug_set_exchange")
+
+
+def attnres_debug_set_slot_rotation(on: bool = True) -> None:
+    _check(library().attnres_debug_set_slot_rotation(1 if on else 0), "attnres_debug_set_slot_rotation")
 
 
 def attnres_debug_reset_scratch() -> None:

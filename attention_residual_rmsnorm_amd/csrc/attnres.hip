@@ -89,6 +89,7 @@ struct Params {
     int chunks;         // split hidden: workgroups per token
     int64_t M;
     int64_t split_base;       // split hidden: first token it serves (the hybrid's W part takes [0, split_base))
+    int64_t slot_base;        // split hidden: scratch token slot of token split_base
     int split_threads;        // split hidden: threads per chunk (the workgroup's others exit at once)
     int wg_blocks;            // hybrid: workgroups of its W part
     unsigned long long* rec1; // split hidden: [token slot][MAX_CHUNKS][REC1_CHUNK] tagged A2 partials
@@ -973,8 +974,9 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
     const int C = p.chunks;
     const int ib = b >> 3;
     const int chunk = ib - (ib / C) * C;
-    const int64_t slot = (int64_t)(ib / C) * 8 + ((b + p.xcd_skew * chunk) & 7);
-    const int64_t t = p.split_base + slot;
+    const int64_t rel = (int64_t)(ib / C) * 8 + ((b + p.xcd_skew * chunk) & 7);
+    const int64_t t = p.split_base + rel;
+    const int64_t slot = p.slot_base + rel;
     if (t >= p.M)
         return;
 
@@ -1334,6 +1336,7 @@ const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8,
 const std::array<Kernel, MAX_SNAP + 1> kHybrid[2] = {hybrid_table<false>(Seq{}), hybrid_table<true>(Seq{})};
 
 struct Scratch {
+    int dev = -1;
     void* base = nullptr;
     unsigned long long* rec1 = nullptr;
     unsigned long long* rec2 = nullptr;
@@ -1346,6 +1349,13 @@ std::mutex g_mutex;                          // serialises attnres_init
 Scratch g_scratch[MAX_DEVICES];              // written once per device, under g_mutex
 std::atomic<bool> g_ready[MAX_DEVICES];      // published after g_scratch[dev] is complete
 int g_force_variant = 0;
+// Token slots of the allocated scratch are handed out in turn, per device,
+// when a call is enqueued: [base, base + n) with base the device's next free
+// slot, or 0 when the call would run past the last slot.  Calls enqueued on
+// different streams therefore use different slots unless MAX_SPLIT_TOKENS
+// slots were handed out between them, and may run at the same time.
+std::atomic<int64_t> g_slot_next[MAX_DEVICES];
+std::atomic<bool> g_rotate{true}; // false: every call starts at slot 0 (tests)
 unsigned g_spin_limit = SPIN_LIMIT;
 unsigned g_l2_polls = L2_POLLS;
 int g_xcd_skew = 0;
@@ -1387,12 +1397,25 @@ int init_scratch()
     s.state = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES);
     s.timeouts = reinterpret_cast<unsigned*>(c + REC1_BYTES + REC2_BYTES + STATE_BYTES);
     s.base = base;
+    s.dev = dev;
     g_ready[dev].store(true, std::memory_order_release);
     return ATTNRES_OK;
 }
 
 // The scratch of the current device, or ATTNRES_ENOINIT when attnres_init has
 // not run there.  Never allocates, never synchronises.
+int64_t take_slots(int dev, int64_t n)
+{
+    if (!g_rotate.load(std::memory_order_relaxed))
+        return 0;
+    int64_t cur = g_slot_next[dev].load(std::memory_order_relaxed);
+    for (;;) {
+        const int64_t base = cur + n > MAX_SPLIT_TOKENS ? 0 : cur;
+        if (g_slot_next[dev].compare_exchange_weak(cur, base + n, std::memory_order_relaxed))
+            return base;
+    }
+}
+
 int scratch_for_current_device(Scratch** out)
 {
     int dev = 0;
@@ -1535,6 +1558,8 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.chunks = pl.chunks;
     p.M = M;
     p.split_base = pl.split_base;
+    // the static scratch's slots are fixed (one call at a time per device)
+    p.slot_base = !static_scratch && pl.split_slots > 0 ? take_slots(sc->dev, pl.split_slots) : 0;
     p.split_threads = pl.variant == 3 ? pl.split_threads : pl.threads;
     p.wg_blocks = pl.wg_blocks;
     p.spin_limit = g_spin_limit;
@@ -1707,6 +1732,13 @@ extern "C" int attnres_debug_reset_scratch(void)
     if (hipDeviceSynchronize() != hipSuccess || hipMemset(sc->base, 0, SCRATCH_BYTES) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
         return ATTNRES_EHIP;
+    g_slot_next[sc->dev].store(0, std::memory_order_relaxed);
+    return ATTNRES_OK;
+}
+
+extern "C" int attnres_debug_set_slot_rotation(int on)
+{
+    g_rotate.store(on != 0, std::memory_order_relaxed);
     return ATTNRES_OK;
 }
 

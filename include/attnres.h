@@ -115,10 +115,15 @@ extern "C" {
  * between calls, HIP-graph replays included).  attnres_init() allocates it;
  * the call itself never allocates or synchronises, and returns
  * ATTNRES_ENOINIT (launching nothing) on a device where attnres_init() has
- * not run, whatever kernel the sizes would select.  Calls on the same device
- * must be ordered with respect to each other (same stream, or synchronised):
- * two overlapping calls on different streams of one device race on the
- * scratch.  The split-hidden kernel's waits for the other workgroups of a
+ * not run, whatever kernel the sizes would select.  The scratch holds 512
+ * token slots, handed out in turn when a call is enqueued (a call takes M
+ * slots, or M - 256 for the hybrid's split part; it starts again from slot 0
+ * when the rest would not fit): calls enqueued on different streams of one
+ * device may run at the same time, as long as fewer than 512 slots are handed
+ * out between the enqueue of the earliest call still running and that of the
+ * latest.  A call captured into a HIP graph keeps the slots it was given, so
+ * replays of one graph must be ordered with respect to each other (replays of
+ * different graphs need not be).  The split-hidden kernel's waits for the other workgroups of a
  * token are bounded; a wait that gives up (which a correct run never does:
  * see attnres_debug_timeouts) makes that token's out_norm (and out_mix)
  * elements that depend on it NaN instead of wrong; out_prefix is unaffected.
@@ -172,8 +177,9 @@ int attnres_add_rmsnorm_mix_fwd(const void* prefix, const void* add, const void*
  * allocation, no synchronisation) and enqueues one kernel on `stream` that
  * clears it, ordered before the call's own kernel; attnres_init(), if called
  * on the device, does both beforehand.  Every call on a device shares that
- * device's array: calls on one device that overlap in time (different
- * streams, not synchronised) race on it, as for attnres_add_rmsnorm_fwd.
+ * device's array, at the same token slots (they are not handed out in turn):
+ * calls on one device must be ordered with respect to each other (same
+ * stream, or synchronised); calls that overlap in time race on it.
  *
  * Returns ATTNRES_OK, ATTNRES_ESCRATCH or one of the codes of
  * attnres_add_rmsnorm_fwd other than ATTNRES_ENOINIT.
@@ -271,8 +277,18 @@ int attnres_debug_set_spin_limit(unsigned limit);
 int attnres_debug_set_exchange(int mode);
 
 /*
+ * attnres_debug_set_slot_rotation -- diagnostic, for tests that need calls on
+ * the same token slots of the scratch: on = 0 makes every later call start at
+ * slot 0 instead of taking the next slots in turn (on != 0, the default,
+ * restores that).  Process-wide; not thread-safe with concurrent calls.
+ * Returns ATTNRES_OK.
+ */
+int attnres_debug_set_slot_rotation(int on);
+
+/*
  * attnres_debug_reset_scratch -- diagnostic: clears the split-hidden scratch of
- * the current device (records, epoch words, timeout counter) synchronously.
+ * the current device (records, epoch words, timeout counter) synchronously,
+ * and hands out token slots from slot 0 again.
  * No call may be in flight on the device.  Not for use during HIP-graph
  * capture.  Returns ATTNRES_OK, ATTNRES_ENOINIT or ATTNRES_EHIP.
  */

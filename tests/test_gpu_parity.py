@@ -432,14 +432,19 @@ def test_exchange_forms_alternate(ar, orc, variant):
     run, within the bound of the oracle)."""
     cases = [W.make_case(cfg=75, M=8, N=4, add2=True), W.make_case(cfg=76, M=8, N=8, add2=True),
              _cancelling_case(4, 1e-3, M=8)]
-    first = [P.run_gpu(c) for c in cases]
-    for c, (gp, gn) in zip(cases, first):
-        rp, rn = P.run_oracle(orc, c)
-        P.assert_parity(gp, gn, rp, rn, c.name)
-    for rep in range(30):
-        i = (rep * 7) % 3
-        gp, gn = P.run_gpu(cases[i])
-        assert np.array_equal(gp, first[i][0]) and np.array_equal(gn, first[i][1]), "call %d (case %d)" % (rep, i)
+    ar.attnres_debug_set_slot_rotation(False)  # every call on token slots 0..7
+    try:
+        first = [P.run_gpu(c) for c in cases]
+        for c, (gp, gn) in zip(cases, first):
+            rp, rn = P.run_oracle(orc, c)
+            P.assert_parity(gp, gn, rp, rn, c.name)
+        for rep in range(30):
+            i = (rep * 7) % 3
+            gp, gn = P.run_gpu(cases[i])
+            assert np.array_equal(gp, first[i][0]) and np.array_equal(gn, first[i][1]), "call %d (case %d)" % (
+                rep, i)
+    finally:
+        ar.attnres_debug_set_slot_rotation(True)
     assert ar.attnres_debug_timeouts() == 0
 
 
@@ -620,6 +625,7 @@ def test_epoch_wrap(ar, orc):
     ra, rb = P.run_oracle(orc, a), P.run_oracle(orc, b)
     try:
         ar.attnres_debug_reset_scratch()
+        ar.attnres_debug_set_slot_rotation(False)  # every call on token slots 0..7
         ar.attnres_set_variant(2, 1)
         assert ar.attnres_plan(8, 8, 7168)[1] == 14
         ar.attnres_debug_set_epoch(5)
@@ -638,7 +644,40 @@ def test_epoch_wrap(ar, orc):
             ar.attnres_debug_set_epoch(EPOCH_PERIOD)
     finally:
         ar.attnres_set_variant(0, 0)
+        ar.attnres_debug_set_slot_rotation(True)
         ar.attnres_debug_reset_scratch()
+
+
+def test_concurrent_streams(ar, orc):
+    """Split-kernel calls enqueued on two streams with no ordering between
+    them (two exchanges and the Gram form's one, 1- and 2-wave chunks): each
+    call takes its own token slots of the scratch, so calls that run at the
+    same time do not share records.  Every output against the oracle, and no
+    wait given up."""
+    import torch
+
+    cases = [W.make_case(cfg=90 + i, M=32, N=(12, 4, 8)[i % 3], add2=True) for i in range(6)]
+    refs = [P.run_oracle(orc, c) for c in cases]
+    d = P.dev
+    ins = [(d(c.prefix), d(c.add), d(c.add2), [d(s) for s in c.snapshots], d(c.query), d(c.gamma)) for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ar.attnres_debug_reset_scratch()  # slots from 0: the 12 calls take 384 of the 512
+    outs = []
+    for rep in range(2):
+        for i, c in enumerate(cases):
+            op, on = (torch.empty((c.M, c.H), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+            outs.append((i, op, on))
+    torch.cuda.synchronize()
+    for k, (i, op, on) in enumerate(outs):
+        s = streams[k % 2]
+        pre, add, add2, snaps, q, g = ins[i]
+        ar.attnres_add_rmsnorm_fwd(pre, add, add2, snaps, q, g, cases[i].eps, out_prefix=op, out_norm=on,
+                                   stream=s)
+    torch.cuda.synchronize()
+    say("concurrent streams", [ar.attnres_plan(c.M, c.N, c.H) for c in cases[:3]])
+    for k, (i, op, on) in enumerate(outs):
+        P.assert_parity(P.host(op), P.host(on), *refs[i], "call %d (case %d, stream %d)" % (k, i, k % 2))
+    assert ar.attnres_debug_timeouts() == 0
 
 
 # --- the standalone add ----------------------------------------------------------
