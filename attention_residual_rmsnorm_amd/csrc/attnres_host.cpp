@@ -69,19 +69,33 @@ bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
 }
 
 // Hybrid: kernel W (two vectors per thread) on the first nw tokens, one
-// workgroup each, then 4-wave split chunks (a quarter of a row at H = 7168) on
-// the other M - nw; nw is a multiple of 8 so the chunks of a token keep one
-// workgroup id mod 8.
-bool plan_hybrid(int64_t M, int nvec, Plan& pl)
+// workgroup each, then split chunks of `waves` waves on the other M - nw
+// (waves = 0: the narrowest of 1, 2 and 4 whose chunk workgroups, 8 C per
+// group of 8 token slots, number at most HYBRID_WG_TOKENS, else 4): the extra
+// tokens spread over as many CUs as there are, in pieces as small as that
+// allows, so no CU's W token waits behind much of a chunk (M = 264, N = 12:
+// 1-wave 13.60 against 4-wave 15.64 us; M = 288: 2-wave 14.55 against 16.05;
+// M = 300 and 320: 4-wave 15.98 and 17.21 against 18.0 and 19.0 for 2-wave).
+// nw is a multiple of 8 so the chunks of a token keep one workgroup id mod 8.
+bool plan_hybrid(int64_t M, int nvec, int waves, Plan& pl)
 {
-    if (nvec <= 512 || nvec > 1024 || M < 1)
+    if (nvec <= 512 || nvec > 1024 || M < 1 || !(waves == 0 || waves == 1 || waves == 2 || waves == 4))
         return false;
     const int64_t nw = M > HYBRID_WG_TOKENS ? HYBRID_WG_TOKENS : (M / 2) / 8 * 8;
     const int64_t rest = M - nw;
     if (rest > MAX_SPLIT_TOKENS)
         return false;
+    const int64_t groups = (rest + 7) / 8;
+    if (waves == 0) {
+        waves = 4;
+        for (int w = 1; w < 4; w *= 2)
+            if (8 * (int64_t)((nvec + 64 * w - 1) / (64 * w)) * groups <= HYBRID_WG_TOKENS) {
+                waves = w;
+                break;
+            }
+    }
     const int threads = round_up64((nvec + 1) / 2);
-    const int chunk_threads = HYBRID_CHUNK_THREADS;
+    const int chunk_threads = 64 * waves;
     const int chunks = (nvec + chunk_threads - 1) / chunk_threads;
     pl = Plan{};
     pl.variant = 3;
@@ -91,9 +105,9 @@ bool plan_hybrid(int64_t M, int nvec, Plan& pl)
     pl.split_base = nw;
     pl.split_threads = chunk_threads;
     pl.wg_blocks = (int)nw;
-    pl.grid = nw + 8 * (int64_t)chunks * ((rest + 7) / 8);
+    pl.grid = nw + 8 * (int64_t)chunks * groups;
     pl.split_slots = rest;
-    return threads >= HYBRID_CHUNK_THREADS && chunks <= 8;
+    return chunk_threads <= threads && chunks <= MAX_CHUNKS;
 }
 
 } // namespace
@@ -174,7 +188,7 @@ bool valid_override(int variant, int param)
     case 0: return param == 0;
     case 1: return param == 0 || param == 1 || param == 2 || param == 4;
     case 2: return param >= 0 && param <= 8 && param != 3;
-    case 3: return param == 0;
+    case 3: return param == 0 || param == 1 || param == 2 || param == 4;
     default: return false;
     }
 }
@@ -200,7 +214,7 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
                                                                                     : ATTNRES_EINVAL;
     }
     if (force_variant == 3)
-        return !many && plan_hybrid(M, nvec, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+        return !many && plan_hybrid(M, nvec, force_param, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168, one
     // pass of sources:
@@ -258,7 +272,7 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // Just past the CU count, kernel W would give some CUs two whole tokens
     // and the others one; the hybrid gives every CU one W token and a few
     // split chunks of the rest.
-    if (long_rows && !many && M > HYBRID_WG_TOKENS && M <= HYBRID_MAX_TOKENS && plan_hybrid(M, nvec, pl))
+    if (long_rows && !many && M > HYBRID_WG_TOKENS && M <= HYBRID_MAX_TOKENS && plan_hybrid(M, nvec, 0, pl))
         return ATTNRES_OK;
     if (plan_wg(M, nvec, wg_vpt, pl))
         return ATTNRES_OK;

@@ -44,15 +44,14 @@ constexpr int SHORT_WG_THREADS = 256;
 constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 65536;
 
 // The hybrid launch (kernel W's workgroups for the first HYBRID_WG_TOKENS
-// tokens, one token each, and 4-wave split chunks of HYBRID_CHUNK_THREADS
-// threads for the rest), automatic for rows of LONG_ROW_VECTORS..1024 vectors,
-// one pass of sources and HYBRID_WG_TOKENS < M <= HYBRID_MAX_TOKENS: one chunk
-// per CU at most next to its W token.  (Beyond, chunks either queue for a CU's
-// second workgroup slot or, as wide as half a row, lose to kernel W: M = 321,
-// N = 12: 19.65 against 18.79 us.)
+// tokens, one token each, and split chunks of 1, 2 or 4 waves for the rest:
+// the narrowest whose workgroups still number at most HYBRID_WG_TOKENS, one
+// per CU next to its W token), automatic for rows of LONG_ROW_VECTORS..1024
+// vectors, one pass of sources and HYBRID_WG_TOKENS < M <= HYBRID_MAX_TOKENS.
+// (Beyond, chunks either queue for a CU's second workgroup slot or, as wide
+// as half a row, lose to kernel W: M = 321, N = 12: 19.65 against 18.79 us.)
 constexpr int HYBRID_WG_TOKENS = 256;
 constexpr int HYBRID_MAX_TOKENS = 320;
-constexpr int HYBRID_CHUNK_THREADS = 256;
 
 struct Plan {
     int variant = 0; // 1 = workgroup per token, 2 = split hidden, 3 = hybrid

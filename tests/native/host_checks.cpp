@@ -96,18 +96,21 @@ int main()
                                            pl.threads <= 512 && pl.split_slots == m &&
                                            pl.split_threads == pl.threads &&
                                            pl.chunks <= (pl.threads <= 128 ? MAX_CHUNKS : 8));
-                                // the hybrid: W on [0, split_base), one workgroup per token, 4-wave
-                                // chunks on the rest (the split family of up to 8 chunks, one pass of
-                                // sources), chunks of a token on one workgroup id mod 8
+                                // the hybrid: W on [0, split_base), one workgroup per token, 1-, 2- or
+                                // 4-wave chunks on the rest (one pass of sources), chunks of a token on
+                                // one workgroup id mod 8
                                 if (pl.variant == 3)
                                     EXPECT(n <= MAX_SNAP && pl.vpt == 2 && pl.threads <= 512 &&
-                                           pl.threads >= HYBRID_CHUNK_THREADS &&
+                                           pl.threads >= pl.split_threads &&
                                            (int64_t)pl.threads * 2 * 8 >= h && pl.split_base % 8 == 0 &&
                                            pl.wg_blocks == pl.split_base && pl.split_base <= HYBRID_WG_TOKENS &&
                                            pl.split_base < m && m - pl.split_base <= MAX_SPLIT_TOKENS &&
                                            pl.split_slots == m - pl.split_base &&
-                                           pl.split_threads == HYBRID_CHUNK_THREADS && pl.chunks <= 8 &&
+                                           (pl.split_threads == 64 || pl.split_threads == 128 ||
+                                            pl.split_threads == 256) &&
+                                           pl.chunks <= MAX_CHUNKS &&
                                            (int64_t)pl.chunks * pl.split_threads * 8 >= h &&
+                                           (int64_t)(pl.chunks - 1) * pl.split_threads * 8 < h &&
                                            pl.grid == pl.split_base + 8 * pl.chunks * ((pl.split_slots + 7) / 8));
                                 if (pl.variant == 1)
                                     EXPECT(pl.split_slots == 0);
@@ -136,9 +139,16 @@ int main()
         Plan pl;
         EXPECT(make_plan(256, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
         EXPECT(make_plan(257, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 && pl.split_base == 256 &&
-               pl.chunks == 4 && pl.grid == 256 + 32);
+               pl.chunks == 14 && pl.split_threads == 64 && pl.grid == 256 + 112);
+        EXPECT(make_plan(272, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 14 && pl.grid == 256 + 224);
+        EXPECT(make_plan(273, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 7 && pl.split_threads == 128);
+        EXPECT(make_plan(288, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 7 && pl.grid == 256 + 224);
+        EXPECT(make_plan(289, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 4 && pl.split_threads == 256);
         EXPECT(make_plan(HYBRID_MAX_TOKENS, 1, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 &&
-               pl.chunks == 4 && pl.split_threads == 256);
+               pl.chunks == 4 && pl.split_threads == 256 && pl.grid == 512);
+        EXPECT(make_plan(260, 12, 8192, 0, 0, pl) == ATTNRES_OK && pl.chunks == 16 && pl.threads == 512);
+        EXPECT(make_plan(300, 12, 7168, 3, 1, pl) == ATTNRES_OK && pl.chunks == 14 && pl.split_threads == 64);
+        EXPECT(make_plan(300, 12, 7168, 3, 8, pl) == ATTNRES_EINVAL);
         EXPECT(make_plan(HYBRID_MAX_TOKENS + 1, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
         EXPECT(make_plan(300, 13, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
         EXPECT(make_plan(300, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);

@@ -198,8 +198,10 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks
     assert ar.attnres_plan(97, 12, 7168)[0] == 1
     assert ar.attnres_plan(256, 1, 7168) == (1, 1, 448)
-    assert ar.attnres_plan(257, 12, 7168) == (3, 4, 448)   # just past the CU count: the hybrid
-    assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # up to 64 left-over tokens
+    assert ar.attnres_plan(257, 12, 7168) == (3, 14, 448)  # just past the CU count: the hybrid, 1-wave
+    assert ar.attnres_plan(272, 12, 7168) == (3, 14, 448)  # chunks up to 16 left-over tokens,
+    assert ar.attnres_plan(273, 12, 7168) == (3, 7, 448)   # 2-wave up to 32,
+    assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # 4-wave up to 64
     assert ar.attnres_plan(321, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(384, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(300, 13, 7168) == (1, 1, 448)
@@ -241,7 +243,7 @@ def test_set_exchange_validation():
 def test_set_variant_validation():
     lib = ar.library()
     assert lib.attnres_set_variant(4, 0) == ar.ATTNRES_EINVAL
-    assert lib.attnres_set_variant(3, 1) == ar.ATTNRES_EINVAL
+    assert lib.attnres_set_variant(3, 3) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(1, 3) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(2, 9) == ar.ATTNRES_EINVAL
     assert lib.attnres_set_variant(2, 3) == ar.ATTNRES_EINVAL
@@ -265,11 +267,15 @@ def test_set_variant_validation():
         with pytest.raises(ar.AttnResError):  # more than 12 only in the 1-2-wave family
             ar.attnres_plan(1, 13, 7168)
         ar.attnres_set_variant(3, 0)
-        assert ar.attnres_plan(20, 12, 7168) == (3, 4, 448)  # the hybrid, forced at a small M
+        assert ar.attnres_plan(20, 12, 7168) == (3, 14, 448)  # the hybrid, forced at a small M
         with pytest.raises(ar.AttnResError):  # its split part: one pass of sources
             ar.attnres_plan(20, 13, 7168)
         with pytest.raises(ar.AttnResError):  # rows of 513..1024 vectors only
             ar.attnres_plan(20, 4, 3584)
+        ar.attnres_set_variant(3, 2)
+        assert ar.attnres_plan(20, 12, 7168) == (3, 7, 448)   # its chunks forced to 2 waves
+        ar.attnres_set_variant(3, 4)
+        assert ar.attnres_plan(300, 12, 7168) == (3, 4, 448)
     finally:
         ar.attnres_set_variant(0, 0)
 

@@ -110,13 +110,14 @@ def check(ar, orc, case, what):
 KERNELS = [((1, 0), 4, "W"), ((1, 0), 12, "W"), ((1, 0), 20, "W batched"), ((1, 4), 12, "W 4 vectors"),
            ((2, 1), 12, "S1w"), ((2, 2), 12, "S2w"), ((2, 7), 12, "S7w"), ((2, 2), 4, "S2w Gram"),
            ((2, 1), 7, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"),
+           ((3, 4), 12, "hybrid 4w"),
            ((0, 0), 1, "auto")]
 
 
 @pytest.mark.parametrize("eps", EPS)
 @pytest.mark.parametrize("variant,N,label", KERNELS, ids=[k[2] + " N=%d" % k[1] for k in KERNELS])
 def test_eps(ar, orc, variant, N, label, eps):
-    case = eps_case(5 if variant != (3, 0) else 21, N, eps, add2=(N % 2 == 0))
+    case = eps_case(5 if variant[0] != 3 else 21, N, eps, add2=(N % 2 == 0))
     ar.attnres_set_variant(*variant)
     try:
         check(ar, orc, case, "%s N=%d eps=%g" % (label, N, eps))

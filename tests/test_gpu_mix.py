@@ -19,8 +19,8 @@ from attention_residual_rmsnorm_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7), (3, 0)]
-VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w", "hybrid"]
+VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7), (3, 0), (3, 4)]
+VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w", "hybrid", "hybrid4w"]
 
 
 def say(*a):

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 # (variant, param): 0 = automatic; W = workgroup per token with param vectors
 # per thread; S = split hidden with param waves per workgroup
-VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7), (3, 0)]
-VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w", "hybrid"]
+VARIANTS = [(0, 0), (1, 1), (1, 2), (2, 1), (2, 2), (2, 7), (3, 0), (3, 4)]
+VID = ["auto", "W1", "W2", "S1w", "S2w", "S7w", "hybrid", "hybrid4w"]
 
 
 def say(*a):
@@ -148,7 +148,7 @@ def test_add2_equals_presummed(ar, variant, M):
 @pytest.mark.parametrize("variant", VARIANTS, ids=VID, indirect=True)
 def test_golden_fold_add(ar, variant):
     rows = pins.read_golden_fold()
-    H = 64 if variant != (3, 0) else 7168  # the hybrid serves rows of 4104..8192 elements
+    H = 64 if variant[0] != 3 else 7168  # the hybrid serves rows of 4104..8192 elements
     M = len(rows)
     if not supported(ar, M, 0, H):
         pytest.skip("variant not available for this size")
@@ -409,8 +409,8 @@ def test_in_place_prefix(ar, orc, variant):
 # --- determinism, graphs, canaries ---------------------------------------------
 
 # W; split with 1, 2 (gather in every wave), 7 waves (wave 0); the hybrid of W and 4-wave chunks
-SYNC_VARIANTS = [(1, 0), (2, 1), (2, 2), (2, 7), (3, 0)]
-SYNC_VID = ["W", "S1w", "S2w", "S7w", "hybrid"]
+SYNC_VARIANTS = [(1, 0), (2, 1), (2, 2), (2, 7), (3, 0), (3, 4)]
+SYNC_VID = ["W", "S1w", "S2w", "S7w", "hybrid", "hybrid4w"]
 
 
 @pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
@@ -497,13 +497,14 @@ def test_graph_replay(ar, variant, N):
     assert ar.attnres_debug_timeouts() == 0
 
 
-@pytest.mark.parametrize("variant", [(1, 0), (2, 0), (3, 0)], ids=["W", "S", "hybrid"], indirect=True)
+@pytest.mark.parametrize("variant", [(1, 0), (2, 0), (3, 0), (3, 4)], ids=["W", "S", "hybrid", "hybrid4w"],
+                         indirect=True)
 def test_canaries(ar, orc, variant):
     """Outputs live inside larger buffers filled with a canary pattern: nothing
     outside [M,H] may change."""
     import torch
 
-    case = W.make_case(cfg=63, M=7, H=1000, N=3, add2=True) if variant != (3, 0) else \
+    case = W.make_case(cfg=63, M=7, H=1000, N=3, add2=True) if variant[0] != 3 else \
         W.make_case(cfg=63, M=21, H=7176, N=3, add2=True)
     n = case.M * case.H
     pad = 4096
