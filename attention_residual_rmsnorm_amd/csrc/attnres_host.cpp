@@ -226,11 +226,14 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    2-wave; M = 80 and 96: 2-wave 9.15 and 9.54 against 10.13 and 10.35
     //    for W, N = 8 7.97 and 8.14 against 8.26 and 8.50; from 112 tokens
     //    within 0.1-0.4 us of W);
-    //  * 2 <= N <= 7 (the Gram form's one exchange): 2-wave chunks up to 16
-    //    tokens, up to 32 from N = 4 on, then 4-wave chunks up to 64 (M = 1,
-    //    N = 7: 5.58 against 5.93 for 1-wave chunks, whose 35 values do not fit
-    //    one round of polling; M = 64, N = 7: 7.24 against 7.91 for W; N = 2
-    //    from 24 tokens: W 5.29 against 5.32);
+    //  * 2 <= N <= 7 (the Gram form's one exchange): 1-wave chunks up to 16
+    //    tokens while the form's values fit one polling round (N <= 5: at
+    //    most 27), 2-wave chunks up to 32 tokens, then 4-wave chunks up to 64
+    //    from N = 4 on (M = 1, N = 4: 4.72 against 5.01 us for 2-wave chunks;
+    //    M = 16, N = 5: 5.64 against 5.70; N = 6, whose 35 values take two
+    //    rounds: 1-wave 6.10 against 5.95 at M = 8; M = 24, N = 3: 2-wave
+    //    5.39 against 5.43 for 1-wave and 5.67 for W; M = 64, N = 7: 7.24
+    //    against 7.91 for W);
     //  * N <= 1 at every M: one workgroup per token (at N = 1 the split wins
     //    with add2 and loses without it, M = 1: 4.21 against 4.64 us and 4.37
     //    against 4.30; the dispatch may not depend on add2, and the named
@@ -263,8 +266,10 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         if (M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
     } else if (n >= 2) {
-        const bool two_wave = M <= SPLIT_SMALL_TOKENS || (n >= 4 && M <= SPLIT_SMALL_TOKENS_WIDE);
-        if (two_wave && plan_split(M, nvec, 2, pl))
+        const int gram_values = (n + 1) + (n + 1) * (n + 2) / 2;
+        if (gram_values <= 32 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
+            return ATTNRES_OK;
+        if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
         if (n >= 4 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;

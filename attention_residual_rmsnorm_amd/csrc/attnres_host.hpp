@@ -17,9 +17,9 @@ constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hi
 // automatic dispatch (see make_plan) at H >= 7168, one pass of sources:
 // N >= 8: 1-wave split chunks up to SPLIT_ONE_WAVE_TOKENS tokens, 4-wave up
 // to SPLIT_MID_TOKENS, 2-wave up to SPLIT_WIDE_TOKENS; 2 <= N <
-// GRAM_MAX_SOURCES: 2-wave chunks up to SPLIT_SMALL_TOKENS tokens (up to
-// SPLIT_SMALL_TOKENS_WIDE from N = 4 on), then 4-wave up to SPLIT_MID_TOKENS
-// from N = 4 on
+// GRAM_MAX_SOURCES: 1-wave chunks up to SPLIT_SMALL_TOKENS tokens while the
+// Gram form's values fit one polling round (N <= 5), 2-wave chunks up to
+// SPLIT_SMALL_TOKENS_WIDE, then 4-wave up to SPLIT_MID_TOKENS from N = 4 on
 constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_ONE_WAVE_TOKENS = 48;

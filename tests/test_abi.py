@@ -175,11 +175,14 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(65, 12, 7168) == (2, 7, 128)    # then 2-wave chunks up to 96
     assert ar.attnres_plan(96, 8, 7168) == (2, 7, 128)
     assert ar.attnres_plan(97, 8, 7168)[0] == 1
-    assert ar.attnres_plan(2, 3, 7168) == (2, 7, 128)      # 2 <= N <= 7: 2-wave chunks (one exchange)
-    assert ar.attnres_plan(16, 4, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(16, 3, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(17, 3, 7168)[0] == 1            # N < 4: up to 16 tokens
-    assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)     # N >= 4: up to 32 tokens
+    assert ar.attnres_plan(2, 3, 7168) == (2, 14, 64)      # 2 <= N <= 5: 1-wave chunks (one exchange)
+    assert ar.attnres_plan(16, 4, 7168) == (2, 14, 64)     # up to 16 tokens
+    assert ar.attnres_plan(16, 5, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(16, 6, 7168) == (2, 7, 128)     # N = 6, 7: 2-wave chunks
+    assert ar.attnres_plan(17, 3, 7168) == (2, 7, 128)     # then 2-wave chunks up to 32 tokens
+    assert ar.attnres_plan(32, 2, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(33, 3, 7168)[0] == 1            # N < 4: then a workgroup per token
+    assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)
     assert ar.attnres_plan(33, 6, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
     assert ar.attnres_plan(2, 7, 7168) == (2, 7, 128)
     assert ar.attnres_plan(32, 7, 7168) == (2, 7, 128)
@@ -190,7 +193,7 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(16, 13, 7168) == (2, 7, 128)    # above 12 sources: 2-wave family
     assert ar.attnres_plan(32, 4, 7168) == (2, 7, 128)
     assert ar.attnres_plan(33, 4, 7168) == (2, 4, 256)
-    assert ar.attnres_plan(1, 2, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(1, 2, 7168) == (2, 14, 64)
     assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
     assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(64, 2, 7168) == (1, 1, 448)

@@ -266,14 +266,14 @@ def test_shapes(ar, orc, variant, M, H, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 6, 7, 8, 12])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8, 12])
 @pytest.mark.parametrize("M", [1, 2, 16, 17, 24, 32, 33, 48, 49, 64, 65, 96, 97])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
     (for N >= 8 1-wave chunks up to 48 tokens, then 4-wave up to 64, 2-wave up
-    to 96; for 2 <= N <= 7, the one-exchange form, 2-wave chunks up to 16
-    tokens, up to 32 from N = 4, then 4-wave up to 64; then a workgroup per
-    token) and
+    to 96; for 2 <= N <= 7, the one-exchange form, 1-wave chunks up to 16
+    tokens for N <= 5, 2-wave chunks up to 32, then 4-wave up to 64 from N =
+    4; then a workgroup per token) and
     source-count bounds (the split kernel's single-exchange form up to seven
     snapshots, and the halved polling of up to 32 values; one group of up to
     four sources in kernel W)."""

@@ -63,8 +63,8 @@ def out_pair(M, H):
 
 
 # (M, N): the split kernel at the most tokens the automatic dispatch gives it
-# (2-wave chunks, two exchanges), then smaller calls (1-wave chunks; 2-wave
-# chunks in the Gram form), one token, the most sources the split kernel
+# (2-wave chunks, two exchanges), then smaller calls (1-wave chunks, two
+# exchanges and the Gram form's one), one token, the most sources the split kernel
 # takes, calls kernel W serves (no scratch), the hybrid of W and split chunks
 # just past the CU count (its split part at the most tokens the automatic
 # dispatch gives it), and 2-wave chunks again
