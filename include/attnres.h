@@ -127,6 +127,10 @@ extern "C" {
  * token are bounded; a wait that gives up (which a correct run never does:
  * see attnres_debug_timeouts) makes that token's out_norm (and out_mix)
  * elements that depend on it NaN instead of wrong; out_prefix is unaffected.
+ * The records such a call leaves behind can match the tags of later calls on
+ * the same token slots, so once attnres_debug_timeouts reports a nonzero
+ * count, clear the scratch (attnres_debug_reset_scratch) before trusting
+ * later results.
  *
  * Returns ATTNRES_OK or one of the negative codes above.
  */
