@@ -109,7 +109,7 @@ def check(ar, orc, case, what):
 # its Gram form (N <= 7)
 KERNELS = [((1, 0), 4, "W"), ((1, 0), 12, "W"), ((1, 0), 20, "W batched"), ((1, 4), 12, "W 4 vectors"),
            ((2, 1), 12, "S1w"), ((2, 2), 12, "S2w"), ((2, 7), 12, "S7w"), ((2, 2), 4, "S2w Gram"),
-           ((2, 1), 7, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"),
+           ((2, 1), 7, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"), ((2, 1), 8, "S1w N=8"),
            ((3, 4), 12, "hybrid 4w"),
            ((0, 0), 1, "auto")]
 
@@ -126,14 +126,16 @@ def test_eps(ar, orc, variant, N, label, eps):
 
 
 @pytest.mark.parametrize("eps", [0.0, 1e-3])
-@pytest.mark.parametrize("variant", [(2, 1), (2, 2), (2, 7), (0, 0)], ids=["S1w", "S2w", "S7w", "auto"])
-def test_eps_gram_fallback(ar, orc, variant, eps):
+@pytest.mark.parametrize("variant,N", [((2, 1), 4), ((2, 2), 4), ((2, 7), 4), ((0, 0), 4), ((0, 0), 12)],
+                         ids=["S1w", "S2w", "S7w", "auto", "auto N=12"])
+def test_eps_gram_fallback(ar, orc, variant, N, eps):
     """Cancelling sources at eps = 0 and 1e-3 through the Gram form's
-    conditioning test (N = 4: the fallback to the second exchange)."""
-    case = cancelling_eps_case(4, eps)
+    conditioning test (N = 4: the fallback to the second exchange), and the
+    same sources at N = 12 through the two exchanges."""
+    case = cancelling_eps_case(N, eps)
     ar.attnres_set_variant(*variant)
     try:
-        check(ar, orc, case, "cancelling N=4 eps=%g %s" % (eps, variant))
+        check(ar, orc, case, "cancelling N=%d eps=%g %s" % (N, eps, variant))
     finally:
         ar.attnres_set_variant(0, 0)
 

@@ -226,7 +226,7 @@ def _cancelling_case(N, noise=1e-3, M=3, H=7168, seed=5):
 @pytest.mark.parametrize("variant", [(0, 0), (2, 1), (2, 2), (2, 7)], ids=["auto", "S1w", "S2w", "S7w"],
                          indirect=True)
 @pytest.mark.parametrize("noise", [1e-3, 0.15, 0.3, 0.6])
-@pytest.mark.parametrize("N", [1, 3, 4, 7])
+@pytest.mark.parametrize("N", [1, 3, 4, 7, 8, 9, 12])
 def test_cancelling_sources(ar, orc, variant, N, noise):
     """Sources that nearly cancel.  The split kernel takes sum x^2 = alpha' G
     alpha from its one exchange for few sources.  With noise 1e-3 that form
@@ -234,8 +234,11 @@ def test_cancelling_sources(ar, orc, variant, N, noise):
     and run the second exchange; with 0.15 the conditioning bound still sends
     it there; with 0.6 (and 0.3 at N = 1) the sources cancel by a factor of
     about 12 to 57, under the bound, so the form is accepted and its rounding
-    must stay far below the tolerance.  out_norm within the parity bound of
-    the oracle either way."""
+    must stay far below the tolerance.  From 8 snapshots (two exchanges) the
+    second exchange sums the chunks' x^2 of the cancelled mixture.  out_norm
+    within the parity bound of the oracle either way."""
+    if not supported(ar, 3, N, 7168):
+        pytest.skip("variant not available for this size")
     case = case_for(("cancel", N, noise), lambda: _cancelling_case(N, noise))
     say("cancelling sources", N, noise, variant, ar.attnres_plan(case.M, N, case.H))
     gp, gn = P.run_gpu(case)
@@ -417,6 +420,8 @@ SYNC_VID = ["W", "S1w", "S2w", "S7w", "hybrid", "hybrid4w"]
 @pytest.mark.parametrize("name", ["cfg4", "cfg2"])  # N = 12: two exchanges; N = 4: the Gram form's one
 def test_deterministic(ar, variant, name):
     case = case_for(name, lambda: W.config_case(name))
+    if not supported(ar, case.M, case.N, case.H):
+        pytest.skip("variant not available for this size")
     first = P.run_gpu(case)
     for _ in range(20):
         again = P.run_gpu(case)
@@ -456,6 +461,8 @@ def test_graph_replay(ar, variant, N):
     must equal the eager call on the same inputs, bit for bit."""
     import torch
 
+    if not supported(ar, 16, N, 7168):
+        pytest.skip("variant not available for this size")
     cases = [W.make_case(cfg=70 + i, M=16, N=N, add2=True) for i in range(4)]
     c0 = cases[0]
     d = P.dev
