@@ -26,10 +26,13 @@
 //      the row (one 16-byte vector per thread).  All chunks of a token are
 //      placed on one XCD (workgroup id mod 8).  The 2(N+1) partials and the
 //      chunk's share of sum x^2 are exchanged through tagged 64-bit records
-//      with relaxed device-scope atomics (no fences); with at most eight
-//      sources the chunk's Gram matrix travels instead and one exchange gives
-//      both.  Spreads a few tokens over many CUs, which is what the
-//      latency-bound small-M calls need.
+//      with relaxed atomics (no fences), each record in two copies: one in
+//      the XCD's L2, read first, and a device-scope one, the fallback; with
+//      at most eight sources the chunk's Gram matrix travels instead and one
+//      exchange gives both.  Spreads a few tokens over many CUs, which is
+//      what the latency-bound small-M calls need.  Token slots of the
+//      scratch are handed out per call.
+//   W and S in one launch (the hybrid) just past the CU count.
 // Outputs are written with the non-temporal hint in both kernels; kernel W
 // writes out_prefix after the token's last group, right before out_norm.
 // Both reduce in a fixed order: the same inputs give the same bits, and the
