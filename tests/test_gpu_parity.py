@@ -658,18 +658,19 @@ def test_epoch_wrap(ar, orc):
 
 def test_concurrent_streams(ar, orc):
     """Split-kernel calls enqueued on two streams with no ordering between
-    them (two exchanges and the Gram form's one, 1- and 2-wave chunks): each
-    call takes its own token slots of the scratch, so calls that run at the
-    same time do not share records.  Every output against the oracle, and no
-    wait given up."""
+    them (two exchanges and the Gram form's one, 1- and 2-wave chunks, and
+    the hybrid launch's 1- and 2-wave chunks): each call takes its own token
+    slots of the scratch, so calls that run at the same time do not share
+    records.  Every output against the oracle, and no wait given up."""
     import torch
 
     cases = [W.make_case(cfg=90 + i, M=32, N=(12, 4, 8)[i % 3], add2=True) for i in range(6)]
+    cases += [W.make_case(cfg=96, M=264, N=12, add2=True), W.make_case(cfg=97, M=288, N=4, add2=True)]
     refs = [P.run_oracle(orc, c) for c in cases]
     d = P.dev
     ins = [(d(c.prefix), d(c.add), d(c.add2), [d(s) for s in c.snapshots], d(c.query), d(c.gamma)) for c in cases]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    ar.attnres_debug_reset_scratch()  # slots from 0: the 12 calls take 384 of the 512
+    ar.attnres_debug_reset_scratch()  # slots from 0: the 16 calls take 464 of the 512
     outs = []
     for rep in range(2):
         for i, c in enumerate(cases):
@@ -682,7 +683,7 @@ def test_concurrent_streams(ar, orc):
         ar.attnres_add_rmsnorm_fwd(pre, add, add2, snaps, q, g, cases[i].eps, out_prefix=op, out_norm=on,
                                    stream=s)
     torch.cuda.synchronize()
-    say("concurrent streams", [ar.attnres_plan(c.M, c.N, c.H) for c in cases[:3]])
+    say("concurrent streams", [ar.attnres_plan(c.M, c.N, c.H) for c in cases[:3] + cases[6:]])
     for k, (i, op, on) in enumerate(outs):
         P.assert_parity(P.host(op), P.host(on), *refs[i], "call %d (case %d, stream %d)" % (k, i, k % 2))
     assert ar.attnres_debug_timeouts() == 0
