@@ -279,7 +279,12 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // split chunks of the rest.
     if (long_rows && !many && M > HYBRID_WG_TOKENS && M <= HYBRID_MAX_TOKENS && plan_hybrid(M, nvec, 0, pl))
         return ATTNRES_OK;
-    if (plan_wg(M, nvec, wg_vpt, pl))
+    // Prefill-sized calls with long rows: four vectors per thread (256
+    // threads; M = 2048, N = 12: 85.98 against 90.48 us for two; M = 4096:
+    // 170.3 against 172.2; M = 8192: 343.0 against 345.6; below 2048 tokens
+    // two vectors win or tie: M = 512: 23.19 against 23.67).
+    const int vpt = !many && long_rows && nvec <= 1024 && M >= PREFILL_WG4_TOKENS ? 4 : wg_vpt;
+    if (plan_wg(M, nvec, vpt, pl))
         return ATTNRES_OK;
     return split_ok && plan_split(M, nvec, many ? 2 : 0, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
 }

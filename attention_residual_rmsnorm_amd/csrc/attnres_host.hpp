@@ -41,6 +41,9 @@ constexpr int MID_SPLIT_MIN_SNAP = 8;
 // beyond that the form with groups of two keeps more waves per CU and streams
 // faster.
 constexpr int SHORT_WG_THREADS = 256;
+// Prefill-sized calls (M >= PREFILL_WG4_TOKENS, rows of 513..1024 vectors,
+// one pass of sources) take kernel W with four vectors per thread.
+constexpr int64_t PREFILL_WG4_TOKENS = 2048;
 constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 65536;
 
 // The hybrid launch (kernel W's workgroups for the first HYBRID_WG_TOKENS

@@ -209,6 +209,10 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(384, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(300, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
+    assert ar.attnres_plan(2047, 12, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(2048, 12, 7168) == (1, 1, 256)  # prefill-sized: four vectors per thread
+    assert ar.attnres_plan(4096, 4, 8192) == (1, 1, 256)
+    assert ar.attnres_plan(4096, 13, 7168) == (1, 1, 448)  # more than 12 sources: batches, two vectors
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
     # more sources than one pass: the 2-wave split up to 31 snapshots at small

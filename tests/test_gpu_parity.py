@@ -371,12 +371,13 @@ def test_random_shapes(ar, orc, M, H, N, add2, var, cancel):
 
 def test_beyond_split_slots_and_grid(ar, orc):
     """M above the split-hidden token slots (workgroup per token; 600 tokens put
-    two workgroups on some CUs), the prefill-sized call bench.py times (1,024
-    tokens, N = 12), and M above the W grid cap (grid-stride over tokens),
+    two workgroups on some CUs), the prefill-sized calls bench.py times (1,024
+    tokens, N = 12) and the form with four vectors per thread (2,048 and
+    4,096 tokens), and M above the W grid cap (grid-stride over tokens),
     checked on sampled rows."""
     import torch
 
-    for M, H, N in ((600, 7168, 4), (1024, 7168, 12), ((1 << 20) + 5, 8, 2)):
+    for M, H, N in ((600, 7168, 4), (1024, 7168, 12), (2048, 7168, 12), (4096, 8192, 4), ((1 << 20) + 5, 8, 2)):
         case = W.make_case(cfg=61, M=M, H=H, N=N, add2=True)
         say("large M", M, H, N, ar.attnres_plan(M, N, H))
         gp, gn = P.run_gpu(case)
