@@ -246,7 +246,10 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
     //    against 5.7 us for one token, 5.2 against 6.3 for 256);
     //  * H = 3584 / 4096: with N >= 8 and M <= 64 the split still wins
-    //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us).
+    //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us),
+    //    and with N = 12 up to 96 tokens in 1-wave chunks (H = 3584, M = 80:
+    //    7.06 against 7.54; H = 4096, M = 96: 7.50 against 7.73; N = 8 and
+    //    M = 128 stay with W: 6.20 against 6.47, 7.78 against 7.87).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (many) {
         if (M <= SPLIT_MID_TOKENS && split_ok && plan_split(M, nvec, 2, pl))
@@ -256,6 +259,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
             if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
                 return ATTNRES_OK;
             if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
+                return ATTNRES_OK;
+            if (n >= MAX_SNAP && M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 1, pl))
                 return ATTNRES_OK;
         }
     } else if (n >= GRAM_MAX_SOURCES) {

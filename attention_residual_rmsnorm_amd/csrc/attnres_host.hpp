@@ -32,7 +32,8 @@ constexpr int GRAM_MAX_SOURCES = 8;
 // workgroup per token at every M and N <= 12; rows shorter than
 // LONG_ROW_VECTORS (H < 7168) are split only with N >= MID_SPLIT_MIN_SNAP and
 // M <= SPLIT_MID_TOKENS (1 wave per workgroup up to SPLIT_SMALL_TOKENS_WIDE
-// tokens); rows of LONG_ROW_VECTORS and more follow the rules above.
+// tokens), or with N = MAX_SNAP up to SPLIT_WIDE_TOKENS (1 wave); rows of
+// LONG_ROW_VECTORS and more follow the rules above.
 constexpr int SHORT_ROW_VECTORS = 256;
 constexpr int LONG_ROW_VECTORS = 896;
 constexpr int MID_SPLIT_MIN_SNAP = 8;

@@ -231,7 +231,11 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(1, 12, 3584) == (2, 7, 64)      # H < 7168, N >= 8: 1-wave chunks up to 32 tokens
     assert ar.attnres_plan(32, 8, 4096) == (2, 8, 64)
     assert ar.attnres_plan(64, 12, 3584) == (2, 4, 128)    # then 2-wave chunks up to 64
-    assert ar.attnres_plan(65, 12, 3584)[0] == 1
+    assert ar.attnres_plan(65, 12, 3584) == (2, 7, 64)     # N = 12: 1-wave chunks up to 96
+    assert ar.attnres_plan(96, 12, 4096) == (2, 8, 64)
+    assert ar.attnres_plan(97, 12, 3584)[0] == 1
+    assert ar.attnres_plan(65, 11, 3584)[0] == 1
+    assert ar.attnres_plan(65, 8, 3584)[0] == 1             # N < 12: a workgroup per token beyond 64
     assert ar.attnres_plan(1, 7, 3584)[0] == 1             # fewer sources: workgroup per token
     with pytest.raises(ar.AttnResError):
         ar.attnres_plan(1, 65, 7168)
