@@ -1267,8 +1267,8 @@ constexpr int WG_SHORT_LOOKAHEAD = 1;
 // ---------------------------------------------------------------------------
 // The hybrid launch (H of 4104..8192, a few more tokens than CUs, one pass of
 // sources): workgroups [0, wg_blocks) run kernel W on tokens [0, split_base),
-// the rest run kernel S's chunks of split_threads threads (4 to 8 waves; the
-// workgroup's other waves exit at once) on tokens [split_base, M).  With
+// the rest run kernel S's chunks of split_threads threads (1, 2 or 4 waves;
+// the workgroup's other waves exit at once) on tokens [split_base, M).  With
 // split_base = the CU count each CU holds one W token and about one chunk,
 // instead of some CUs holding two whole tokens and the others one.
 constexpr int HYBRID_WG_THREADS_MAX = 512;

@@ -585,7 +585,7 @@ def fold_suite(launcher, cold_bytes=1.1e9):
     return out
 
 
-def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 48, 64, 96, 128, 256, 288, 320, 384, 512, 1024),
+def grid_suite(launcher, Ms=(1, 2, 4, 8, 16, 32, 48, 64, 96, 128, 256, 288, 320, 384, 448, 512, 1024),
                Ns=(0, 1, 2, 4, 8, 12),
                H=7168, cold_bytes=1.1e9, max_sets=20000):
     """The metric over a grid of token and source counts (add2, automatic
