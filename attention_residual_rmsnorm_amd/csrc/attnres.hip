@@ -956,13 +956,12 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
     constexpr bool GRAM = S <= GRAM_MAX_SOURCES;
     constexpr int NV = GRAM ? S + S * (S + 1) / 2 : 2 * S; // values of the first exchange
     constexpr int NVP = (NV + 3) / 4 * 4;
-    constexpr int MAXROWS = MAXB / 16;
     static_assert(S <= 32 && NV <= 64 && NV <= REC_STRIDE && MAXC <= 64, "one lane per value and per chunk");
     // 1-2 waves per workgroup: every wave gathers the records itself (no
     // barrier after either exchange); 4-8 waves: wave 0 gathers and shares
     // through LDS (less polling traffic when many workgroups wait at once)
     constexpr bool PERWAVE = MAXB <= 128;
-    __shared__ __align__(16) float rows[MAXROWS * NVP];
+    __shared__ __align__(16) float wsum[(MAXB / 64) * NVP];
     __shared__ float red2[MAXB / 64];
     __shared__ float alpha_sh[PERWAVE ? 1 : 32];
     __shared__ float ssum_sh;
@@ -1001,42 +1000,31 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
     if (ok[0])
         store_stream(&p.out_prefix[row + v], k[NS][0]);
 
-    // A2: this chunk's partials (row sums on DPP, rows through LDS); thread
-    // v < NV adds the rows of value v and publishes it
+    // A2: this chunk's partials, each wave's totals by the butterfly (one value
+    // per lane); one wave publishes them from those lanes, more than one add
+    // the waves' totals in order through LDS (thread v < NV: value v)
     float part[NV];
     if constexpr (GRAM)
         gram_partials<S>(k, q, ok, part);
     else
         source_partials<S, 1>(k, q, ok, part);
     fence_sources<S, 1>(k);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        part[i] = row_sum(part[i]);
-    if ((tid & 15) == 0) {
-        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * NVP);
-#pragma unroll
-        for (int i = 0; i < NVP / 4; ++i)
-            r[i] = make_float4(4 * i + 0 < NV ? part[(4 * i + 0) % NV] : 0.f,
-                               4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
-                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
-                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
-    }
-    __syncthreads();
+    const float wt = wave_totals<NV>(part, lane);
+    const int wv = bfly_index<pow2_at_least(NV)>(lane);
     unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
-    if (tid < NV) { // rows in order, loaded 8 at a time so the loads overlap
-        const int nrows = nthreads >> 4;
-        float acc = rows[tid];
-        for (int r0 = 1; r0 < nrows; r0 += 8) {
-            float vr[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                vr[r] = r0 + r < nrows ? rows[(r0 + r) * NVP + tid] : 0.f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (r0 + r < nrows)
-                    acc += vr[r];
+    if (nw == 1) {
+        if (wv >= 0 && wv < NV)
+            publish(&rec1[chunk * REC1_CHUNK + wv], REC_STRIDE, tag1, wt);
+    } else {
+        if (wv >= 0 && wv < NV)
+            wsum[wave * NVP + wv] = wt;
+        __syncthreads();
+        if (tid < NV) {
+            float acc = wsum[tid];
+            for (int w = 1; w < nw; ++w)
+                acc += wsum[w * NVP + tid];
+            publish(&rec1[chunk * REC1_CHUNK + tid], REC_STRIDE, tag1, acc);
         }
-        publish(&rec1[chunk * REC1_CHUNK + tid], REC_STRIDE, tag1, acc);
     }
 
     // A3 in every wave (PERWAVE) or in wave 0: lane v < NV ends with value v

@@ -129,6 +129,86 @@ __device__ __forceinline__ float wave_max(float v)
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Wave totals of V per-lane values (V a power of two, <= 64) by a
+// butterfly that halves each lane's list at every step: at step s lanes pair
+// across lane bit step_bit(s), the lane with that bit clear keeps the lower
+// half of the list (its own plus its partner's) and the other lane the upper
+// half.  The first four pairings are DPP row permutations (row_mirror across
+// bit 3, row_half_mirror across bit 2, quad_perm across bits 1 and 0: each
+// partner has the same bits as its lane at the steps before), the last two
+// lane shuffles (bits 4 and 5); once the list has one value the remaining
+// steps add the partner's copy.  Both partners of a pair add the same two
+// values, so a total has the same bits in every lane that holds it.  All 64
+// lanes must be active.
+constexpr int step_bit(int s) { return s < 4 ? 3 - s : s; }
+
+template <int STEP>
+__device__ __forceinline__ float bfly_xchg(float v)
+{
+    if constexpr (STEP == 0)
+        return dpp<0x140>(v); // row_mirror: lane i <-> 15 - i within a row
+    else if constexpr (STEP == 1)
+        return dpp<0x141>(v); // row_half_mirror: i <-> 7 - i within 8 lanes
+    else if constexpr (STEP == 2)
+        return dpp<0x4e>(v); // quad_perm [2,3,0,1]
+    else if constexpr (STEP == 3)
+        return dpp<0xb1>(v); // quad_perm [1,0,3,2]
+    else if constexpr (STEP == 4)
+        return __shfl_xor(v, 16);
+    else
+        return __shfl_xor(v, 32);
+}
+
+template <int L, int STEP>
+__device__ __forceinline__ void bfly_steps(float* w, int lane)
+{
+    if constexpr (STEP < 6) {
+        if constexpr (L > 1) {
+            const bool upper = (lane >> step_bit(STEP)) & 1;
+#pragma unroll
+            for (int i = 0; i < L / 2; ++i) {
+                const float keep = upper ? w[i + L / 2] : w[i];
+                const float send = upper ? w[i] : w[i + L / 2];
+                w[i] = keep + bfly_xchg<STEP>(send);
+            }
+            bfly_steps<L / 2, STEP + 1>(w, lane);
+        } else {
+            w[0] = w[0] + bfly_xchg<STEP>(w[0]);
+            bfly_steps<1, STEP + 1>(w, lane);
+        }
+    }
+}
+
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+
+// The value whose total wave_totals leaves in `lane`, or -1 where the lane
+// holds a second copy (lane bits the halving steps did not use are not all
+// zero).
+template <int V>
+__device__ __forceinline__ int bfly_index(int lane)
+{
+    int idx = 0, used = 0;
+#pragma unroll
+    for (int s = 0; (V >> (s + 1)) >= 1; ++s) {
+        idx += ((lane >> step_bit(s)) & 1) * (V >> (s + 1));
+        used |= 1 << step_bit(s);
+    }
+    return (lane & ~used & 63) == 0 ? idx : -1;
+}
+
+template <int NV>
+__device__ __forceinline__ float wave_totals(const float (&part)[NV], int lane)
+{
+    constexpr int V = pow2_at_least(NV);
+    static_assert(V <= 64, "one lane per value");
+    float w[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        w[i] = i < NV ? part[i % NV] : 0.f;
+    bfly_steps<V, 0>(w, lane);
+    return w[0];
+}
+
 // ---- cross-workgroup exchange --------------------------------------------
 //
 // Workgroups that share a token exchange binary32 partial sums through 64-bit
