@@ -129,34 +129,46 @@ __device__ __forceinline__ float wave_max(float v)
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// Wave totals of V per-lane values (V a power of two, <= 64) by a
-// butterfly that halves each lane's list at every step: at step s lanes pair
-// across lane bit step_bit(s), the lane with that bit clear keeps the lower
-// half of the list (its own plus its partner's) and the other lane the upper
-// half.  The first four pairings are DPP row permutations (row_mirror across
-// bit 3, row_half_mirror across bit 2, quad_perm across bits 1 and 0: each
-// partner has the same bits as its lane at the steps before), the last two
-// lane shuffles (bits 4 and 5); once the list has one value the remaining
-// steps add the partner's copy.  Both partners of a pair add the same two
-// values, so a total has the same bits in every lane that holds it.  All 64
-// lanes must be active.
-constexpr int step_bit(int s) { return s < 4 ? 3 - s : s; }
-
+// Wave totals of V per-lane values (V a power of two, <= 64) by a butterfly
+// that halves each lane's list at every step: at step s lanes pair across
+// lane bit 5 - s, the lane with that bit clear keeps the lower half of the
+// list (its own plus its partner's) and the other lane the upper half, so
+// after log2(V) steps lane v * (64 / V) holds the total of value v, and the
+// remaining steps add the partner's copy.  The two steps across 16-lane rows
+// use gfx950's v_permlane32_swap / v_permlane16_swap: given (lower half, upper
+// half), the swap leaves in each lane the two terms of the half it keeps, so
+// a pair costs one swap and one add.  The four steps within a row use DPP row
+// permutations (row_mirror across bit 3, row_half_mirror across bit 2,
+// quad_perm across bits 1 and 0; each partner has the same higher bits as its
+// lane) and a select of the half to send.  Where both partners end with the
+// same total they add the same two values, so it has the same bits in both.
+// All 64 lanes must be active.
 template <int STEP>
-__device__ __forceinline__ float bfly_xchg(float v)
+__device__ __forceinline__ float bfly_dpp(float v)
 {
-    if constexpr (STEP == 0)
+    if constexpr (STEP == 2)
         return dpp<0x140>(v); // row_mirror: lane i <-> 15 - i within a row
-    else if constexpr (STEP == 1)
-        return dpp<0x141>(v); // row_half_mirror: i <-> 7 - i within 8 lanes
-    else if constexpr (STEP == 2)
-        return dpp<0x4e>(v); // quad_perm [2,3,0,1]
     else if constexpr (STEP == 3)
-        return dpp<0xb1>(v); // quad_perm [1,0,3,2]
+        return dpp<0x141>(v); // row_half_mirror: i <-> 7 - i within 8 lanes
     else if constexpr (STEP == 4)
-        return __shfl_xor(v, 16);
+        return dpp<0x4e>(v); // quad_perm [2,3,0,1]
     else
-        return __shfl_xor(v, 32);
+        return dpp<0xb1>(v); // quad_perm [1,0,3,2]
+}
+
+// Steps 0 and 1: lanes 0-31 keep lo and receive lo from lanes 32-63, which
+// keep hi and receive hi from lanes 0-31 (step 0); the same between even and
+// odd rows (step 1).  Returns the sum of the two terms each lane keeps.
+template <int STEP>
+__device__ __forceinline__ float bfly_swap_add(float lo, float hi)
+{
+    if constexpr (STEP == 0) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
 }
 
 template <int L, int STEP>
@@ -164,16 +176,25 @@ __device__ __forceinline__ void bfly_steps(float* w, int lane)
 {
     if constexpr (STEP < 6) {
         if constexpr (L > 1) {
-            const bool upper = (lane >> step_bit(STEP)) & 1;
+            if constexpr (STEP < 2) {
 #pragma unroll
-            for (int i = 0; i < L / 2; ++i) {
-                const float keep = upper ? w[i + L / 2] : w[i];
-                const float send = upper ? w[i] : w[i + L / 2];
-                w[i] = keep + bfly_xchg<STEP>(send);
+                for (int i = 0; i < L / 2; ++i)
+                    w[i] = bfly_swap_add<STEP>(w[i], w[i + L / 2]);
+            } else {
+                const bool upper = (lane >> (5 - STEP)) & 1;
+#pragma unroll
+                for (int i = 0; i < L / 2; ++i) {
+                    const float keep = upper ? w[i + L / 2] : w[i];
+                    const float send = upper ? w[i] : w[i + L / 2];
+                    w[i] = keep + bfly_dpp<STEP>(send);
+                }
             }
             bfly_steps<L / 2, STEP + 1>(w, lane);
         } else {
-            w[0] = w[0] + bfly_xchg<STEP>(w[0]);
+            if constexpr (STEP < 2)
+                w[0] = bfly_swap_add<STEP>(w[0], w[0]);
+            else
+                w[0] = w[0] + bfly_dpp<STEP>(w[0]);
             bfly_steps<1, STEP + 1>(w, lane);
         }
     }
@@ -182,18 +203,11 @@ __device__ __forceinline__ void bfly_steps(float* w, int lane)
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
 // The value whose total wave_totals leaves in `lane`, or -1 where the lane
-// holds a second copy (lane bits the halving steps did not use are not all
-// zero).
+// holds another lane's copy.
 template <int V>
 __device__ __forceinline__ int bfly_index(int lane)
 {
-    int idx = 0, used = 0;
-#pragma unroll
-    for (int s = 0; (V >> (s + 1)) >= 1; ++s) {
-        idx += ((lane >> step_bit(s)) & 1) * (V >> (s + 1));
-        used |= 1 << step_bit(s);
-    }
-    return (lane & ~used & 63) == 0 ? idx : -1;
+    return lane % (64 / V) == 0 ? lane / (64 / V) : -1;
 }
 
 template <int NV>

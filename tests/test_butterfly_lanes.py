@@ -1,7 +1,9 @@
 """CPU model of the split kernel's wave totals (wave_totals / bfly_index in
 csrc/attnres_device.hpp): 64 lanes, each with V per-lane values, halve their
-lists at six steps whose partners come from DPP row permutations (row_mirror,
-row_half_mirror, two quad_perms) and xor-16 / xor-32 shuffles.
+lists at six steps across lane bits 5, 4, ..., 0, whose partners come from
+v_permlane32_swap / v_permlane16_swap (lanes l and l ^ 32, l and l ^ 16, each
+keeping the two terms of its own half) and DPP row permutations (row_mirror,
+row_half_mirror, two quad_perms).
 
 Checked for every value count 1..64 the kernel can use: at each halving step a
 lane's partner has the other value of the split bit (so one keeps the lower
@@ -16,21 +18,21 @@ import pytest
 
 
 def step_bit(s):
-    return 3 - s if s < 4 else s
+    return 5 - s
 
 
 def partner(step, lane):
-    if step == 0:  # row_mirror: lane i <-> 15 - i within a 16-lane row
-        return (lane & ~15) | (15 - (lane & 15))
-    if step == 1:  # row_half_mirror: i <-> 7 - i within 8 lanes
-        return (lane & ~7) | (7 - (lane & 7))
-    if step == 2:  # quad_perm [2,3,0,1]
-        return lane ^ 2
-    if step == 3:  # quad_perm [1,0,3,2]
-        return lane ^ 1
-    if step == 4:
+    if step == 0:  # v_permlane32_swap: lanes 0-31 with lanes 32-63
+        return lane ^ 32
+    if step == 1:  # v_permlane16_swap: even rows with odd rows
         return lane ^ 16
-    return lane ^ 32
+    if step == 2:  # row_mirror: lane i <-> 15 - i within a 16-lane row
+        return (lane & ~15) | (15 - (lane & 15))
+    if step == 3:  # row_half_mirror: i <-> 7 - i within 8 lanes
+        return (lane & ~7) | (7 - (lane & 7))
+    if step == 4:  # quad_perm [2,3,0,1]
+        return lane ^ 2
+    return lane ^ 1  # quad_perm [1,0,3,2]
 
 
 def pow2_at_least(n):
@@ -38,12 +40,7 @@ def pow2_at_least(n):
 
 
 def bfly_index(V, lane):
-    idx, used, s = 0, 0, 0
-    while (V >> (s + 1)) >= 1:
-        idx += ((lane >> step_bit(s)) & 1) * (V >> (s + 1))
-        used |= 1 << step_bit(s)
-        s += 1
-    return idx if (lane & ~used & 63) == 0 else -1
+    return lane // (64 // V) if lane % (64 // V) == 0 else -1
 
 
 def wave_totals(part):
