@@ -17,8 +17,8 @@
 //      in registers) are loaded in a software pipeline, source-major across
 //      the waves, and mixed two at a time as they arrive (up to four
 //      sources as one group), under a running softmax maximum and sum; each
-//      group's partials are summed on DPP within rows and by one wave across
-//      rows.  With short rows (at most 256 threads of one vector) all sources
+//      group's partials are summed per wave by a butterfly of lane swaps and
+//      DPP permutations, then across the waves by one thread per value.  With short rows (at most 256 threads of one vector) all sources
 //      form one group, summed in one round.  No inter-workgroup
 //      communication.  Used when there are many tokens, for short rows, and
 //      for more than 12 sources (in batches of 12).
@@ -427,46 +427,34 @@ __device__ __forceinline__ float uniform(float v)
 // argument, so the library's rescaling around it is not needed.
 __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v); }
 
-// Workgroup totals of NV <= 8 per-thread values in two levels.  Each 16-lane
-// row is summed on DPP and lane 0 of the row stores its NV sums (row r at
-// rows[8r..8r+7]; the 64 - blockDim.x/16 rows of absent waves hold zeros);
-// after a barrier wave 0 adds the rows: lane l takes value l/8 over rows
-// l%8, l%8 + 8, ..., l%8 + 56 in order, three DPP steps add the 8 lanes of a
-// value, and lane 8v stores tot[v].  After a second barrier every thread
-// reads the same bits.
-template <int NV>
-__device__ __forceinline__ void group_sums(float (&part)[NV], float* rows, float* tot, int tid)
+// Workgroup totals of NV <= 8 per-thread values in two levels.  Each wave
+// sums its values by the butterfly of wave_totals (value v ends in lane
+// v * 64 / V) and those lanes store them at rows[8 * wave + v]; after a
+// barrier thread v < NV adds the present waves' entries in wave order (all
+// MAXW read at once, those of absent waves dropped by a select, never added)
+// and stores tot[v].  After a second barrier every thread reads the same bits.
+template <int NV, int MAXW>
+__device__ __forceinline__ void group_sums(const float (&part)[NV], float* rows, float* tot, int tid,
+                                           int nthreads)
 {
-    static_assert(NV >= 1 && NV <= 8, "at most 8 values per group");
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        part[i] = row_sum(part[i]);
-    if ((tid & 15) == 0) {
-        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * 8);
-        r[0] = make_float4(part[0], 1 < NV ? part[1 % NV] : 0.f, 2 < NV ? part[2 % NV] : 0.f,
-                           3 < NV ? part[3 % NV] : 0.f);
-        if (NV > 4)
-            r[1] = make_float4(4 < NV ? part[4 % NV] : 0.f, 5 < NV ? part[5 % NV] : 0.f,
-                               6 < NV ? part[6 % NV] : 0.f, 7 < NV ? part[7 % NV] : 0.f);
-    }
+    static_assert(NV >= 1 && NV <= 8 && MAXW >= 1 && MAXW <= 16, "at most 8 values and 16 waves");
+    const int lane = tid & 63, wave = tid >> 6;
+    const float wt = wave_totals<NV>(part, lane);
+    const int v = bfly_index<pow2_at_least(NV)>(lane);
+    if (v >= 0 && v < NV)
+        rows[8 * wave + v] = wt;
     __syncthreads();
-    if (tid < 64) {
-        // lanes of values v >= NV add stale entries, but only among themselves
-        const int v = tid >> 3, r0 = tid & 7;
-        const float* base = rows + r0 * 8 + v;
-        float t[8];
+    if (tid < NV) {
+        const int nw = nthreads >> 6;
+        float t[MAXW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            t[i] = base[64 * i];
+        for (int r = 0; r < MAXW; ++r)
+            t[r] = rows[8 * r + tid];
         float acc = t[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i)
-            acc += t[i];
-        acc = acc + dpp<0xb1>(acc);  // quad_perm [1,0,3,2]
-        acc = acc + dpp<0x4e>(acc);  // quad_perm [2,3,0,1]
-        acc = acc + dpp<0x141>(acc); // row_half_mirror: the two quads of each 8 lanes
-        if (r0 == 0 && v < NV)
-            tot[v] = acc;
+        for (int r = 1; r < MAXW; ++r)
+            acc = r < nw ? acc + t[r] : acc;
+        tot[tid] = acc;
     }
     __syncthreads();
 }
@@ -476,9 +464,7 @@ __device__ __forceinline__ void group_sums(float (&part)[NV], float* rows, float
 // stores its NV sums at rows[32r..32r+NV); after a barrier thread v < NV adds
 // value v over the present rows in order and stores tot[v].  After a second
 // barrier every thread reads the same bits.  One round for all of a token's
-// sources where the rows are short (few threads per token).  A kernel uses
-// either this or group_sums for all its groups: this one leaves entries that
-// group_sums expects to be zero.
+// sources where the rows are short (few threads per token).
 template <int NV, int MAXROWS>
 __device__ __forceinline__ void group_sums_wide(float (&part)[NV], float* rows, float* tot, int tid, int nthreads)
 {
@@ -522,7 +508,7 @@ struct Mix {
 };
 
 // A2-A4 for one group of n consecutive sources ks[0..n).
-template <int n, int VPT, bool FIRST, int MAXROWS>
+template <int n, int VPT, bool FIRST, int MAXROWS, int MAXW>
 __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q, const bool* ok, Mix<VPT>& mx,
                                           float* rows, float* tot, const Params& p, int tid, int nthreads)
 {
@@ -536,7 +522,7 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
     if constexpr (MAXROWS > 0)
         group_sums_wide<2 * n, MAXROWS>(part, rows, tot, tid, nthreads);
     else
-        group_sums<2 * n>(part, rows, tot, tid);
+        group_sums<2 * n, MAXW>(part, rows, tot, tid, nthreads);
     float z[n];
 #pragma unroll
     for (int s = 0; s < n; ++s)
@@ -623,12 +609,12 @@ constexpr int ONE_GROUP = 4;
 constexpr int TOT_SLOT = 32;
 static_assert(2 * (MAX_SNAP + 1) <= TOT_SLOT, "one pass of sources in one group");
 
-// Kernel W's LDS floats per group slot: group_sums' 64 rows of 8 values, or
-// (G > ONE_GROUP) group_sums_wide's MAXB/16 rows of 32.
+// Kernel W's LDS floats per group slot: group_sums' 8 values for each of the
+// MAXB/64 waves, or (G > ONE_GROUP) group_sums_wide's MAXB/16 rows of 32.
 template <int G, int MAXB>
 constexpr int row_slot()
 {
-    return G > ONE_GROUP ? 32 * (MAXB / 16) : 64 * 8;
+    return G > ONE_GROUP ? 32 * (MAXB / 16) : 8 * (MAXB / 64);
 }
 
 template <int S, int G>
@@ -654,9 +640,9 @@ constexpr int group_start(int i)
 // group GI + LA, then (batch with p', step 0) apply A1, then mix group GI.
 // Group gi uses LDS slot gi % 2.  Any reuse of a slot is ordered by the two
 // barriers of every group: a thread writes a group's rows
-// only after the previous group's second barrier (wave 0 has read that
-// group's rows), and wave 0 writes a group's totals only after its first
-// barrier (every thread has read the previous totals).  FIRSTBATCH: the first
+// only after the previous group's second barrier (the threads that add the
+// rows have read that group's), and a group's totals are written only after
+// its first barrier (every thread has read the previous totals).  FIRSTBATCH: the first
 // group starts the running softmax.
 template <int S, int G, int LA, int GI, bool HASP, bool FIRSTBATCH, bool ADD2, int VPT, int MAXB>
 __device__ __forceinline__ void stream_groups(const Params& p, const uint4* const* snap, int64_t row,
@@ -674,8 +660,8 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
             fold_add<ADD2, VPT>(a, b, c, k[0]); // A1 (p' stored after the batch, see stream_batch)
         constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
         constexpr int wide_rows = G > ONE_GROUP ? MAXB / 16 : 0;
-        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, wide_rows>(&k[g0], q, ok, mx, rows[GI & 1], tot[GI & 1], p,
-                                                                   tid, nthreads);
+        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, wide_rows, MAXB / 64>(&k[g0], q, ok, mx, rows[GI & 1],
+                                                                              tot[GI & 1], p, tid, nthreads);
         stream_groups<S, G, LA, GI + 1, HASP, FIRSTBATCH, ADD2, VPT, MAXB>(p, snap, row, vc, a, b, c, k, q, ok, mx,
                                                                            rows, tot, tid, nthreads);
     }
@@ -702,21 +688,14 @@ __device__ __forceinline__ void stream_batch(const Params& p, const uint4* const
     }
 }
 
-// LDS set-up shared by both forms of kernel W: group_sums' entries of absent
-// waves stay zero (ordered before use by the first barrier); group_sums_wide
-// (G > ONE_GROUP) reads present rows only.
-template <int MAXW, int G, int MAXB>
-__device__ __forceinline__ void wg_prologue(float* rows, float* red2, int tid, int nthreads)
+// LDS set-up shared by both forms of kernel W: A5's per-wave sums of absent
+// waves stay zero (ordered before use by the barriers of the first group).
+template <int MAXW>
+__device__ __forceinline__ void wg_prologue(float* red2, int tid, int nthreads)
 {
     const int nw = nthreads >> 6;
     if (tid < MAXW && tid >= nw)
         red2[tid] = 0.f;
-    if constexpr (G <= ONE_GROUP) {
-        static_assert(row_slot<G, MAXB>() == 64 * 8, "group_sums' slot");
-        for (int i = tid; i < 2 * 64 * 8; i += nthreads)
-            if ((i & 511) >= nthreads / 2) // row (i & 511) / 8 >= nthreads / 16
-                rows[i] = 0.f;
-    }
 }
 
 // A5 (and the optional mixture output) of one token from the running softmax
@@ -775,7 +754,7 @@ __device__ __forceinline__ void wg_tokens(const Params& p, int64_t t0, int64_t t
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int nvec = p.nvec;
-    wg_prologue<MAXW, G, MAXB>(&rows[0][0], red2, tid, nthreads);
+    wg_prologue<MAXW>(red2, tid, nthreads);
 
     for (int64_t t = t0; t < tend; t += stride) {
         const int64_t row = t * (int64_t)nvec;
@@ -834,7 +813,7 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int nvec = p.nvec;
-    wg_prologue<MAXW, G, MAXB>(&rows[0][0], red2, tid, nthreads);
+    wg_prologue<MAXW>(red2, tid, nthreads);
 
     for (int64_t t = blockIdx.x; t < p.M; t += gridDim.x) {
         const int64_t row = t * (int64_t)nvec;
