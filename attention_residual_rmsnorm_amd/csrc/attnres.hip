@@ -460,39 +460,34 @@ __device__ __forceinline__ void group_sums(const float (&part)[NV], float* rows,
 }
 
 // Workgroup totals of NV <= 32 per-thread values, for workgroups of at most
-// 16 * MAXROWS threads: each 16-lane row is summed on DPP and lane 0 of row r
-// stores its NV sums at rows[32r..32r+NV); after a barrier thread v < NV adds
-// value v over the present rows in order and stores tot[v].  After a second
-// barrier every thread reads the same bits.  One round for all of a token's
-// sources where the rows are short (few threads per token).
-template <int NV, int MAXROWS>
-__device__ __forceinline__ void group_sums_wide(float (&part)[NV], float* rows, float* tot, int tid, int nthreads)
+// MAXW waves: each wave sums its values by the butterfly of wave_totals and
+// the lanes holding the totals store them at rows[32 * wave + v]; after a
+// barrier thread v < NV adds value v over the present waves in order (all
+// MAXW entries read at once, those of absent waves dropped by a select, never
+// added) and stores tot[v].  After a second barrier every thread reads the
+// same bits.  One round for all of a token's sources where the rows are short
+// (few threads per token).
+template <int NV, int MAXW>
+__device__ __forceinline__ void group_sums_wide(const float (&part)[NV], float* rows, float* tot, int tid,
+                                                int nthreads)
 {
     static_assert(NV >= 1 && NV <= 32, "at most 32 values per group");
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        part[i] = row_sum(part[i]);
-    if ((tid & 15) == 0) {
-        float4* r = reinterpret_cast<float4*>(rows + (tid >> 4) * 32);
-#pragma unroll
-        for (int i = 0; i < (NV + 3) / 4; ++i)
-            r[i] = make_float4(part[4 * i], 4 * i + 1 < NV ? part[(4 * i + 1) % NV] : 0.f,
-                               4 * i + 2 < NV ? part[(4 * i + 2) % NV] : 0.f,
-                               4 * i + 3 < NV ? part[(4 * i + 3) % NV] : 0.f);
-    }
+    const int lane = tid & 63, wave = tid >> 6;
+    const float wt = wave_totals<NV>(part, lane);
+    const int v = bfly_index<pow2_at_least(NV)>(lane);
+    if (v >= 0 && v < NV)
+        rows[32 * wave + v] = wt;
     __syncthreads();
     if (tid < NV) {
-        // all MAXROWS entries read at once; those of absent rows (stale) are
-        // dropped by a select, never added
-        const int nrows = nthreads >> 4;
-        float t[MAXROWS];
+        const int nw = nthreads >> 6;
+        float t[MAXW];
 #pragma unroll
-        for (int r = 0; r < MAXROWS; ++r)
+        for (int r = 0; r < MAXW; ++r)
             t[r] = rows[32 * r + tid];
         float acc = t[0];
 #pragma unroll
-        for (int r = 1; r < MAXROWS; ++r)
-            acc += r < nrows ? t[r] : 0.f;
+        for (int r = 1; r < MAXW; ++r)
+            acc = r < nw ? acc + t[r] : acc;
         tot[tid] = acc;
     }
     __syncthreads();
@@ -508,7 +503,7 @@ struct Mix {
 };
 
 // A2-A4 for one group of n consecutive sources ks[0..n).
-template <int n, int VPT, bool FIRST, int MAXROWS, int MAXW>
+template <int n, int VPT, bool FIRST, bool WIDE, int MAXW>
 __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q, const bool* ok, Mix<VPT>& mx,
                                           float* rows, float* tot, const Params& p, int tid, int nthreads)
 {
@@ -519,8 +514,8 @@ __device__ __forceinline__ void mix_group(const uint4 (*ks)[VPT], const uint4* q
         part[2 * s] = v.x;
         part[2 * s + 1] = v.y;
     }
-    if constexpr (MAXROWS > 0)
-        group_sums_wide<2 * n, MAXROWS>(part, rows, tot, tid, nthreads);
+    if constexpr (WIDE)
+        group_sums_wide<2 * n, MAXW>(part, rows, tot, tid, nthreads);
     else
         group_sums<2 * n, MAXW>(part, rows, tot, tid, nthreads);
     float z[n];
@@ -609,12 +604,12 @@ constexpr int ONE_GROUP = 4;
 constexpr int TOT_SLOT = 32;
 static_assert(2 * (MAX_SNAP + 1) <= TOT_SLOT, "one pass of sources in one group");
 
-// Kernel W's LDS floats per group slot: group_sums' 8 values for each of the
-// MAXB/64 waves, or (G > ONE_GROUP) group_sums_wide's MAXB/16 rows of 32.
+// Kernel W's LDS floats per group slot: 8 values (group_sums) or, with G >
+// ONE_GROUP, 32 (group_sums_wide) for each of the MAXB/64 waves.
 template <int G, int MAXB>
 constexpr int row_slot()
 {
-    return G > ONE_GROUP ? 32 * (MAXB / 16) : 8 * (MAXB / 64);
+    return (G > ONE_GROUP ? 32 : 8) * (MAXB / 64);
 }
 
 template <int S, int G>
@@ -659,8 +654,7 @@ __device__ __forceinline__ void stream_groups(const Params& p, const uint4* cons
         if constexpr (HASP && GI == 0)
             fold_add<ADD2, VPT>(a, b, c, k[0]); // A1 (p' stored after the batch, see stream_batch)
         constexpr int g0 = group_start<S, G>(GI), g1 = group_start<S, G>(GI + 1);
-        constexpr int wide_rows = G > ONE_GROUP ? MAXB / 16 : 0;
-        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, wide_rows, MAXB / 64>(&k[g0], q, ok, mx, rows[GI & 1],
+        mix_group<g1 - g0, VPT, FIRSTBATCH && GI == 0, (G > ONE_GROUP), MAXB / 64>(&k[g0], q, ok, mx, rows[GI & 1],
                                                                               tot[GI & 1], p, tid, nthreads);
         stream_groups<S, G, LA, GI + 1, HASP, FIRSTBATCH, ADD2, VPT, MAXB>(p, snap, row, vc, a, b, c, k, q, ok, mx,
                                                                            rows, tot, tid, nthreads);
@@ -745,8 +739,8 @@ __device__ __forceinline__ void wg_tokens(const Params& p, int64_t t0, int64_t t
 {
     constexpr int S = NS + 1;
     constexpr int MAXW = MAXB / 64;
-    static_assert(MAXB / 16 <= 64, "rows of one group slot");
-    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 32 rows");
+    static_assert(MAXB / 64 <= 16, "waves of one group slot");
+    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 8 waves");
     __shared__ __align__(16) float rows[2][row_slot<G, MAXB>()];
     __shared__ __align__(16) float tot[2][TOT_SLOT];
     __shared__ float red2[MAXW];
@@ -804,7 +798,7 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 {
     constexpr int B = MAX_SNAP;
     constexpr int MAXW = MAXB / 64;
-    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 32 rows");
+    static_assert(G <= ONE_GROUP || MAXB <= 512, "group_sums_wide: at most 8 waves");
     __shared__ __align__(16) float rows[2][row_slot<G, MAXB>()];
     __shared__ __align__(16) float tot[2][TOT_SLOT];
     __shared__ float red2[MAXW];
