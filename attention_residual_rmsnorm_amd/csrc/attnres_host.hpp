@@ -40,12 +40,14 @@ constexpr int MID_SPLIT_MIN_SNAP = 8;
 // Kernel W's single-group form (one vector per thread, at most
 // SHORT_WG_THREADS threads) while M * threads <= SHORT_WG_MAX_THREADS_TOTAL:
 // beyond that the form with groups of two keeps more waves per CU and streams
-// faster.
+// faster at N = 12 (H = 896, M = 2,048: 13.1 against 14.0 us; up to the bound
+// the single group wins, e.g. M = 1,024: 8.8 against 8.9, and H = 2048, M =
+// 384: 8.2 against 8.7).
 constexpr int SHORT_WG_THREADS = 256;
 // Prefill-sized calls (M >= PREFILL_WG4_TOKENS, rows of 513..1024 vectors,
 // one pass of sources) take kernel W with four vectors per thread.
 constexpr int64_t PREFILL_WG4_TOKENS = 2048;
-constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 65536;
+constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 131072;
 
 // The hybrid launch (kernel W's workgroups for the first HYBRID_WG_TOKENS
 // tokens, one token each, and split chunks of 1, 2 or 4 waves for the rest:

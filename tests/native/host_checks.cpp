@@ -121,14 +121,14 @@ int main()
                 }
         }
     }
-    // kernel W's single-group form: short rows, up to 65536 threads per call
+    // kernel W's single-group form: short rows, up to 131072 threads per call
     {
         Plan pl;
-        EXPECT(make_plan(512, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && pl.threads == 128 &&
+        EXPECT(make_plan(1024, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && pl.threads == 128 &&
                pl.single_group);
-        EXPECT(make_plan(513, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
-        EXPECT(make_plan(256, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.threads == 256 && pl.single_group);
-        EXPECT(make_plan(257, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(1025, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(512, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.threads == 256 && pl.single_group);
+        EXPECT(make_plan(513, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
         EXPECT(make_plan(1, 12, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 2);
         EXPECT(make_plan(1, 4, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
         EXPECT(make_plan(1, 12, 7168, 1, 1, pl) == ATTNRES_OK && pl.threads == 896 && !pl.single_group);
