@@ -73,26 +73,6 @@ __device__ __forceinline__ float dpp(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over each group of 4 consecutive lanes (a quad), returned in all four
-// lanes with identical bits (both partners of a DPP exchange add the same two
-// values).  All 64 lanes must be active.
-__device__ __forceinline__ float quad_sum(float v)
-{
-    v = v + dpp<0xb1>(v); // quad_perm [1,0,3,2]
-    v = v + dpp<0x4e>(v); // quad_perm [2,3,0,1]
-    return v;
-}
-
-// Sum over each 16-lane DPP row, returned in all 16 lanes with identical bits.
-// All 64 lanes must be active.
-__device__ __forceinline__ float row_sum(float v)
-{
-    v = quad_sum(v);
-    v = v + dpp<0x141>(v); // row_half_mirror: pairs quads 0-1, 2-3
-    v = v + dpp<0x140>(v); // row_mirror: pairs the two halves of a row
-    return v;
-}
-
 // Maximum over each 16-lane DPP row, returned in all 16 lanes.  All 64 lanes
 // must be active.
 __device__ __forceinline__ float row_max(float v)
@@ -102,19 +82,6 @@ __device__ __forceinline__ float row_max(float v)
     v = fmaxf(v, dpp<0x141>(v));
     v = fmaxf(v, dpp<0x140>(v));
     return v;
-}
-
-// Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
-// lane: the four 16-lane row sums are read as scalars and added in a fixed
-// order.  All 64 lanes must be active.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v = row_sum(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
 }
 
 // Maximum over the 64 lanes of a wave, in every lane (the four row maxima read
@@ -221,6 +188,16 @@ __device__ __forceinline__ float wave_totals(const float (&part)[NV], int lane)
         w[i] = i < NV ? part[i % NV] : 0.f;
     bfly_steps<V, 0>(w, lane);
     return w[0];
+}
+
+// Sum over the 64 lanes of a wave, returned identically (bit for bit) in every
+// lane: the butterfly with one value, so every step adds the partner's copy
+// (two lane swaps across rows, four DPP steps within them).  All 64 lanes must
+// be active.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    const float part[1] = {v};
+    return wave_totals<1>(part, 0);
 }
 
 // ---- cross-workgroup exchange --------------------------------------------
