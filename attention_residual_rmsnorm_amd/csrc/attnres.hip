@@ -698,7 +698,7 @@ __device__ __forceinline__ void wg_prologue(float* red2, int tid, int nthreads)
 //   scale = 1/(den*sqrt(mean((x/den)^2) + eps)) = 1/sqrt(mean(x^2) + eps*den^2).
 template <int VPT, int MAXW>
 __device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, const uint4* g, const Params& p,
-                                          int64_t row, float* red2, int tid, int nthreads)
+                                          int64_t row, float* red2, int tid, int nthreads, bool more)
 {
     const int lane = tid & 63, wave = tid >> 6;
     float sx = 0.f;
@@ -730,7 +730,8 @@ __device__ __forceinline__ void wg_finish(const Mix<VPT>& mx, const bool* ok, co
             if (ok[j])
                 store_stream(&p.out_mix[row + tid + j * nthreads], pack_scaled(mx.x[j], inv));
     }
-    __syncthreads(); // LDS reuse by the next token
+    if (more)
+        __syncthreads(); // LDS reuse by the next token (a uniform branch)
 }
 
 // Kernel W's body: tokens t0, t0 + stride, ... below tend, one at a time.
@@ -771,7 +772,7 @@ __device__ __forceinline__ void wg_tokens(const Params& p, int64_t t0, int64_t t
         stream_batch<S, G, LA, true, true, ADD2, VPT, MAXB>(p, p.snap, row, vc, a, b, c, k, q, ok, mx, rows, tot, tid,
                                                       nthreads);
         // A5
-        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
+        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads, t + stride < tend);
     }
 }
 
@@ -842,7 +843,7 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
             stream_batch<NB_LAST, G, LA, false, false, ADD2, VPT, MAXB>(p, pl.more + pl.n_full * B, row, vc, a, b, c, k,
                                                                   q, ok, mx, rows, tot, tid, nthreads);
         }
-        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads);
+        wg_finish<VPT, MAXW>(mx, ok, g, p, row, red2, tid, nthreads, t + gridDim.x < p.M);
     }
 }
 
