@@ -28,7 +28,7 @@
 //      chunk's share of sum x^2 are exchanged through tagged 64-bit records
 //      with relaxed atomics (no fences), each record in two copies: one in
 //      the XCD's L2, read first, and a device-scope one, the fallback; with
-//      at most eight sources the chunk's Gram matrix travels instead and one
+//      at most six sources the chunk's Gram matrix travels instead and one
 //      exchange gives both.  Spreads a few tokens over many CUs, which is
 //      what the latency-bound small-M calls need.  Token slots of the
 //      scratch are handed out per call.

@@ -218,22 +218,22 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // Automatic, from per-call times of every variant on MI355X (graph
     // replay, inputs cold in HBM, M = 1..512, N = 1..12).  At H = 7168, one
     // pass of sources:
-    //  * N >= 8: 1-wave chunks (14 per token, every chunk's records in flight
-    //    at once) up to 48 tokens, 4-wave chunks up to 64, 2-wave chunks up to
-    //    96 (M = 1, N = 12: 5.49 against 6.07 us for 2-wave chunks and 9.40
-    //    for one workgroup per token; M = 16: 6.43 against 7.21; M = 48: 7.48
-    //    against 7.67 for 4-wave chunks; M = 64: 4-wave 7.96 against 8.64 for
-    //    2-wave; M = 80 and 96: 2-wave 9.15 and 9.54 against 10.13 and 10.35
-    //    for W, N = 8 7.97 and 8.14 against 8.26 and 8.50; from 112 tokens
-    //    within 0.1-0.4 us of W);
-    //  * 2 <= N <= 7 (the Gram form's one exchange): 1-wave chunks up to 16
-    //    tokens while the form's values fit one polling round (N <= 5: at
-    //    most 27), 2-wave chunks up to 32 tokens, then 4-wave chunks up to 64
-    //    from N = 4 on (M = 1, N = 4: 4.72 against 5.01 us for 2-wave chunks;
-    //    M = 16, N = 5: 5.64 against 5.70; N = 6, whose 35 values take two
-    //    rounds: 1-wave 6.10 against 5.95 at M = 8; M = 24, N = 3: 2-wave
-    //    5.39 against 5.43 for 1-wave and 5.67 for W; M = 64, N = 7: 7.24
-    //    against 7.91 for W);
+    //  * N >= 6 (two exchanges): 1-wave chunks (14 per token, every chunk's
+    //    records in flight at once) up to 48 tokens, and up to 64 with at
+    //    most 8 snapshots (M = 64, N = 8: 7.10 against 7.16 us for 4-wave
+    //    chunks); otherwise 4-wave chunks up to 64 (N = 10: 7.33 against
+    //    7.53 for 1-wave); 1-wave again up to 88 (M = 80, N = 9..11:
+    //    7.98-8.57 against 8.21-8.74 for 2-wave; M = 88, N = 8 and 12: 7.85
+    //    and 9.10 against 8.03 and 9.25); then up to 96, 2-wave chunks from 8
+    //    snapshots on (N = 12, M = 96: 9.46 against 10.02 for W), 1-wave at
+    //    N = 7 (7.64 against 7.92 for W), W at N = 6 (7.30 against 7.40);
+    //    M = 1, N = 12: 5.07 us; N = 6: 4.62 against 5.40 for the Gram form
+    //    in 2-wave chunks;
+    //  * 2 <= N <= 5 (the Gram form's one exchange): 1-wave chunks up to 40
+    //    tokens at N = 2, 56 at N = 3, 64 from N = 4 on (M = 24, N = 2: 5.00
+    //    against 5.13 for 2-wave chunks; M = 48, N = 4: 5.85 against 6.16
+    //    for 4-wave chunks; M = 64, N = 2 and 3: W 5.45 and 5.84 against
+    //    5.66 and 5.87);
     //  * N <= 1 at every M: one workgroup per token (at N = 1 the split wins
     //    with add2 and loses without it, M = 1: 4.21 against 4.64 us and 4.37
     //    against 4.30; the dispatch may not depend on add2, and the named
@@ -264,19 +264,17 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
                 return ATTNRES_OK;
         }
     } else if (n >= GRAM_MAX_SOURCES) {
-        if (M <= SPLIT_ONE_WAVE_TOKENS && plan_split(M, nvec, 1, pl))
+        const bool one_wave = M <= SPLIT_ONE_WAVE_TOKENS || (M <= SPLIT_MID_TOKENS && n <= SPLIT_MID_ONE_WAVE_SNAP) ||
+                              (M > SPLIT_MID_TOKENS && M <= SPLIT_LATE_ONE_WAVE_TOKENS) ||
+                              (n == 7 && M > SPLIT_MID_TOKENS && M <= SPLIT_WIDE_TOKENS);
+        if (one_wave && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
         if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
             return ATTNRES_OK;
-        if (M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 2, pl))
+        if (n >= 8 && M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
     } else if (n >= 2) {
-        const int gram_values = (n + 1) + (n + 1) * (n + 2) / 2;
-        if (gram_values <= 32 && M <= SPLIT_SMALL_TOKENS && plan_split(M, nvec, 1, pl))
-            return ATTNRES_OK;
-        if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 2, pl))
-            return ATTNRES_OK;
-        if (n >= 4 && M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 4, pl))
+        if (M <= gram_one_wave_tokens(n) && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
     }
     // Just past the CU count, kernel W would give some CUs two whole tokens

@@ -15,19 +15,26 @@ constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
 // automatic dispatch (see make_plan) at H >= 7168, one pass of sources:
-// N >= 8: 1-wave split chunks up to SPLIT_ONE_WAVE_TOKENS tokens, 4-wave up
-// to SPLIT_MID_TOKENS, 2-wave up to SPLIT_WIDE_TOKENS; 2 <= N <
-// GRAM_MAX_SOURCES: 1-wave chunks up to SPLIT_SMALL_TOKENS tokens while the
-// Gram form's values fit one polling round (N <= 5), 2-wave chunks up to
-// SPLIT_SMALL_TOKENS_WIDE, then 4-wave up to SPLIT_MID_TOKENS from N = 4 on
-constexpr int SPLIT_SMALL_TOKENS = 16;
+// N >= GRAM_MAX_SOURCES (two exchanges): 1-wave split chunks up to
+// SPLIT_ONE_WAVE_TOKENS tokens, and up to SPLIT_MID_TOKENS with at most
+// SPLIT_MID_ONE_WAVE_SNAP snapshots, else 4-wave chunks up to SPLIT_MID_TOKENS;
+// 1-wave chunks again up to SPLIT_LATE_ONE_WAVE_TOKENS, then (from
+// SPLIT_LATE_ONE_WAVE_TOKENS + 1) 2-wave chunks up to SPLIT_WIDE_TOKENS from 8
+// snapshots on and 1-wave chunks at N = 7; 2 <= N < GRAM_MAX_SOURCES (the
+// Gram form's one exchange): 1-wave chunks up to gram_one_wave_tokens(N).
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_ONE_WAVE_TOKENS = 48;
 constexpr int SPLIT_MID_TOKENS = 64;
+constexpr int SPLIT_MID_ONE_WAVE_SNAP = 8;
+constexpr int SPLIT_LATE_ONE_WAVE_TOKENS = 88;
 constexpr int SPLIT_WIDE_TOKENS = 96;
+constexpr int gram_one_wave_tokens(int n) { return n <= 2 ? 40 : n == 3 ? 56 : SPLIT_MID_TOKENS; }
 // The split kernel's Gram form (one exchange instead of two) serves up to
-// GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1).
-constexpr int GRAM_MAX_SOURCES = 8;
+// GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1): its 6 + 21 values
+// per chunk at N = 5 still fit one polling round with two lanes per value,
+// and from 7 sources on the second exchange costs less than the Gram form's
+// extra values and arithmetic.
+constexpr int GRAM_MAX_SOURCES = 6;
 // Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one
 // workgroup per token at every M and N <= 12; rows shorter than
 // LONG_ROW_VECTORS (H < 7168) are split only with N >= MID_SPLIT_MIN_SNAP and

@@ -164,41 +164,41 @@ def test_bf16_add_validation():
 
 def test_plan_is_pure_and_sane():
     # the measured automatic dispatch at H = 7168
-    assert ar.attnres_plan(1, 12, 7168) == (2, 14, 64)     # N >= 8: 1-wave chunks up to 48 tokens
+    assert ar.attnres_plan(1, 12, 7168) == (2, 14, 64)     # N >= 6: 1-wave chunks up to 48 tokens
     assert ar.attnres_plan(2, 8, 7168) == (2, 14, 64)
     assert ar.attnres_plan(8, 12, 7168) == (2, 14, 64)
     assert ar.attnres_plan(24, 12, 7168) == (2, 14, 64)
     assert ar.attnres_plan(32, 8, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(48, 8, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(49, 8, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
+    assert ar.attnres_plan(48, 12, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(49, 8, 7168) == (2, 14, 64)     # up to 64 with at most 8 snapshots
+    assert ar.attnres_plan(64, 6, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(49, 9, 7168) == (2, 4, 256)     # else 4-wave chunks up to 64
     assert ar.attnres_plan(64, 12, 7168) == (2, 4, 256)
-    assert ar.attnres_plan(65, 12, 7168) == (2, 7, 128)    # then 2-wave chunks up to 96
-    assert ar.attnres_plan(96, 8, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(65, 12, 7168) == (2, 14, 64)    # 1-wave again up to 88
+    assert ar.attnres_plan(88, 6, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(89, 8, 7168) == (2, 7, 128)     # then 2-wave up to 96 from 8 snapshots on
+    assert ar.attnres_plan(96, 12, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(96, 7, 7168) == (2, 14, 64)     # N = 7: 1-wave up to 96
+    assert ar.attnres_plan(89, 6, 7168)[0] == 1            # N = 6: a workgroup per token
     assert ar.attnres_plan(97, 8, 7168)[0] == 1
+    assert ar.attnres_plan(97, 7, 7168)[0] == 1
+    assert ar.attnres_plan(1, 6, 7168) == (2, 14, 64)      # two exchanges from 6 snapshots on
     assert ar.attnres_plan(2, 3, 7168) == (2, 14, 64)      # 2 <= N <= 5: 1-wave chunks (one exchange)
-    assert ar.attnres_plan(16, 4, 7168) == (2, 14, 64)     # up to 16 tokens
-    assert ar.attnres_plan(16, 5, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(16, 6, 7168) == (2, 7, 128)     # N = 6, 7: 2-wave chunks
-    assert ar.attnres_plan(17, 3, 7168) == (2, 7, 128)     # then 2-wave chunks up to 32 tokens
-    assert ar.attnres_plan(32, 2, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 3, 7168)[0] == 1            # N < 4: then a workgroup per token
-    assert ar.attnres_plan(32, 6, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 6, 7168) == (2, 4, 256)     # then 4-wave chunks up to 64
-    assert ar.attnres_plan(2, 7, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(32, 7, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 7, 7168) == (2, 4, 256)
-    assert ar.attnres_plan(64, 7, 7168) == (2, 4, 256)
-    assert ar.attnres_plan(65, 7, 7168)[0] == 1
-    assert ar.attnres_plan(32, 5, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(40, 2, 7168) == (2, 14, 64)     # up to 40 tokens at N = 2,
+    assert ar.attnres_plan(41, 2, 7168)[0] == 1
+    assert ar.attnres_plan(56, 3, 7168) == (2, 14, 64)     # 56 at N = 3,
+    assert ar.attnres_plan(57, 3, 7168)[0] == 1
+    assert ar.attnres_plan(64, 4, 7168) == (2, 14, 64)     # 64 from N = 4 on
+    assert ar.attnres_plan(64, 5, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(65, 5, 7168)[0] == 1
+    assert ar.attnres_plan(65, 4, 7168)[0] == 1
     assert ar.attnres_plan(16, 13, 7168) == (2, 7, 128)    # above 12 sources: 2-wave family
-    assert ar.attnres_plan(32, 4, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(33, 4, 7168) == (2, 4, 256)
     assert ar.attnres_plan(1, 2, 7168) == (2, 14, 64)
     assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
     assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(64, 2, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 2, 896) == (1, 1, 128)       # short rows stay on one workgroup per token
-    assert ar.attnres_plan(64, 8, 7168) == (2, 4, 256)     # 4-wave chunks
+    assert ar.attnres_plan(64, 9, 7168) == (2, 4, 256)     # 4-wave chunks
     assert ar.attnres_plan(97, 12, 7168)[0] == 1
     assert ar.attnres_plan(256, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(257, 12, 7168) == (3, 14, 448)  # just past the CU count: the hybrid, 1-wave

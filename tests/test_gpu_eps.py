@@ -106,10 +106,10 @@ def check(ar, orc, case, what):
 
 # (forced variant, param, N): kernel W (one pass; batches of 12 above 12
 # sources), the split kernel's two exchanges (1, 2 and 7 waves per chunk) and
-# its Gram form (N <= 7)
+# its Gram form (N <= 5)
 KERNELS = [((1, 0), 4, "W"), ((1, 0), 12, "W"), ((1, 0), 20, "W batched"), ((1, 4), 12, "W 4 vectors"),
            ((2, 1), 12, "S1w"), ((2, 2), 12, "S2w"), ((2, 7), 12, "S7w"), ((2, 2), 4, "S2w Gram"),
-           ((2, 1), 7, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"), ((2, 1), 8, "S1w N=8"),
+           ((2, 1), 5, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"), ((2, 1), 8, "S1w N=8"),
            ((3, 4), 12, "hybrid 4w"),
            ((0, 0), 1, "auto")]
 

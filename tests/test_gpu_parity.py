@@ -226,7 +226,7 @@ def _cancelling_case(N, noise=1e-3, M=3, H=7168, seed=5):
 @pytest.mark.parametrize("variant", [(0, 0), (2, 1), (2, 2), (2, 7)], ids=["auto", "S1w", "S2w", "S7w"],
                          indirect=True)
 @pytest.mark.parametrize("noise", [1e-3, 0.15, 0.3, 0.6])
-@pytest.mark.parametrize("N", [1, 3, 4, 7, 8, 9, 12])
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 6, 7, 8, 12])
 def test_cancelling_sources(ar, orc, variant, N, noise):
     """Sources that nearly cancel.  The split kernel takes sum x^2 = alpha' G
     alpha from its one exchange for few sources.  With noise 1e-3 that form
@@ -234,7 +234,7 @@ def test_cancelling_sources(ar, orc, variant, N, noise):
     and run the second exchange; with 0.15 the conditioning bound still sends
     it there; with 0.6 (and 0.3 at N = 1) the sources cancel by a factor of
     about 12 to 57, under the bound, so the form is accepted and its rounding
-    must stay far below the tolerance.  From 8 snapshots (two exchanges) the
+    must stay far below the tolerance.  From 6 snapshots (two exchanges) the
     second exchange sums the chunks' x^2 of the cancelled mixture.  out_norm
     within the parity bound of the oracle either way."""
     if not supported(ar, 3, N, 7168):
@@ -269,17 +269,18 @@ def test_shapes(ar, orc, variant, M, H, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8, 12])
-@pytest.mark.parametrize("M", [1, 2, 16, 17, 24, 32, 33, 48, 49, 64, 65, 96, 97])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12])
+@pytest.mark.parametrize("M", [1, 2, 16, 24, 32, 40, 41, 48, 49, 56, 57, 64, 65, 88, 89, 96, 97])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
-    (for N >= 8 1-wave chunks up to 48 tokens, then 4-wave up to 64, 2-wave up
-    to 96; for 2 <= N <= 7, the one-exchange form, 1-wave chunks up to 16
-    tokens for N <= 5, 2-wave chunks up to 32, then 4-wave up to 64 from N =
-    4; then a workgroup per token) and
-    source-count bounds (the split kernel's single-exchange form up to seven
-    snapshots, and the halved polling of up to 32 values; one group of up to
-    four sources in kernel W)."""
+    (for N >= 6, two exchanges: 1-wave chunks up to 48 tokens, up to 64 with
+    at most 8 snapshots, else 4-wave up to 64, 1-wave again up to 88, then
+    2-wave up to 96 from 8 snapshots on and 1-wave at N = 7; for 2 <= N <= 5,
+    the one-exchange form, 1-wave chunks up to 40 / 56 / 64 tokens at N = 2 /
+    3 / 4-5; then a workgroup per token) and source-count bounds (the split
+    kernel's single-exchange form up to five snapshots, 1-wave chunks at 49-64
+    tokens up to 8, and the halved polling of up to 32 values; one group of
+    up to four sources in kernel W)."""
     case = case_for(("bound", M, N), lambda: W.make_case(cfg=62, M=M, N=N, add2=(M % 2 == 0)))
     say("boundary", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)

@@ -68,7 +68,7 @@ def out_pair(M, H):
 # takes, calls kernel W serves (no scratch), the hybrid of W and split chunks
 # just past the CU count (its split part at the most tokens the automatic
 # dispatch gives it), and 2-wave chunks again
-CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (80, 8)]
+CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (92, 8)]
 
 
 def test_noalloc_matches_fwd(ar, orc):
