@@ -245,24 +245,22 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
     //    against 5.7 us for one token, 5.2 against 6.3 for 256);
-    //  * H = 3584 / 4096: with N >= 8 and M <= 64 the split still wins
-    //    (1-wave chunks up to 32 tokens: M = 1, N = 12: 5.7 against 7.0 us),
-    //    and with N = 12 up to 96 tokens in 1-wave chunks (H = 3584, M = 80:
-    //    7.06 against 7.54; H = 4096, M = 96: 7.50 against 7.73; N = 8 and
-    //    M = 128 stay with W: 6.20 against 6.47, 7.78 against 7.87).
+    //  * H = 3584 / 4096: 1-wave split chunks up to 32 tokens at N = 4, 48
+    //    at N = 5..7, 64 at N = 8..11 and 96 at N = 12 (H = 3584, M = 1, N =
+    //    6: 4.46 against W 5.26; N = 4: 4.30 against 4.64; M = 48, N = 5:
+    //    5.49 against 5.71; N = 6: 5.59 against 5.80; N = 8: 5.73 against
+    //    5.92 for 2-wave chunks; M = 96, N = 12: 6.92 against W 7.67);
+    //    otherwise W (M = 48, N = 4: 5.17 against 5.34; M = 64, N = 6: 5.71
+    //    against 5.77; M = 1, N = 2 and 3: 3.88 and 4.01 against 4.04 and
+    //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (many) {
         if (M <= SPLIT_MID_TOKENS && split_ok && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
     } else if (!long_rows) {
-        if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP) {
-            if (M <= SPLIT_SMALL_TOKENS_WIDE && plan_split(M, nvec, 1, pl))
-                return ATTNRES_OK;
-            if (M <= SPLIT_MID_TOKENS && plan_split(M, nvec, 2, pl))
-                return ATTNRES_OK;
-            if (n >= MAX_SNAP && M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 1, pl))
-                return ATTNRES_OK;
-        }
+        if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP && M <= mid_one_wave_tokens(n) &&
+            plan_split(M, nvec, 1, pl))
+            return ATTNRES_OK;
     } else if (n >= GRAM_MAX_SOURCES) {
         const bool one_wave = M <= SPLIT_ONE_WAVE_TOKENS || (M <= SPLIT_MID_TOKENS && n <= SPLIT_MID_ONE_WAVE_SNAP) ||
                               (M > SPLIT_MID_TOKENS && M <= SPLIT_LATE_ONE_WAVE_TOKENS) ||

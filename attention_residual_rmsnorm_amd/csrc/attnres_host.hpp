@@ -37,13 +37,17 @@ constexpr int gram_one_wave_tokens(int n) { return n <= 2 ? 40 : n == 3 ? 56 : S
 constexpr int GRAM_MAX_SOURCES = 6;
 // Rows of at most SHORT_ROW_VECTORS 16-byte vectors (H <= 2048) stay one
 // workgroup per token at every M and N <= 12; rows shorter than
-// LONG_ROW_VECTORS (H < 7168) are split only with N >= MID_SPLIT_MIN_SNAP and
-// M <= SPLIT_MID_TOKENS (1 wave per workgroup up to SPLIT_SMALL_TOKENS_WIDE
-// tokens), or with N = MAX_SNAP up to SPLIT_WIDE_TOKENS (1 wave); rows of
+// LONG_ROW_VECTORS (H < 7168) are split in 1-wave chunks from N =
+// MID_SPLIT_MIN_SNAP on, up to mid_one_wave_tokens(N) tokens; rows of
 // LONG_ROW_VECTORS and more follow the rules above.
 constexpr int SHORT_ROW_VECTORS = 256;
 constexpr int LONG_ROW_VECTORS = 896;
-constexpr int MID_SPLIT_MIN_SNAP = 8;
+constexpr int MID_SPLIT_MIN_SNAP = 4;
+constexpr int mid_one_wave_tokens(int n)
+{
+    return n >= MAX_SNAP ? SPLIT_WIDE_TOKENS : n >= 8 ? SPLIT_MID_TOKENS : n >= 5 ? SPLIT_ONE_WAVE_TOKENS
+                                                                            : SPLIT_SMALL_TOKENS_WIDE;
+}
 // Kernel W's single-group form (one vector per thread, at most
 // SHORT_WG_THREADS threads) while M * threads <= SHORT_WG_MAX_THREADS_TOTAL:
 // beyond that the form with groups of two keeps more waves per CU and streams

@@ -130,7 +130,8 @@ int main()
         EXPECT(make_plan(512, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.threads == 256 && pl.single_group);
         EXPECT(make_plan(513, 8, 2048, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
         EXPECT(make_plan(1, 12, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 2);
-        EXPECT(make_plan(1, 4, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(1, 3, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 1 && !pl.single_group);
+        EXPECT(make_plan(1, 4, 3584, 0, 0, pl) == ATTNRES_OK && pl.variant == 2 && pl.threads == 64);
         EXPECT(make_plan(1, 12, 7168, 1, 1, pl) == ATTNRES_OK && pl.threads == 896 && !pl.single_group);
         EXPECT(make_plan(1, 13, 896, 1, 0, pl) == ATTNRES_OK && pl.vpt == 2 && !pl.single_group);
     }

@@ -228,15 +228,18 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(1, 12, 896) == (1, 1, 128)      # H <= 2048: workgroup per token
     assert ar.attnres_plan(256, 12, 896) == (1, 1, 128)
     assert ar.attnres_plan(8, 12, 2048) == (1, 1, 256)
-    assert ar.attnres_plan(1, 12, 3584) == (2, 7, 64)      # H < 7168, N >= 8: 1-wave chunks up to 32 tokens
-    assert ar.attnres_plan(32, 8, 4096) == (2, 8, 64)
-    assert ar.attnres_plan(64, 12, 3584) == (2, 4, 128)    # then 2-wave chunks up to 64
-    assert ar.attnres_plan(65, 12, 3584) == (2, 7, 64)     # N = 12: 1-wave chunks up to 96
+    assert ar.attnres_plan(1, 12, 3584) == (2, 7, 64)      # 2048 < H < 7168: 1-wave chunks,
+    assert ar.attnres_plan(32, 4, 3584) == (2, 7, 64)      # up to 32 tokens at N = 4
+    assert ar.attnres_plan(33, 4, 4096)[0] == 1
+    assert ar.attnres_plan(48, 5, 4096) == (2, 8, 64)      # up to 48 at N = 5..7
+    assert ar.attnres_plan(48, 6, 4096) == (2, 8, 64)
+    assert ar.attnres_plan(49, 7, 3584)[0] == 1
+    assert ar.attnres_plan(64, 8, 3584) == (2, 7, 64)      # up to 64 at N = 8..11
+    assert ar.attnres_plan(65, 11, 3584)[0] == 1
+    assert ar.attnres_plan(65, 12, 3584) == (2, 7, 64)     # up to 96 at N = 12
     assert ar.attnres_plan(96, 12, 4096) == (2, 8, 64)
     assert ar.attnres_plan(97, 12, 3584)[0] == 1
-    assert ar.attnres_plan(65, 11, 3584)[0] == 1
-    assert ar.attnres_plan(65, 8, 3584)[0] == 1             # N < 12: a workgroup per token beyond 64
-    assert ar.attnres_plan(1, 7, 3584)[0] == 1             # fewer sources: workgroup per token
+    assert ar.attnres_plan(1, 3, 3584)[0] == 1             # fewer sources: workgroup per token
     with pytest.raises(ar.AttnResError):
         ar.attnres_plan(1, 65, 7168)
     with pytest.raises(ar.AttnResError):

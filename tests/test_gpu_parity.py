@@ -304,12 +304,14 @@ def test_hybrid_boundaries(ar, orc, M, N):
 
 # (M, H, N): kernel W's single-group form (rows of at most 256 vectors, up to
 # 131072 threads per call) on both sides of its bound, ragged short rows, and
-# the split bounds for rows of 257..895 vectors; H = 896 is a tensor-parallel
+# the split bounds for rows of 257..895 vectors (1-wave chunks up to 32 / 48 /
+# 64 / 96 tokens at N = 4 / 5-7 / 8-11 / 12); H = 896 is a tensor-parallel
 # rank's share (1/8) of 7168
 SHORT_ROWS = [(1, 896, n) for n in (0, 1, 3, 4, 5, 8, 12)] + [
     (7, 904, 2), (7, 904, 5), (7, 904, 12), (1024, 896, 12), (1025, 896, 12), (512, 2048, 8), (513, 2048, 8),
     (33, 2048, 12), (1, 3584, 12), (32, 3584, 8), (33, 3584, 12), (65, 3584, 12), (96, 4096, 12), (97, 3584, 12),
-    (80, 3584, 8), (3, 4096, 7)]
+    (80, 3584, 8), (3, 4096, 7), (1, 3584, 3), (32, 3584, 4), (33, 4096, 4), (48, 4096, 5), (49, 3584, 7),
+    (64, 3584, 8), (65, 4096, 11)]
 
 
 @pytest.mark.parametrize("M,H,N", SHORT_ROWS)
