@@ -239,8 +239,14 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    against 4.30; the dispatch may not depend on add2, and the named
     //    single-token call has none);
     //  * otherwise one workgroup per token (or the hybrid, below).
-    // More than one pass of sources: 2-wave chunks (the family that holds up
-    // to 31 snapshots) up to 64 tokens, else W's batches.
+    // More than one pass of sources (up to 31 snapshots, which the 1-2-wave
+    // family holds): 1-wave chunks up to 16 tokens and from 33 to 64, 2-wave
+    // chunks from 17 to 32 and from 65 to 96, else W's batches (N = 13, 20,
+    // 31: M = 1 5.15 against 5.86 us for 2-wave, N = 13; M = 24, N = 31:
+    // 2-wave 8.65 against 9.10; M = 64: 1-wave 8.13 / 9.98 / 12.00 against
+    // 8.64 / 10.69 / 13.10; M = 96: 2-wave 9.60 / 12.03 / 15.08 against W
+    // 10.92 / 14.45 / 19.75; M = 192: W 12.35 / 16.31 / 22.73 against
+    // 14.64 / 18.94 / 27.30).
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
@@ -255,7 +261,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (many) {
-        if (M <= SPLIT_MID_TOKENS && split_ok && plan_split(M, nvec, 2, pl))
+        const int waves = M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_MID_TOKENS) ? 1 : 2;
+        if (M <= SPLIT_WIDE_TOKENS && split_ok && plan_split(M, nvec, waves, pl))
             return ATTNRES_OK;
     } else if (!long_rows) {
         if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP && M <= mid_one_wave_tokens(n) &&

@@ -22,6 +22,10 @@ constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hi
 // SPLIT_LATE_ONE_WAVE_TOKENS + 1) 2-wave chunks up to SPLIT_WIDE_TOKENS from 8
 // snapshots on and 1-wave chunks at N = 7; 2 <= N < GRAM_MAX_SOURCES (the
 // Gram form's one exchange): 1-wave chunks up to gram_one_wave_tokens(N).
+// More than one pass of sources (up to MAX_SPLIT_SNAP snapshots): 1-wave
+// chunks up to SPLIT_SMALL_TOKENS tokens and from SPLIT_SMALL_TOKENS_WIDE + 1
+// to SPLIT_MID_TOKENS, 2-wave chunks otherwise up to SPLIT_WIDE_TOKENS.
+constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_ONE_WAVE_TOKENS = 48;
 constexpr int SPLIT_MID_TOKENS = 64;

@@ -192,7 +192,7 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(64, 5, 7168) == (2, 14, 64)
     assert ar.attnres_plan(65, 5, 7168)[0] == 1
     assert ar.attnres_plan(65, 4, 7168)[0] == 1
-    assert ar.attnres_plan(16, 13, 7168) == (2, 7, 128)    # above 12 sources: 2-wave family
+    assert ar.attnres_plan(16, 13, 7168) == (2, 14, 64)    # above 12 sources: 1-wave chunks up to 16,
     assert ar.attnres_plan(1, 2, 7168) == (2, 14, 64)
     assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
     assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)
@@ -215,13 +215,17 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(4096, 13, 7168) == (1, 1, 448)  # more than 12 sources: batches, two vectors
     v, c, t = ar.attnres_plan(256, 12, 7168)
     assert v == 1 and c == 1 and t % 64 == 0
-    # more sources than one pass: the 2-wave split up to 31 snapshots at small
-    # M, else workgroup per token in batches
-    assert ar.attnres_plan(1, 13, 7168) == (2, 7, 128)
+    # more sources than one pass: the split up to 31 snapshots and 96 tokens,
+    # else workgroup per token in batches
+    assert ar.attnres_plan(1, 13, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(17, 20, 7168) == (2, 7, 128)    # 2-wave chunks from 17 to 32,
     assert ar.attnres_plan(32, 31, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(1, 32, 7168) == (1, 1, 448)
-    assert ar.attnres_plan(64, 13, 7168) == (2, 7, 128)
-    assert ar.attnres_plan(65, 13, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(33, 31, 7168) == (2, 14, 64)    # 1-wave from 33 to 64,
+    assert ar.attnres_plan(64, 13, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(65, 13, 7168) == (2, 7, 128)    # 2-wave from 65 to 96
+    assert ar.attnres_plan(96, 31, 7168) == (2, 7, 128)
+    assert ar.attnres_plan(97, 13, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(1, 32, 7168) == (1, 1, 448)     # more than 31 snapshots: W's batches
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
     assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
     # shorter rows (a tensor-parallel rank's share of the hidden size)
