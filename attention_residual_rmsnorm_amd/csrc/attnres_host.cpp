@@ -234,10 +234,13 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    against 5.13 for 2-wave chunks; M = 48, N = 4: 5.85 against 6.16
     //    for 4-wave chunks; M = 64, N = 2 and 3: W 5.45 and 5.84 against
     //    5.66 and 5.87);
-    //  * N <= 1 at every M: one workgroup per token (at N = 1 the split wins
-    //    with add2 and loses without it, M = 1: 4.21 against 4.64 us and 4.37
-    //    against 4.30; the dispatch may not depend on add2, and the named
-    //    single-token call has none);
+    //  * N = 1: 1-wave chunks up to 8 tokens (M = 1: 4.01 against 4.35 us
+    //    for one workgroup per token without add2, 4.11 against 4.62 with it;
+    //    M = 8: 4.45 against 4.42 and 4.55 against 4.68; M = 16: 4.53 against
+    //    4.46 and 4.63 against 4.73), then one workgroup per token;
+    //  * N = 0 at every M: one workgroup per token (M = 1: 3.83 against 3.96
+    //    without add2, 4.24 against 4.06 with it; the dispatch may not depend
+    //    on add2);
     //  * otherwise one workgroup per token (or the hybrid, below).
     // More than one pass of sources (up to 31 snapshots, which the 1-2-wave
     // family holds): 1-wave chunks up to 16 tokens and from 33 to 64, 2-wave
@@ -278,7 +281,7 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
             return ATTNRES_OK;
         if (n >= 8 && M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, 2, pl))
             return ATTNRES_OK;
-    } else if (n >= 2) {
+    } else if (n >= 1) {
         if (M <= gram_one_wave_tokens(n) && plan_split(M, nvec, 1, pl))
             return ATTNRES_OK;
     }

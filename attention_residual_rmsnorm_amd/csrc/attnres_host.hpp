@@ -21,7 +21,8 @@ constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hi
 // 1-wave chunks again up to SPLIT_LATE_ONE_WAVE_TOKENS, then (from
 // SPLIT_LATE_ONE_WAVE_TOKENS + 1) 2-wave chunks up to SPLIT_WIDE_TOKENS from 8
 // snapshots on and 1-wave chunks at N = 7; 2 <= N < GRAM_MAX_SOURCES (the
-// Gram form's one exchange): 1-wave chunks up to gram_one_wave_tokens(N).
+// Gram form's one exchange; N = 1 too): 1-wave chunks up to
+// gram_one_wave_tokens(N).
 // More than one pass of sources (up to MAX_SPLIT_SNAP snapshots): 1-wave
 // chunks up to SPLIT_SMALL_TOKENS tokens and from SPLIT_SMALL_TOKENS_WIDE + 1
 // to SPLIT_MID_TOKENS, 2-wave chunks otherwise up to SPLIT_WIDE_TOKENS.
@@ -32,7 +33,7 @@ constexpr int SPLIT_MID_TOKENS = 64;
 constexpr int SPLIT_MID_ONE_WAVE_SNAP = 8;
 constexpr int SPLIT_LATE_ONE_WAVE_TOKENS = 88;
 constexpr int SPLIT_WIDE_TOKENS = 96;
-constexpr int gram_one_wave_tokens(int n) { return n <= 2 ? 40 : n == 3 ? 56 : SPLIT_MID_TOKENS; }
+constexpr int gram_one_wave_tokens(int n) { return n <= 1 ? 8 : n == 2 ? 40 : n == 3 ? 56 : SPLIT_MID_TOKENS; }
 // The split kernel's Gram form (one exchange instead of two) serves up to
 // GRAM_MAX_SOURCES sources (N <= GRAM_MAX_SOURCES - 1): its 6 + 21 values
 // per chunk at N = 5 still fit one polling round with two lanes per value,

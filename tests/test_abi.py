@@ -194,8 +194,10 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(65, 4, 7168)[0] == 1
     assert ar.attnres_plan(16, 13, 7168) == (2, 14, 64)    # above 12 sources: 1-wave chunks up to 16,
     assert ar.attnres_plan(1, 2, 7168) == (2, 14, 64)
-    assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N <= 1: workgroup per token
-    assert ar.attnres_plan(8, 1, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N = 0: workgroup per token
+    assert ar.attnres_plan(1, 1, 7168) == (2, 14, 64)      # N = 1: 1-wave chunks up to 8 tokens
+    assert ar.attnres_plan(8, 1, 7168) == (2, 14, 64)
+    assert ar.attnres_plan(9, 1, 7168) == (1, 1, 448)
     assert ar.attnres_plan(64, 2, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 2, 896) == (1, 1, 128)       # short rows stay on one workgroup per token
     assert ar.attnres_plan(64, 9, 7168) == (2, 4, 256)     # 4-wave chunks

@@ -270,14 +270,15 @@ def test_shapes(ar, orc, variant, M, H, N):
 
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12])
-@pytest.mark.parametrize("M", [1, 2, 16, 24, 32, 40, 41, 48, 49, 56, 57, 64, 65, 88, 89, 96, 97])
+@pytest.mark.parametrize("M", [1, 2, 8, 9, 16, 24, 32, 40, 41, 48, 49, 56, 57, 64, 65, 88, 89, 96, 97])
 def test_dispatch_boundaries(ar, orc, M, N):
     """The automatic dispatch on both sides of each of its token-count bounds
     (for N >= 6, two exchanges: 1-wave chunks up to 48 tokens, up to 64 with
     at most 8 snapshots, else 4-wave up to 64, 1-wave again up to 88, then
     2-wave up to 96 from 8 snapshots on and 1-wave at N = 7; for 2 <= N <= 5,
     the one-exchange form, 1-wave chunks up to 40 / 56 / 64 tokens at N = 2 /
-    3 / 4-5; then a workgroup per token) and source-count bounds (the split
+    3 / 4-5, up to 8 at N = 1; then a workgroup per token) and source-count
+    bounds (the split
     kernel's single-exchange form up to five snapshots, 1-wave chunks at 49-64
     tokens up to 8, and the halved polling of up to 32 values; one group of
     up to four sources in kernel W)."""
