@@ -226,7 +226,7 @@ def _cancelling_case(N, noise=1e-3, M=3, H=7168, seed=5):
 @pytest.mark.parametrize("variant", [(0, 0), (2, 1), (2, 2), (2, 7)], ids=["auto", "S1w", "S2w", "S7w"],
                          indirect=True)
 @pytest.mark.parametrize("noise", [1e-3, 0.15, 0.3, 0.6])
-@pytest.mark.parametrize("N", [1, 3, 4, 5, 6, 7, 8, 12])
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12])
 def test_cancelling_sources(ar, orc, variant, N, noise):
     """Sources that nearly cancel.  The split kernel takes sum x^2 = alpha' G
     alpha from its one exchange for few sources.  With noise 1e-3 that form
@@ -293,9 +293,9 @@ def test_dispatch_boundaries(ar, orc, M, N):
 @pytest.mark.parametrize("M", [256, 257, 264, 288, 289, 319, 320, 321, 352, 383, 384, 385, 511])
 def test_hybrid_boundaries(ar, orc, M, N):
     """Past the CU count: the automatic dispatch's hybrid launch (kernel W on
-    the first 256 tokens, 4-wave split chunks on the rest) at its bounds, and
-    kernel W beyond it (two tokens on some CUs), every output element against
-    the oracle."""
+    the first 256 tokens, 1-, 2- or 4-wave split chunks on the rest) at its
+    bounds, and kernel W beyond it (two tokens on some CUs), every output
+    element against the oracle."""
     case = case_for(("hybrid", M, N), lambda: W.make_case(cfg=67, M=M, N=N, add2=(N % 2 == 0)))
     say("hybrid", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)
