@@ -249,11 +249,14 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // 2-wave 8.65 against 9.10; M = 64: 1-wave 8.13 / 9.98 / 12.00 against
     // 8.64 / 10.69 / 13.10; M = 96: 2-wave 9.60 / 12.03 / 15.08 against W
     // 10.92 / 14.45 / 19.75; M = 192: W 12.35 / 16.31 / 22.73 against
-    // 14.64 / 18.94 / 27.30).
+    // 14.64 / 18.94 / 27.30).  Shorter rows (2 or 7 chunks per token at H =
+    // 896 / 3584): 1-wave chunks at every M up to 96 (H = 3584, M = 80, N =
+    // 20: 8.13 against 9.72 us for 2-wave and 10.79 for W; H = 896, M = 32,
+    // N = 31: 6.72 against 7.24 and 12.25).
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
-    //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 4.1
-    //    against 5.7 us for one token, 5.2 against 6.3 for 256);
+    //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 3.88
+    //    against 4.90 us for one token, 4.66 against 6.00 for 256);
     //  * H = 3584 / 4096: 1-wave split chunks up to 32 tokens at N = 4, 48
     //    at N = 5..7, 64 at N = 8..11 and 96 at N = 12 (H = 3584, M = 1, N =
     //    6: 4.46 against W 5.26; N = 4: 4.30 against 4.64; M = 48, N = 5:
@@ -264,7 +267,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (many) {
-        const int waves = M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_MID_TOKENS) ? 1 : 2;
+        const int waves =
+            !long_rows || M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_MID_TOKENS) ? 1 : 2;
         if (M <= SPLIT_WIDE_TOKENS && split_ok && plan_split(M, nvec, waves, pl))
             return ATTNRES_OK;
     } else if (!long_rows) {

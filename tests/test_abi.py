@@ -228,6 +228,9 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(96, 31, 7168) == (2, 7, 128)
     assert ar.attnres_plan(97, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 32, 7168) == (1, 1, 448)     # more than 31 snapshots: W's batches
+    assert ar.attnres_plan(24, 20, 3584) == (2, 7, 64)     # shorter rows: 1-wave chunks up to 96
+    assert ar.attnres_plan(96, 31, 896) == (2, 2, 64)
+    assert ar.attnres_plan(97, 13, 896)[0] == 1
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
     assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
     # shorter rows (a tensor-parallel rank's share of the hidden size)
