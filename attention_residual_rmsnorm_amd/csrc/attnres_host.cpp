@@ -242,6 +242,15 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    without add2, 4.24 against 4.06 with it; the dispatch may not depend
     //    on add2);
     //  * otherwise one workgroup per token (or the hybrid, below).
+    // Rows longer than 8192 (1,536 and 2,048 vectors measured), N <= 12: kernel
+    // W's token is one CU's stream of a long row, so the split wins at every
+    // N up to 96 tokens, in chunks that keep 6-16 per token: 2-wave up to 16
+    // tokens and from 33 to 48, 4-wave from 17 to 32 and from 49 to 96 (H =
+    // 16384: M = 1, N = 0: 4.62 against 6.26 us for W; M = 16, N = 1: 5.13
+    // against 7.39; M = 32, N = 12: 4-wave 8.22 against 8.68 for 1-wave and
+    // 17.40 for W; M = 48, N = 12: 2-wave 10.10 against 10.47 for 4-wave; M =
+    // 96, N = 4: 4-wave 9.79 against 11.51 for W; H = 12288, M = 64, N = 8:
+    // 2-wave 8.61 against 4-wave 9.02 and W 12.25).
     // More than one pass of sources (up to 31 snapshots, which the 1-2-wave
     // family holds): 1-wave chunks up to 16 tokens and from 33 to 64, 2-wave
     // chunks from 17 to 32 and from 65 to 96, else W's batches (N = 13, 20,
@@ -274,6 +283,10 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     } else if (!long_rows) {
         if (nvec > SHORT_ROW_VECTORS && n >= MID_SPLIT_MIN_SNAP && M <= mid_one_wave_tokens(n) &&
             plan_split(M, nvec, 1, pl))
+            return ATTNRES_OK;
+    } else if (nvec > VERY_LONG_ROW_VECTORS) {
+        const int waves = M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_ONE_WAVE_TOKENS) ? 2 : 4;
+        if (M <= SPLIT_WIDE_TOKENS && plan_split(M, nvec, waves, pl))
             return ATTNRES_OK;
     } else if (n >= GRAM_MAX_SOURCES) {
         const bool one_wave = M <= SPLIT_ONE_WAVE_TOKENS || (M <= SPLIT_MID_TOKENS && n <= SPLIT_MID_ONE_WAVE_SNAP) ||

@@ -48,6 +48,12 @@ constexpr int GRAM_MAX_SOURCES = 6;
 // LONG_ROW_VECTORS and more follow the rules above.
 constexpr int SHORT_ROW_VECTORS = 256;
 constexpr int LONG_ROW_VECTORS = 896;
+// Rows of more than VERY_LONG_ROW_VECTORS vectors (H > 8192), N <= 12: the
+// split in 2-wave chunks up to SPLIT_SMALL_TOKENS tokens and from
+// SPLIT_SMALL_TOKENS_WIDE + 1 to SPLIT_ONE_WAVE_TOKENS, 4-wave chunks from
+// SPLIT_SMALL_TOKENS + 1 to SPLIT_SMALL_TOKENS_WIDE and from
+// SPLIT_ONE_WAVE_TOKENS + 1 to SPLIT_WIDE_TOKENS, at every N.
+constexpr int VERY_LONG_ROW_VECTORS = 1024;
 constexpr int MID_SPLIT_MIN_SNAP = 4;
 constexpr int mid_one_wave_tokens(int n)
 {

@@ -233,6 +233,15 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(97, 13, 896)[0] == 1
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
     assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
+    # rows longer than 8192, one pass: the split at every N up to 96 tokens
+    assert ar.attnres_plan(1, 0, 16384) == (2, 16, 128)    # 2-wave chunks up to 16 tokens,
+    assert ar.attnres_plan(16, 12, 12288) == (2, 12, 128)
+    assert ar.attnres_plan(17, 4, 16384) == (2, 8, 256)    # 4-wave from 17 to 32,
+    assert ar.attnres_plan(33, 8, 16384) == (2, 16, 128)   # 2-wave from 33 to 48,
+    assert ar.attnres_plan(49, 1, 12288) == (2, 6, 256)    # 4-wave from 49 to 96
+    assert ar.attnres_plan(96, 12, 16384) == (2, 8, 256)
+    assert ar.attnres_plan(97, 12, 16384)[0] == 1
+    assert ar.attnres_plan(1, 12, 8192) == (2, 16, 64)     # 8192 and shorter: the rules above
     # shorter rows (a tensor-parallel rank's share of the hidden size)
     assert ar.attnres_plan(1, 12, 896) == (1, 1, 128)      # H <= 2048: workgroup per token
     assert ar.attnres_plan(256, 12, 896) == (1, 1, 128)

@@ -315,6 +315,20 @@ SHORT_ROWS = [(1, 896, n) for n in (0, 1, 3, 4, 5, 8, 12)] + [
     (64, 3584, 8), (65, 4096, 11)]
 
 
+@pytest.mark.parametrize("H", [16384, 12288])
+@pytest.mark.parametrize("N", [0, 4, 12])
+@pytest.mark.parametrize("M", [1, 16, 17, 32, 33, 48, 49, 96, 97])
+def test_very_long_rows_dispatch(ar, orc, M, H, N):
+    """Rows longer than 8192 under the automatic dispatch, on both sides of
+    each token bound (2-wave split chunks up to 16 tokens and from 33 to 48,
+    4-wave from 17 to 32 and 49 to 96, then kernel W)."""
+    case = case_for(("vlong", M, H, N), lambda: W.make_case(cfg=69, M=M, H=H, N=N, add2=(M % 2 == 1)))
+    say("very long rows", M, H, N, ar.attnres_plan(M, N, H))
+    gp, gn = P.run_gpu(case)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+
+
 @pytest.mark.parametrize("M,H,N", SHORT_ROWS)
 def test_short_rows(ar, orc, M, H, N):
     """Rows shorter than 7168 under the automatic dispatch."""
