@@ -261,7 +261,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // 14.64 / 18.94 / 27.30).  Shorter rows (2 or 7 chunks per token at H =
     // 896 / 3584): 1-wave chunks at every M up to 96 (H = 3584, M = 80, N =
     // 20: 8.13 against 9.72 us for 2-wave and 10.79 for W; H = 896, M = 32,
-    // N = 31: 6.72 against 7.24 and 12.25).
+    // N = 31: 6.72 against 7.24 and 12.25).  Rows longer than 8192: 2-wave
+    // chunks except from 17 to 32 tokens, where 1-wave (H = 16384, M = 48,
+    // N = 31: 16.76 against 18.34 us for 1-wave; M = 16, N = 20: 8.74
+    // against 9.66; H = 12288, M = 32, N = 31: 1-wave 11.65 against 13.00;
+    // one token within 0.4 us either way).
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 3.88
@@ -276,8 +280,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (many) {
-        const int waves =
-            !long_rows || M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_MID_TOKENS) ? 1 : 2;
+        const bool mid_m = M > SPLIT_SMALL_TOKENS && M <= SPLIT_SMALL_TOKENS_WIDE; // 17..32
+        const int waves = !long_rows                      ? 1
+                          : nvec > VERY_LONG_ROW_VECTORS ? (mid_m ? 1 : 2)
+                          : (M <= SPLIT_SMALL_TOKENS || (M > SPLIT_SMALL_TOKENS_WIDE && M <= SPLIT_MID_TOKENS)) ? 1
+                                                                                                              : 2;
         if (M <= SPLIT_WIDE_TOKENS && split_ok && plan_split(M, nvec, waves, pl))
             return ATTNRES_OK;
     } else if (!long_rows) {

@@ -26,7 +26,9 @@ constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hi
 // More than one pass of sources (up to MAX_SPLIT_SNAP snapshots): 1-wave
 // chunks up to SPLIT_SMALL_TOKENS tokens and from SPLIT_SMALL_TOKENS_WIDE + 1
 // to SPLIT_MID_TOKENS, 2-wave chunks otherwise up to SPLIT_WIDE_TOKENS (rows
-// shorter than LONG_ROW_VECTORS: 1-wave chunks up to SPLIT_WIDE_TOKENS).
+// shorter than LONG_ROW_VECTORS: 1-wave chunks up to SPLIT_WIDE_TOKENS; rows
+// of more than VERY_LONG_ROW_VECTORS: 1-wave chunks from SPLIT_SMALL_TOKENS +
+// 1 to SPLIT_SMALL_TOKENS_WIDE, else 2-wave).
 constexpr int SPLIT_SMALL_TOKENS = 16;
 constexpr int SPLIT_SMALL_TOKENS_WIDE = 32;
 constexpr int SPLIT_ONE_WAVE_TOKENS = 48;

@@ -193,6 +193,10 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(65, 5, 7168)[0] == 1
     assert ar.attnres_plan(65, 4, 7168)[0] == 1
     assert ar.attnres_plan(16, 13, 7168) == (2, 14, 64)    # above 12 sources: 1-wave chunks up to 16,
+    assert ar.attnres_plan(16, 20, 16384) == (2, 16, 128)  # rows longer than 8192: 2-wave chunks
+    assert ar.attnres_plan(17, 31, 16384) == (2, 32, 64)   # except 1-wave from 17 to 32 tokens
+    assert ar.attnres_plan(33, 13, 12288) == (2, 12, 128)
+    assert ar.attnres_plan(1, 31, 12288) == (2, 12, 128)
     assert ar.attnres_plan(1, 2, 7168) == (2, 14, 64)
     assert ar.attnres_plan(1, 0, 7168) == (1, 1, 448)      # N = 0: workgroup per token
     assert ar.attnres_plan(1, 1, 7168) == (2, 14, 64)      # N = 1: 1-wave chunks up to 8 tokens

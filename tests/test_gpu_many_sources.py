@@ -65,14 +65,15 @@ def test_many_sources(ar, orc, variant, M, H, N):
     P.assert_mix_parity(gm, rm, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("H", [7168, 3584, 896])
+@pytest.mark.parametrize("H", [7168, 3584, 896, 16384])
 @pytest.mark.parametrize("N", [13, 31])
 @pytest.mark.parametrize("M", [16, 17, 32, 33, 64, 65, 96, 97])
 def test_many_sources_dispatch_bounds(ar, orc, M, N, H):
     """The automatic dispatch above 12 snapshots on both sides of each token
     bound (at H = 7168 1-wave split chunks up to 16 tokens and from 33 to 64,
-    2-wave from 17 to 32 and 65 to 96; shorter rows 1-wave up to 96; then
-    kernel W's batches)."""
+    2-wave from 17 to 32 and 65 to 96; shorter rows 1-wave up to 96; rows
+    longer than 8192 1-wave from 17 to 32, else 2-wave; then kernel W's
+    batches)."""
     case = W.make_case(cfg=86, M=M, H=H, N=N, add2=(M % 2 == 1))
     say("many sources, auto", M, H, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)
