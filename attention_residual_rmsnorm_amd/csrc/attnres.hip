@@ -1196,6 +1196,233 @@ __global__ __launch_bounds__(MAXB, WPE) void fwd_split(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Kernel S's two-wave form, for 32..MAX_SPLIT_LONG_SNAP snapshots (S = N + 1
+// sources, more than one wave's registers hold): chunks of 64 vectors, at
+// most LONG_PAGE per token, the same token placement, epochs, tags and
+// bounded waits as kernel S above, and two waves per chunk that share the
+// vectors and split the sources.  Source s is snapshot s for s < N and the
+// folded prefix for s = N; wave w holds sources 32w .. 32w + 31 in registers
+// (wave 1 also computes A1 and holds the folded prefix apart), so every row
+// of the chunk is loaded at once and read once.
+//  * A2: each wave's 64 values (sum k_s^2, q.k_s of its sources: values 2s
+//    and 2s + 1) are summed over the wave by the butterfly and published in
+//    page w: the chunk's own records for wave 0, those of chunk index
+//    c + LONG_PAGE for wave 1 (never a chunk of this token, as C <= LONG_PAGE).
+//  * A3: each wave gathers its page over the C chunks in a fixed order; the
+//    two waves' maxima and sums of exponentials meet in LDS (one barrier).
+//  * A4: each wave mixes its sources; wave 1 adds its mixture to wave 0's
+//    through LDS (second barrier), and wave 0 runs A5 as kernel S's second
+//    exchange does and stores the outputs.
+constexpr int LONG_WAVE_SOURCES = 32;
+constexpr int LONG_PAGE = SPLIT_LONG_MAX_CHUNKS;
+constexpr int LONG_TABLE = 2 * LONG_WAVE_SOURCES; // pointer table entries (snapshots 0..63)
+static_assert(2 * (MAX_SPLIT_LONG_SNAP + 1) <= 2 * REC_STRIDE && 2 * LONG_PAGE <= MAX_CHUNKS,
+              "two record pages per chunk");
+static_assert(MAX_SPLIT_LONG_SNAP + 1 <= LONG_TABLE && MAX_SPLIT_LONG_SNAP >= LONG_WAVE_SOURCES,
+              "wave 0: snapshots only; wave 1: the rest and the folded prefix");
+
+struct ParamsSplitLong {
+    Params p;
+    const uint4* snaps[LONG_TABLE]; // snapshot s < n_snap; entries past it repeat the last snapshot
+    int n_snap;
+};
+
+template <bool ADD2>
+__global__ __launch_bounds__(128, 1) void fwd_split_long(ParamsSplitLong pl)
+{
+    const Params& p = pl.p;
+    __shared__ float zs[2][2];                  // per wave: largest logit, sum of exponentials below it
+    __shared__ __align__(16) float xs[8][64];   // wave 1's mixture, element e of lane l at [e][l]
+
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int C = p.chunks;
+    const int ib = b >> 3;
+    const int chunk = ib - (ib / C) * C;
+    const int64_t rel = (int64_t)(ib / C) * 8 + ((b + p.xcd_skew * chunk) & 7);
+    const int64_t t = p.split_base + rel;
+    const int64_t slot = p.slot_base + rel;
+    if (t >= p.M)
+        return;
+
+    unsigned* state = p.state + (size_t)slot * STATE_STRIDE;
+    const unsigned epoch = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tag1 = 2u * epoch + 1u, tag2 = 2u * epoch + 2u;
+
+    const int ns = pl.n_snap;
+    const int nv = 2 * (ns + 1); // values of the first exchange
+    const int s0 = LONG_WAVE_SOURCES * wave;
+    const int nvec = p.nvec;
+    const int64_t row = t * (int64_t)nvec;
+    const int v = chunk * 64 + lane;
+    bool ok[1];
+    ok[0] = v < nvec;
+    const int vc = ok[0] ? v : nvec - 1;
+
+    // every load of the wave in flight at once: its snapshots (a slot past the
+    // last reads the token-independent q row instead and counts as zero), q,
+    // and gamma (wave 0) or the prefix and addends (wave 1)
+    uint4 k[LONG_WAVE_SOURCES][1];
+    {
+        const uint4* ptr[LONG_WAVE_SOURCES];
+#pragma unroll
+        for (int j = 0; j < LONG_WAVE_SOURCES; ++j)
+            ptr[j] = pl.snaps[s0 + j];
+#pragma unroll
+        for (int j = 0; j < LONG_WAVE_SOURCES; ++j) {
+            const bool real = s0 + j < ns; // the same in every lane
+            const uint4 x = load_stream(real ? ptr[j] + row + vc : p.query + vc);
+            k[j][0] = real ? x : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const uint4 q = p.query[vc];
+    uint4 g = make_uint4(0u, 0u, 0u, 0u), kp[1] = {make_uint4(0u, 0u, 0u, 0u)};
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
+    unsigned long long* page = rec1 + (size_t)(chunk + LONG_PAGE * wave) * REC1_CHUNK;
+    if (wave == 0) {
+        g = p.gamma[vc];
+    } else {
+        // A1, and the folded prefix's A2 values (2N, 2N + 1, in page 1)
+        uint4 a[1], bb[1], c[1];
+        a[0] = load_stream(&p.prefix[row + vc]);
+        bb[0] = load_stream(&p.add[row + vc]);
+        c[0] = ADD2 ? load_stream(&p.add2[row + vc]) : make_uint4(0u, 0u, 0u, 0u);
+        fold_add<ADD2, 1>(a, bb, c, kp);
+        if (ok[0])
+            store_stream(&p.out_prefix[row + v], kp[0]);
+        const float2 pp = source_partial<1>(kp, &q, ok);
+        const float part[2] = {pp.x, pp.y};
+        const float wt = wave_totals<2>(part, lane);
+        const int wv = bfly_index<2>(lane);
+        if (wv >= 0)
+            publish(&page[2 * ns - 64 + wv], REC_STRIDE, tag1, wt);
+    }
+
+    // A2 of the wave's snapshots: lane v ends with value 64w + v
+    {
+        float part[2 * LONG_WAVE_SOURCES];
+        source_partials<LONG_WAVE_SOURCES, 1>(k, &q, ok, part);
+        fence_sources<LONG_WAVE_SOURCES, 1>(k);
+        const float wt = wave_totals<2 * LONG_WAVE_SOURCES>(part, lane);
+        if (2 * s0 + lane < 2 * ns)
+            publish(&page[lane], REC_STRIDE, tag1, wt);
+    }
+
+    // A3: lane 2j of the wave's page holds sum k_s^2 and lane 2j + 1 q.k_s, s = 32w + j
+    const bool want = 2 * s0 + lane < nv;
+    const unsigned long long ready_zero = (unsigned long long)tag1 << 32; // absent: reads as 0
+    float tv = 0.f;
+    for (int c0 = 0; c0 < C; c0 += 8) {
+        unsigned long long r0[8];
+        int off = p.l2_polls ? 0 : REC_STRIDE; // the L2 copies first (see publish)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cj = c0 + j;
+            r0[j] = cj < C && want ? peek(&rec1[(cj + LONG_PAGE * wave) * REC1_CHUNK + off + lane]) : ready_zero;
+        }
+        for (unsigned polls = 0;; ++polls) {
+            bool ready = true;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ready &= tag_of(r0[j]) == tag1;
+            if (ready)
+                break;
+            if (polls >= p.spin_limit) {
+                atomicAdd(p.timeouts, 1u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (tag_of(r0[j]) != tag1)
+                        r0[j] = gave_up(tag1);
+                break;
+            }
+            if (polls >= p.l2_polls)
+                off = REC_STRIDE; // then the device-scope copies
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int cj = c0 + j;
+                if (cj < C && want && tag_of(r0[j]) != tag1)
+                    r0[j] = peek(&rec1[(cj + LONG_PAGE * wave) * REC1_CHUNK + off + lane]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            tv += __uint_as_float((unsigned)r0[j]);
+    }
+    const float qd = dpp<0xb1>(tv); // quad_perm [1,0,3,2]: lane 2j gets lane 2j+1's value
+    const bool src = (lane & 1) == 0 && want;
+    const float z = src ? rsqrtf(tv * p.inv_h + p.eps) * qd : -INFINITY;
+    const float zm = wave_max(z);
+    const float e = src ? __expf(z - zm) : 0.f;
+    const float den = wave_sum(e);
+    if (lane == 0) {
+        zs[wave][0] = zm;
+        zs[wave][1] = den;
+    }
+    __syncthreads();
+    // the same bits in both waves and in every chunk: wave 0's terms first
+    const float zmax = fmaxf(zs[0][0], zs[1][0]);
+    const float total = zs[0][1] * __expf(zs[0][0] - zmax) + zs[1][1] * __expf(zs[1][0] - zmax);
+    const float al = e * (__expf(zm - zmax) / total);
+    float alpha[LONG_WAVE_SOURCES];
+#pragma unroll
+    for (int i = 0; i < LONG_WAVE_SOURCES; ++i)
+        alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * i));
+
+    // A4: the wave's snapshots (wave 1's slot of the folded prefix holds zero),
+    // then wave 1 adds the folded prefix's term and hands its mixture over
+    float x[1][8];
+    combine<LONG_WAVE_SOURCES, 1>(k, alpha, ok, x);
+    if (wave == 1) {
+        const float an = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * (ns - s0)));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t A = word(kp[0], w);
+            xs[2 * w][lane] = __builtin_fmaf(an, lo_f32(A), x[0][2 * w]);
+            xs[2 * w + 1][lane] = __builtin_fmaf(an, hi_f32(A), x[0][2 * w + 1]);
+        }
+    }
+    __syncthreads();
+    if (wave == 1)
+        return;
+    float sx = 0.f;
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+        x[0][e8] += xs[e8][lane];
+        sx = __builtin_fmaf(x[0][e8], x[0][e8], sx);
+    }
+    sx = wave_sum(ok[0] ? sx : 0.f);
+
+    // A5: as in kernel S (one wave)
+    unsigned long long* rec2 = p.rec2 + (size_t)slot * REC2_SLOT;
+    if (lane == 0)
+        publish(&rec2[chunk], MAX_CHUNKS, tag2, sx);
+    int off = p.l2_polls ? 0 : MAX_CHUNKS;
+    unsigned long long w2 = lane < C ? peek(&rec2[off + lane]) : (unsigned long long)tag2 << 32;
+    for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
+        if (polls >= p.spin_limit) {
+            atomicAdd(p.timeouts, 1u);
+            w2 = gave_up(tag2);
+            break;
+        }
+        if (polls >= p.l2_polls)
+            off = MAX_CHUNKS;
+        __builtin_amdgcn_s_sleep(1);
+        w2 = peek(&rec2[off + lane]);
+    }
+    const float ssum = wave_sum(__uint_as_float((unsigned)w2));
+    if (chunk == 0 && lane == 0) // every chunk has published its second record: all have read the epoch
+        advance_epoch(p, state, epoch, slot, C);
+    const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
+    if (ok[0]) {
+        store_stream(&p.out_norm[row + v], normalise(x[0], rstd, g));
+        if (p.out_mix)
+            store_stream(&p.out_mix[row + v], pack_scaled(x[0], 1.0f));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The standalone bf16 addition (the unfused tail): 16-byte vectors, grid-stride,
 // plus a scalar tail of n % 8 elements.
 __global__ __launch_bounds__(256) void bf16_add_kernel(const uint4* a, const uint4* b, uint4* out,
@@ -1297,6 +1524,9 @@ const std::array<Kernel, MAX_SPLIT_SNAP + 1> kSpSmall[2] = {
 // split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
 const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8, 4>(Seq{}),
                                                       split_table<true, 512, 8, 4>(Seq{})};
+// split hidden, two-wave form (32..MAX_SPLIT_LONG_SNAP snapshots)
+using KernelSplitLong = void (*)(ParamsSplitLong);
+const KernelSplitLong kSpLong[2] = {&fwd_split_long<false>, &fwd_split_long<true>};
 // the hybrid of the two
 const std::array<Kernel, MAX_SNAP + 1> kHybrid[2] = {hybrid_table<false>(Seq{}), hybrid_table<true>(Seq{})};
 
@@ -1532,6 +1762,26 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     p.xcd_skew = g_xcd_skew;
 
     const int a2 = add2 ? 1 : 0;
+    if (pl.variant == 2 || pl.variant == 3) {
+        p.rec1 = sc->rec1;
+        p.rec2 = sc->rec2;
+        p.state = sc->state;
+        p.timeouts = sc->timeouts;
+    }
+    if (n_snapshots > MAX_SPLIT_SNAP && pl.variant == 2) {
+        // the split kernel's two-wave form: one table of snapshot pointers,
+        // its tail repeating the last snapshot (never read: see fwd_split_long)
+        ParamsSplitLong lp{};
+        lp.p = p;
+        for (int s = 0; s < LONG_TABLE; ++s)
+            lp.snaps[s] = static_cast<const uint4*>(snapshots[s < n_snapshots ? s : n_snapshots - 1]);
+        lp.n_snap = n_snapshots;
+        void* largs[] = {&lp};
+        if (hipLaunchKernel(reinterpret_cast<const void*>(kSpLong[a2]), dim3((unsigned)pl.grid), dim3(pl.threads),
+                            largs, 0, stream) != hipSuccess)
+            return ATTNRES_EHIP;
+        return ATTNRES_OK;
+    }
     if (n_snapshots > MAX_SNAP && pl.variant == 1) {
         // batched sources: batch 0 = p' + snapshots 0..11, then full batches of
         // 12 and a last batch of 1..12
@@ -1551,10 +1801,6 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
     }
     Kernel fn = nullptr;
     if (pl.variant == 2 || pl.variant == 3) {
-        p.rec1 = sc->rec1;
-        p.rec2 = sc->rec2;
-        p.state = sc->state;
-        p.timeouts = sc->timeouts;
         if (pl.variant == 3)
             fn = kHybrid[a2][n_snapshots];
         else

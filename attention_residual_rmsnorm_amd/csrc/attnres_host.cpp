@@ -77,6 +77,25 @@ bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
 // 1-wave 13.60 against 4-wave 15.64 us; M = 288: 2-wave 14.55 against 16.05;
 // M = 300 and 320: 4-wave 15.98 and 17.21 against 18.0 and 19.0 for 2-wave).
 // nw is a multiple of 8 so the chunks of a token keep one workgroup id mod 8.
+// The split kernel's two-wave form for 32..MAX_SPLIT_LONG_SNAP snapshots:
+// chunks of 64 vectors, two waves each (each holding half of the sources), at
+// most SPLIT_LONG_MAX_CHUNKS per token.
+bool plan_split_long(int64_t M, int nvec, Plan& pl)
+{
+    const int chunks = (nvec + 63) / 64;
+    if (chunks > SPLIT_LONG_MAX_CHUNKS || M > MAX_SPLIT_TOKENS)
+        return false;
+    pl = Plan{};
+    pl.variant = 2;
+    pl.vpt = 1;
+    pl.threads = 128;
+    pl.chunks = chunks;
+    pl.grid = 8 * (int64_t)chunks * ((M + 7) / 8);
+    pl.split_threads = 128;
+    pl.split_slots = M;
+    return true;
+}
+
 bool plan_hybrid(int64_t M, int nvec, int waves, Plan& pl)
 {
     if (nvec <= 512 || nvec > 1024 || M < 1 || !(waves == 0 || waves == 1 || waves == 2 || waves == 4))
@@ -198,16 +217,20 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     const int nvec = (int)(H / 8);
     // More sources than one pass of kernel W holds: W takes them in batches of
     // MAX_SNAP (instantiated for 2 and 4 vectors per thread); the split kernel
-    // takes up to MAX_SPLIT_SNAP in its 1-2-wave family.
+    // takes up to MAX_SPLIT_SNAP in its 1-2-wave family, and up to
+    // MAX_SPLIT_LONG_SNAP in its two-wave form (chunks of 64 vectors).
     const bool many = n > MAX_SNAP;
     const int wg_vpt = many ? nvec <= 1024 ? 2 : 4 : 0;
     const bool split_ok = !many || n <= MAX_SPLIT_SNAP;
+    const bool split_long = n > MAX_SPLIT_SNAP && n <= MAX_SPLIT_LONG_SNAP;
     if (force_variant == 1) {
         if (many && force_param == 1)
             return ATTNRES_EINVAL;
         return plan_wg(M, nvec, force_param ? force_param : wg_vpt, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     }
     if (force_variant == 2) {
+        if (split_long && force_param <= 1)
+            return plan_split_long(M, nvec, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
         if (!split_ok || (many && force_param > 2))
             return ATTNRES_EINVAL;
         return plan_split(M, nvec, many && force_param == 0 ? 2 : force_param, pl) ? ATTNRES_OK
@@ -266,6 +289,14 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // N = 31: 16.76 against 18.34 us for 1-wave; M = 16, N = 20: 8.74
     // against 9.66; H = 12288, M = 32, N = 31: 1-wave 11.65 against 13.00;
     // one token within 0.4 us either way).
+    // 32..63 snapshots (the split's two-wave form, rows of at most 8192): up
+    // to 96 tokens, but up to 64 on rows of 7168..8192 below 52 snapshots,
+    // else W's batches (H = 7168, M = 1, N = 32 / 63: 8.72 / 9.06 against
+    // 19.49 / 34.90 us; M = 64, N = 32: 16.86 against 19.91; M = 80, N = 32:
+    // W 19.93 against 22.32; M = 96, N = 52: 29.41 against 30.55, N = 44: W
+    // 26.52 against 28.00; H = 8192, M = 64, N = 32: 20.68 against 20.88;
+    // H = 3584, M = 96, N = 63: 16.76 against 28.14; H = 896, M = 96, N =
+    // 32: 8.73 against 12.76).
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 3.88
@@ -279,7 +310,11 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    against 5.77; M = 1, N = 2 and 3: 3.88 and 4.01 against 4.04 and
     //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
-    if (many) {
+    if (split_long) {
+        const int most = !long_rows || n >= SPLIT_LONG_WIDE_SNAP ? SPLIT_LONG_TOKENS : SPLIT_LONG_TOKENS_LONG_ROWS;
+        if (M <= most && plan_split_long(M, nvec, pl))
+            return ATTNRES_OK;
+    } else if (many) {
         const bool mid_m = M > SPLIT_SMALL_TOKENS && M <= SPLIT_SMALL_TOKENS_WIDE; // 17..32
         const int waves = !long_rows                      ? 1
                           : nvec > VERY_LONG_ROW_VECTORS ? (mid_m ? 1 : 2)

@@ -85,7 +85,9 @@ int main()
                                 EXPECT((int64_t)pl.threads * pl.vpt * pl.chunks * 8 >= h);
                                 if (n > MAX_SNAP)
                                     EXPECT((pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4)) ||
-                                           (pl.variant == 2 && n <= MAX_SPLIT_SNAP && pl.threads <= 128));
+                                           (pl.variant == 2 && n <= MAX_SPLIT_SNAP && pl.threads <= 128) ||
+                                           (pl.variant == 2 && n <= MAX_SPLIT_LONG_SNAP && pl.threads == 128 &&
+                                            pl.chunks <= SPLIT_LONG_MAX_CHUNKS));
                                 // the single-group table is built for at most SHORT_WG_THREADS
                                 if (pl.single_group)
                                     EXPECT(pl.variant == 1 && pl.vpt == 1 && pl.threads <= SHORT_WG_THREADS &&

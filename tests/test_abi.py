@@ -231,7 +231,16 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(65, 13, 7168) == (2, 7, 128)    # 2-wave from 65 to 96
     assert ar.attnres_plan(96, 31, 7168) == (2, 7, 128)
     assert ar.attnres_plan(97, 13, 7168) == (1, 1, 448)
-    assert ar.attnres_plan(1, 32, 7168) == (1, 1, 448)     # more than 31 snapshots: W's batches
+    assert ar.attnres_plan(1, 32, 7168) == (2, 14, 128)    # 32..63 snapshots: the split's two-wave
+    assert ar.attnres_plan(64, 51, 7168) == (2, 14, 128)   # form up to 64 tokens on long rows,
+    assert ar.attnres_plan(65, 51, 8192) == (1, 1, 512)
+    assert ar.attnres_plan(65, 52, 7168) == (2, 14, 128)   # up to 96 from 52 snapshots on,
+    assert ar.attnres_plan(96, 63, 7168) == (2, 14, 128)
+    assert ar.attnres_plan(96, 32, 896) == (2, 2, 128)     # and on shorter rows;
+    assert ar.attnres_plan(1, 40, 8192) == (2, 16, 128)    # at most 16 chunks per token
+    assert ar.attnres_plan(5, 36, 1000) == (2, 2, 128)
+    assert ar.attnres_plan(97, 52, 7168) == (1, 1, 448)    # then W's batches,
+    assert ar.attnres_plan(1, 64, 7168) == (1, 1, 448)     # and W alone at 64 snapshots
     assert ar.attnres_plan(24, 20, 3584) == (2, 7, 64)     # shorter rows: 1-wave chunks up to 96
     assert ar.attnres_plan(96, 31, 896) == (2, 2, 64)
     assert ar.attnres_plan(97, 13, 896)[0] == 1
@@ -291,13 +300,18 @@ def test_set_variant_validation():
         assert ar.attnres_plan(1, 4, 7168) == (2, 2, 448)
         ar.attnres_set_variant(2, 1)
         assert ar.attnres_plan(3, 4, 7168) == (2, 14, 64)
+        assert ar.attnres_plan(200, 63, 7168) == (2, 14, 128)  # the two-wave form, forced past 96 tokens
+        with pytest.raises(ar.AttnResError):  # more than 16 chunks per token
+            ar.attnres_plan(1, 40, 16384)
+        with pytest.raises(ar.AttnResError):  # two record pages hold at most 63 snapshots
+            ar.attnres_plan(1, 64, 7168)
         ar.attnres_set_variant(1, 1)
         assert ar.attnres_plan(1, 4, 7168) == (1, 1, 896)
         with pytest.raises(ar.AttnResError):  # no one-vector batched kernel
             ar.attnres_plan(1, 13, 7168)
         ar.attnres_set_variant(2, 2)
         assert ar.attnres_plan(1, 31, 7168) == (2, 7, 128)
-        with pytest.raises(ar.AttnResError):  # beyond the split kernel's registers
+        with pytest.raises(ar.AttnResError):  # 32..63: only the two-wave form
             ar.attnres_plan(1, 32, 7168)
         ar.attnres_set_variant(2, 4)
         with pytest.raises(ar.AttnResError):  # more than 12 only in the 1-2-wave family

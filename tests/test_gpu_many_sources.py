@@ -46,7 +46,10 @@ def variant(request, ar):
 
 
 SHAPES = [(1, 7168, 13), (3, 7168, 24), (2, 7168, 25), (5, 1000, 36), (2, 520, 64), (33, 7168, 30),
-          (2, 7176, 14), (3, 16384, 20), (1, 8, 64), (260, 512, 13), (1, 7168, 31), (17, 1000, 16), (8, 520, 31)]
+          (2, 7176, 14), (3, 16384, 20), (1, 8, 64), (260, 512, 13), (1, 7168, 31), (17, 1000, 16), (8, 520, 31),
+          # the split's two-wave form (32..63 snapshots: wave 1 holding 1 to 32 sources)
+          (1, 7168, 32), (2, 7168, 33), (3, 7168, 47), (4, 7168, 48), (1, 7168, 63), (9, 8192, 50),
+          (17, 896, 40), (12, 1000, 49), (1, 8, 63)]
 
 
 @pytest.mark.parametrize("variant", [(0, 0), (1, 2), (1, 4), (2, 1), (2, 2)], ids=["auto", "W2", "W4", "S1w", "S2w"],
@@ -79,6 +82,26 @@ def test_many_sources_dispatch_bounds(ar, orc, M, N, H):
     gp, gn = P.run_gpu(case)
     rp, rn = P.run_oracle(orc, case)
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+
+
+@pytest.mark.parametrize("H", [7168, 8192, 896])
+@pytest.mark.parametrize("N", [32, 51, 52, 63])
+@pytest.mark.parametrize("M", [1, 8, 9, 64, 65, 96, 97])
+def test_split_long_dispatch_bounds(ar, orc, M, N, H):
+    """The automatic dispatch from 32 to 63 snapshots on both sides of its
+    bounds (the split kernel's two-wave form up to 96 tokens, up to 64 on
+    rows of 7168..8192 below 52 snapshots; then kernel W's batches), with
+    the pre-norm mixture output."""
+    case = W.make_case(cfg=87, M=M, H=H, N=N, add2=(M % 2 == 0))
+    say("two-wave split, auto", M, H, N, ar.attnres_plan(M, N, case.H))
+    gp, gn, gm = P.run_gpu_mix(case)
+    rp, rn, rm = P.run_oracle_mix(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
+    P.assert_mix_parity(gm, rm, "M=%d H=%d N=%d" % (M, H, N))
+
+
+def test_split_long_no_timeouts(ar):
+    assert ar.attnres_debug_timeouts() == 0
 
 
 def test_many_sources_scaled_and_presummed(ar, orc):

@@ -555,7 +555,7 @@ def test_no_barrier_timeouts(ar):
 def test_bounded_waits_give_up(ar, orc):
     """The split kernel's waits at its per-token barriers are bounded.  With
     the spin limit forced down to one re-poll from the host, calls of both
-    exchange forms still finish and the waits that give up are counted; each
+    exchange forms and of the two-wave form (32..63 snapshots) still finish and the waits that give up are counted; each
     such call, run on a cleared scratch, leaves out_prefix exact and every
     out_norm element either within the bar of the oracle or NaN (a wait that
     gives up takes NaN for what it did not receive).  Once the scratch is
@@ -564,13 +564,14 @@ def test_bounded_waits_give_up(ar, orc):
 
     two = case_for("cfg4", lambda: W.config_case("cfg4"))  # two exchanges
     one = case_for("cfg2", lambda: W.config_case("cfg2"))  # the Gram form's one
-    refs = [P.run_oracle(orc, c) for c in (two, one)]
+    many = W.make_case(cfg=87, M=3, N=40, add2=True)      # the two-wave form's two record pages
+    refs = [P.run_oracle(orc, c) for c in (two, one, many)]
     forced = 0
     nan_seen = 0
     ar.attnres_set_variant(2, 1)
     try:
         for rep in range(6):
-            for case, (rp, rn) in zip((two, one), refs):
+            for case, (rp, rn) in zip((two, one, many), refs):
                 ar.attnres_debug_reset_scratch()
                 ar.attnres_debug_set_spin_limit(1)
                 try:
@@ -592,7 +593,7 @@ def test_bounded_waits_give_up(ar, orc):
     say("forced timeouts", forced, "NaN elements", nan_seen)
     assert forced > 0
     assert ar.attnres_debug_timeouts() == 0
-    for case in (two, one):
+    for case in (two, one, many):
         gp, gn = P.run_gpu(case)
         rp, rn = P.run_oracle(orc, case)
         P.assert_parity(gp, gn, rp, rn, "after the reset")

@@ -67,9 +67,11 @@ def out_pair(M, H):
 # exchanges and the Gram form's one), one token, the most sources the split kernel
 # takes, calls kernel W serves (no scratch), the hybrid of W and split chunks
 # just past the CU count (its split part at the most tokens the automatic
-# dispatch gives it), 2-wave chunks again, and more than 12 snapshots at the
-# most tokens the split takes them
-CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (92, 8), (96, 20)]
+# dispatch gives it), 2-wave chunks again, more than 12 snapshots at the
+# most tokens the split takes them, and the split's two-wave form (32..63
+# snapshots, its second record page) at its most tokens and at two
+CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (92, 8), (96, 20),
+         (96, 63), (2, 33)]
 
 
 def test_noalloc_matches_fwd(ar, orc):
