@@ -852,13 +852,16 @@ __global__ __launch_bounds__(MAXB, (VPT == 2 ? 4 : 1)) void fwd_wg_long(ParamsLo
 // and wrap to 0, so the tags 2E+1 and 2E+2 are never 0, the tag of a record
 // that was never written (or was cleared).  A record from an earlier call
 // could match a later call's tag only if exactly a multiple of EPOCH_PERIOD
-// calls lay between the two; any such record sits at a chunk index the calls
-// in between did not use (each call rewrites the records of the chunks it
-// uses), and the call that wraps the epoch clears every record at chunk
-// indices it does not use.  The clearing runs in chunk 0 after every chunk of
-// its call has read the records it needs, and no chunk of this call reads
-// those indices; the next call on the token slot starts after this kernel
-// ends (calls on one device's scratch are ordered).
+// calls lay between the two, none of which rewrote it.  The call that wraps
+// the epoch therefore clears every record it does not read itself: the chunk
+// indices it does not use, the first-exchange values past its own count in
+// those it does, and the second exchange's records when it has none (the
+// Gram form without its fallback).  Only the wrapping call's own records
+// survive the wrap, and they could be matched only by the wrapping call of a
+// later period if no call of that whole period rewrote them.  The clearing
+// runs in chunk 0 after every chunk of its call has read E, touches no record
+// any chunk of this call still reads, and the next call on the token slot
+// starts after this kernel ends (calls on one device's scratch are ordered).
 constexpr unsigned EPOCH_PERIOD = 0x7fffffffu;
 
 __device__ __forceinline__ unsigned long long gave_up(unsigned tag)
@@ -866,23 +869,40 @@ __device__ __forceinline__ unsigned long long gave_up(unsigned tag)
     return ((unsigned long long)tag << 32) | 0x7fc00000u; // the tag, and a quiet NaN
 }
 
-__device__ __noinline__ void clear_unused_chunks(const Params& p, int64_t slot, int C)
+// What one call on a token slot reads: chunk indices c < C with first-exchange
+// values [0, nv0); the two-wave form also indices SPLIT_LONG_MAX_CHUNKS + c
+// with values [0, nv1); and the second exchange's records c < C unless the
+// call had no second exchange.
+struct RecordUse {
+    int C, nv0, nv1;
+    bool rec2;
+};
+
+__device__ __noinline__ void clear_unread_records(const Params& p, int64_t slot, RecordUse u)
 {
     unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
     unsigned long long* rec2 = p.rec2 + (size_t)slot * REC2_SLOT;
-    for (int c = C; c < MAX_CHUNKS; ++c) {
-        for (int v = 0; v < REC1_CHUNK; ++v) // both copies
+    for (int c = 0; c < MAX_CHUNKS; ++c) {
+        const int page1 = c - SPLIT_LONG_MAX_CHUNKS;
+        const int used = c < u.C ? u.nv0 : page1 >= 0 && page1 < u.C ? u.nv1 : 0;
+        for (int v = used; v < REC_STRIDE; ++v) { // both copies
             __hip_atomic_store(&rec1[c * REC1_CHUNK + v], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&rec2[c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&rec2[MAX_CHUNKS + c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rec1[c * REC1_CHUNK + REC_STRIDE + v], 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (c >= u.C || !u.rec2) {
+            __hip_atomic_store(&rec2[c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rec2[MAX_CHUNKS + c], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
-__device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, unsigned epoch, int64_t slot, int C)
+__device__ __forceinline__ void advance_epoch(const Params& p, unsigned* state, unsigned epoch, int64_t slot,
+                                              RecordUse u)
 {
     const unsigned next = epoch + 1u >= EPOCH_PERIOD ? 0u : epoch + 1u;
     if (next == 0u)
-        clear_unused_chunks(p, slot, C);
+        clear_unread_records(p, slot, u);
     __hip_atomic_store(state, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1140,7 +1160,7 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
         // chunk's first record, so every workgroup of the token has read E.
         ssum = gram_ssum;
         if (chunk == 0 && tid == 0)
-            advance_epoch(p, state, epoch, slot, C);
+            advance_epoch(p, state, epoch, slot, RecordUse{C, NV, 0, false});
     } else {
         if (lane == 0)
             red2[wave] = sx;
@@ -1172,7 +1192,7 @@ __device__ __forceinline__ void split_chunk(const Params& p, int b, int nthreads
             }
             ssum = wave_sum(__uint_as_float((unsigned)w2));
             if (chunk == 0 && tid == 0) // every chunk has published its second record: all have read the epoch
-                advance_epoch(p, state, epoch, slot, C);
+                advance_epoch(p, state, epoch, slot, RecordUse{C, NV, 0, true});
             if (!PERWAVE && lane == 0)
                 ssum_sh = ssum;
         }
@@ -1413,7 +1433,7 @@ __global__ __launch_bounds__(128, 1) void fwd_split_long(ParamsSplitLong pl)
     }
     const float ssum = wave_sum(__uint_as_float((unsigned)w2));
     if (chunk == 0 && lane == 0) // every chunk has published its second record: all have read the epoch
-        advance_epoch(p, state, epoch, slot, C);
+        advance_epoch(p, state, epoch, slot, RecordUse{C, 64, nv - 64, true});
     const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
     if (ok[0]) {
         store_stream(&p.out_norm[row + v], normalise(x[0], rstd, g));

@@ -643,7 +643,8 @@ EPOCH_PERIOD = 0x7FFFFFFF
 
 def test_epoch_wrap(ar, orc):
     """The split kernel's per-token epoch wraps from 2^31 - 2 to 0, and the
-    wrapping call clears the records of the chunk indices it does not use.
+    wrapping call clears the records it does not read (here: of the chunk
+    indices it does not use).
     A call with 14 chunks (one wave each) at epoch 5 leaves records at chunk
     indices 7..13; calls with 7 chunks (two waves each) then run across the
     wrap; another 14-chunk call on different inputs at epoch 5 again expects
@@ -677,21 +678,86 @@ def test_epoch_wrap(ar, orc):
         ar.attnres_debug_reset_scratch()
 
 
+def test_epoch_wrap_value_slots(ar, orc):
+    """Across the wrap with the same chunk count but fewer first-exchange
+    values: a 31-snapshot call at epoch 5 fills all 64 value slots of chunk
+    indices 0..13, 8-snapshot calls (18 values) run across the wrap, and a
+    31-snapshot call on other inputs at epoch 5 must still be exact, because
+    the wrapping call cleared value slots 18..63 as well."""
+    a = case_for(("wrapv", 0), lambda: W.make_case(cfg=85, M=8, N=31, add2=True))
+    b = case_for(("wrapv", 1), lambda: W.make_case(cfg=86, M=8, N=31, add2=False))
+    c = case_for(("wrapv", 2), lambda: W.make_case(cfg=84, M=8, N=8, add2=True))
+    ra, rb, rc = P.run_oracle(orc, a), P.run_oracle(orc, b), P.run_oracle(orc, c)
+    try:
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_debug_set_slot_rotation(False)
+        ar.attnres_set_variant(2, 1)
+        assert ar.attnres_plan(8, 31, 7168)[1] == 14 and ar.attnres_plan(8, 8, 7168)[1] == 14
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(a), *ra, "31 snapshots at epoch 5")
+        ar.attnres_debug_set_epoch(EPOCH_PERIOD - 2)
+        for i in range(4):
+            say("wrap: 8-snapshot call", i)
+            P.assert_parity(*P.run_gpu(c), *rc, "8 snapshots, call %d across the wrap" % i)
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(b), *rb, "31 snapshots at epoch 5 after the wrap")
+        assert ar.attnres_debug_timeouts() == 0
+    finally:
+        ar.attnres_set_variant(0, 0)
+        ar.attnres_debug_set_slot_rotation(True)
+        ar.attnres_debug_reset_scratch()
+
+
+def test_epoch_wrap_two_wave(ar, orc):
+    """The same across the wrap for the split kernel's two-wave form (32..63
+    snapshots), whose second record page sits at chunk indices 16..29: a
+    two-wave call at epoch 5 leaves records there, one-wave 14-chunk calls
+    run across the wrap (the wrapping call clears indices 14..31), and a
+    two-wave call on other inputs at epoch 5 again expects the tags the old
+    page-1 records carry, and must still be exact."""
+    a = case_for(("wrap2", 0), lambda: W.make_case(cfg=82, M=8, N=40, add2=True))
+    b = case_for(("wrap2", 1), lambda: W.make_case(cfg=83, M=8, N=40, add2=False))
+    c = case_for(("wrap2", 2), lambda: W.make_case(cfg=84, M=8, N=8, add2=True))
+    ra, rb, rc = P.run_oracle(orc, a), P.run_oracle(orc, b), P.run_oracle(orc, c)
+    try:
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_debug_set_slot_rotation(False)  # every call on token slots 0..7
+        assert ar.attnres_plan(8, 40, 7168) == (2, 14, 128)
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(a), *ra, "two-wave call at epoch 5")
+        ar.attnres_set_variant(2, 1)
+        assert ar.attnres_plan(8, 8, 7168)[1] == 14
+        ar.attnres_debug_set_epoch(EPOCH_PERIOD - 2)
+        for i in range(4):  # epochs 2^31 - 3 .. 2^31 - 2, then 0 and 1
+            say("wrap: one-wave call", i)
+            P.assert_parity(*P.run_gpu(c), *rc, "14 one-wave chunks, call %d across the wrap" % i)
+        ar.attnres_set_variant(0, 0)
+        ar.attnres_debug_set_epoch(5)
+        P.assert_parity(*P.run_gpu(b), *rb, "two-wave call at epoch 5 after the wrap")
+        assert ar.attnres_debug_timeouts() == 0
+    finally:
+        ar.attnres_set_variant(0, 0)
+        ar.attnres_debug_set_slot_rotation(True)
+        ar.attnres_debug_reset_scratch()
+
+
 def test_concurrent_streams(ar, orc):
     """Split-kernel calls enqueued on two streams with no ordering between
-    them (two exchanges and the Gram form's one, 1- and 2-wave chunks, and
-    the hybrid launch's 1- and 2-wave chunks): each call takes its own token
+    them (two exchanges and the Gram form's one, 1- and 2-wave chunks, the
+    hybrid launch's 1- and 2-wave chunks, and the two-wave form's two record
+    pages at 40 snapshots): each call takes its own token
     slots of the scratch, so calls that run at the same time do not share
     records.  Every output against the oracle, and no wait given up."""
     import torch
 
     cases = [W.make_case(cfg=90 + i, M=32, N=(12, 4, 8)[i % 3], add2=True) for i in range(6)]
-    cases += [W.make_case(cfg=96, M=264, N=12, add2=True), W.make_case(cfg=97, M=288, N=4, add2=True)]
+    cases += [W.make_case(cfg=96, M=264, N=12, add2=True), W.make_case(cfg=97, M=288, N=4, add2=True),
+              W.make_case(cfg=98, M=16, N=40, add2=True)]
     refs = [P.run_oracle(orc, c) for c in cases]
     d = P.dev
     ins = [(d(c.prefix), d(c.add), d(c.add2), [d(s) for s in c.snapshots], d(c.query), d(c.gamma)) for c in cases]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    ar.attnres_debug_reset_scratch()  # slots from 0: the 16 calls take 464 of the 512
+    ar.attnres_debug_reset_scratch()  # slots from 0: the 18 calls take 496 of the 512
     outs = []
     for rep in range(2):
         for i, c in enumerate(cases):
