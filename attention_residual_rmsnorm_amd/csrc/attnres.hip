@@ -1488,8 +1488,14 @@ __global__ __launch_bounds__(HYBRID_WG_THREADS_MAX, 4) void fwd_hybrid(Params p)
     if ((int)blockIdx.x < p.wg_blocks) // uniform over the workgroup
         wg_tokens<NS, ADD2, 2, HYBRID_WG_THREADS_MAX, WG_GROUP, WG_LOOKAHEAD>(p, blockIdx.x, p.split_base,
                                                                              p.wg_blocks);
-    else
+    else {
+        // the chunks' waves first in their SIMDs' issue order: their exchanges
+        // otherwise wait behind the W tokens' streams on the same CUs (M = 304:
+        // N = 4 10.59 -> 9.72 us, N = 12 16.24 -> 15.66; M = 320: N = 8 13.76
+        // -> 13.28, N = 12 16.84 -> 16.29..16.55)
+        __builtin_amdgcn_s_setprio(3);
         split_chunk<NS, ADD2, HYBRID_WG_THREADS_MAX, 8>(p, (int)blockIdx.x - p.wg_blocks, p.split_threads);
+    }
 }
 
 template <bool A2, int... I>
