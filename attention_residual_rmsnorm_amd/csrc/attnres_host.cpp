@@ -98,23 +98,24 @@ bool plan_split_long(int64_t M, int nvec, Plan& pl)
 
 bool plan_hybrid(int64_t M, int nvec, int waves, Plan& pl)
 {
-    if (nvec <= 512 || nvec > 1024 || M < 1 || !(waves == 0 || waves == 1 || waves == 2 || waves == 4))
+    if (nvec <= 512 || nvec > 1024 || M < 1 ||
+        !(waves == 0 || waves == 1 || waves == 2 || waves == 4 || waves == HYBRID_HALF_ROW))
         return false;
     const int64_t nw = M > HYBRID_WG_TOKENS ? HYBRID_WG_TOKENS : (M / 2) / 8 * 8;
     const int64_t rest = M - nw;
     if (rest > MAX_SPLIT_TOKENS)
         return false;
     const int64_t groups = (rest + 7) / 8;
+    const int threads = round_up64((nvec + 1) / 2);
     if (waves == 0) {
-        waves = 4;
-        for (int w = 1; w < 4; w *= 2)
+        waves = HYBRID_HALF_ROW;
+        for (int w = 1; w <= 4; w *= 2)
             if (8 * (int64_t)((nvec + 64 * w - 1) / (64 * w)) * groups <= HYBRID_WG_TOKENS) {
                 waves = w;
                 break;
             }
     }
-    const int threads = round_up64((nvec + 1) / 2);
-    const int chunk_threads = 64 * waves;
+    const int chunk_threads = waves == HYBRID_HALF_ROW ? threads : 64 * waves;
     const int chunks = (nvec + chunk_threads - 1) / chunk_threads;
     pl = Plan{};
     pl.variant = 3;
@@ -207,7 +208,7 @@ bool valid_override(int variant, int param)
     case 0: return param == 0;
     case 1: return param == 0 || param == 1 || param == 2 || param == 4;
     case 2: return param >= 0 && param <= 8 && param != 3;
-    case 3: return param == 0 || param == 1 || param == 2 || param == 4;
+    case 3: return param == 0 || param == 1 || param == 2 || param == 4 || param == HYBRID_HALF_ROW;
     default: return false;
     }
 }

@@ -88,14 +88,15 @@ constexpr int64_t PREFILL_WG4_TOKENS = 2048;
 constexpr int64_t SHORT_WG_MAX_THREADS_TOTAL = 131072;
 
 // The hybrid launch (kernel W's workgroups for the first HYBRID_WG_TOKENS
-// tokens, one token each, and split chunks of 1, 2 or 4 waves for the rest:
-// the narrowest whose workgroups still number at most HYBRID_WG_TOKENS, one
-// per CU next to its W token), automatic for rows of LONG_ROW_VECTORS..1024
-// vectors, one pass of sources and HYBRID_WG_TOKENS < M <= HYBRID_MAX_TOKENS.
-// (Beyond, chunks either queue for a CU's second workgroup slot or, as wide
-// as half a row, lose to kernel W: M = 321, N = 12: 19.65 against 18.79 us.)
+// tokens, one token each, and split chunks for the rest: the narrowest of 1,
+// 2 and 4 waves whose workgroups still number at most HYBRID_WG_TOKENS, one
+// per CU next to its W token, else half rows, W's workgroup width), automatic
+// for rows of LONG_ROW_VECTORS..1024 vectors, one pass of sources and
+// HYBRID_WG_TOKENS < M <= HYBRID_MAX_TOKENS.  (Beyond, kernel W alone wins:
+// M = 384, N = 12: 19.25 against 19.58 us in half rows.)
 constexpr int HYBRID_WG_TOKENS = 256;
-constexpr int HYBRID_MAX_TOKENS = 320;
+constexpr int HYBRID_MAX_TOKENS = 352;
+constexpr int HYBRID_HALF_ROW = 8; // attnres_set_variant(3, 8): half-row chunks
 
 struct Plan {
     int variant = 0; // 1 = workgroup per token, 2 = split hidden, 3 = hybrid

@@ -237,9 +237,10 @@ int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunk
  * benchmarks: variant 0 = automatic (param 0); 1 = workgroup per token, param =
  * 16-byte vectors per thread (0 automatic, or 1, 2, 4); 2 = split hidden, param
  * = waves per workgroup (0 automatic, or 1, 2, 4..8); 3 = hybrid, param =
- * waves per split chunk (0 automatic, or 1, 2, 4; rows of 4104..8192
- * elements, at most 12 snapshots; below 257 tokens the workgroup-per-token
- * part takes about half of them).  A size the forced
+ * waves per split chunk (0 automatic, or 1, 2, 4, or 8 for half rows, the
+ * workgroup-per-token width; rows of 4104..8192 elements, at most 12
+ * snapshots; below 257 tokens the workgroup-per-token part takes about half
+ * of them).  A size the forced
  * variant cannot serve makes the fused call return ATTNRES_EINVAL.  Not thread-safe
  * with concurrent calls.  Returns ATTNRES_OK or ATTNRES_EINVAL.
  */

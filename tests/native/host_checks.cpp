@@ -109,7 +109,7 @@ int main()
                                            pl.split_base < m && m - pl.split_base <= MAX_SPLIT_TOKENS &&
                                            pl.split_slots == m - pl.split_base &&
                                            (pl.split_threads == 64 || pl.split_threads == 128 ||
-                                            pl.split_threads == 256) &&
+                                            pl.split_threads == 256 || pl.split_threads == pl.threads) &&
                                            pl.chunks <= MAX_CHUNKS &&
                                            (int64_t)pl.chunks * pl.split_threads * 8 >= h &&
                                            (int64_t)(pl.chunks - 1) * pl.split_threads * 8 < h &&
@@ -147,11 +147,16 @@ int main()
         EXPECT(make_plan(273, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 7 && pl.split_threads == 128);
         EXPECT(make_plan(288, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 7 && pl.grid == 256 + 224);
         EXPECT(make_plan(289, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.chunks == 4 && pl.split_threads == 256);
-        EXPECT(make_plan(HYBRID_MAX_TOKENS, 1, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 &&
+        EXPECT(make_plan(320, 1, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 &&
                pl.chunks == 4 && pl.split_threads == 256 && pl.grid == 512);
         EXPECT(make_plan(260, 12, 8192, 0, 0, pl) == ATTNRES_OK && pl.chunks == 16 && pl.threads == 512);
         EXPECT(make_plan(300, 12, 7168, 3, 1, pl) == ATTNRES_OK && pl.chunks == 14 && pl.split_threads == 64);
-        EXPECT(make_plan(300, 12, 7168, 3, 8, pl) == ATTNRES_EINVAL);
+        EXPECT(make_plan(300, 12, 7168, 3, 8, pl) == ATTNRES_OK && pl.chunks == 2 && pl.split_threads == 448);
+        EXPECT(make_plan(321, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 && pl.chunks == 2 &&
+               pl.split_threads == 448 && pl.grid == 256 + 8 * 2 * 9);
+        EXPECT(make_plan(352, 4, 8192, 0, 0, pl) == ATTNRES_OK && pl.variant == 3 && pl.chunks == 2 &&
+               pl.split_threads == 512);
+        EXPECT(make_plan(300, 12, 7168, 3, 7, pl) == ATTNRES_EINVAL);
         EXPECT(make_plan(HYBRID_MAX_TOKENS + 1, 12, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
         EXPECT(make_plan(300, 13, 7168, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);
         EXPECT(make_plan(300, 12, 896, 0, 0, pl) == ATTNRES_OK && pl.variant == 1);

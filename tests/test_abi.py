@@ -210,8 +210,10 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(257, 12, 7168) == (3, 14, 448)  # just past the CU count: the hybrid, 1-wave
     assert ar.attnres_plan(272, 12, 7168) == (3, 14, 448)  # chunks up to 16 left-over tokens,
     assert ar.attnres_plan(273, 12, 7168) == (3, 7, 448)   # 2-wave up to 32,
-    assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # 4-wave up to 64
-    assert ar.attnres_plan(321, 12, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(320, 12, 7168) == (3, 4, 448)   # 4-wave up to 64,
+    assert ar.attnres_plan(321, 12, 7168) == (3, 2, 448)   # half rows up to 96
+    assert ar.attnres_plan(352, 0, 7168) == (3, 2, 448)
+    assert ar.attnres_plan(353, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(384, 12, 7168) == (1, 1, 448)
     assert ar.attnres_plan(300, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(513, 12, 7168)[0] == 1
@@ -326,6 +328,8 @@ def test_set_variant_validation():
         assert ar.attnres_plan(20, 12, 7168) == (3, 7, 448)   # its chunks forced to 2 waves
         ar.attnres_set_variant(3, 4)
         assert ar.attnres_plan(300, 12, 7168) == (3, 4, 448)
+        ar.attnres_set_variant(3, 8)
+        assert ar.attnres_plan(300, 12, 7168) == (3, 2, 448)  # half-row chunks
     finally:
         ar.attnres_set_variant(0, 0)
 

@@ -290,12 +290,12 @@ def test_dispatch_boundaries(ar, orc, M, N):
 
 
 @pytest.mark.parametrize("N", [0, 1, 3, 4, 7, 8, 12])
-@pytest.mark.parametrize("M", [256, 257, 264, 288, 289, 319, 320, 321, 352, 383, 384, 385, 511])
+@pytest.mark.parametrize("M", [256, 257, 264, 288, 289, 319, 320, 321, 336, 352, 353, 383, 384, 385, 511])
 def test_hybrid_boundaries(ar, orc, M, N):
     """Past the CU count: the automatic dispatch's hybrid launch (kernel W on
-    the first 256 tokens, 1-, 2- or 4-wave split chunks on the rest) at its
-    bounds, and kernel W beyond it (two tokens on some CUs), every output
-    element against the oracle."""
+    the first 256 tokens, 1-, 2- or 4-wave split chunks or half rows on the
+    rest) at its bounds, and kernel W beyond it (two tokens on some CUs),
+    every output element against the oracle."""
     case = case_for(("hybrid", M, N), lambda: W.make_case(cfg=67, M=M, N=N, add2=(N % 2 == 0)))
     say("hybrid", M, N, ar.attnres_plan(M, N, case.H))
     gp, gn = P.run_gpu(case)

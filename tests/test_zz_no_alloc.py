@@ -69,9 +69,10 @@ def out_pair(M, H):
 # just past the CU count (its split part at the most tokens the automatic
 # dispatch gives it), 2-wave chunks again, more than 12 snapshots at the
 # most tokens the split takes them, and the split's two-wave form (32..63
-# snapshots, its second record page) at its most tokens and at two
+# snapshots, its second record page) at its most tokens and at two, and the
+# hybrid's half-row chunks at its most tokens
 CALLS = [(96, 12), (48, 12), (8, 4), (1, 12), (64, 31), (256, 12), (3, 0), (320, 12), (300, 4), (92, 8), (96, 20),
-         (96, 63), (2, 33)]
+         (96, 63), (2, 33), (352, 8)]
 
 
 def test_noalloc_matches_fwd(ar, orc):
