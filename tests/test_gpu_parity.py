@@ -303,6 +303,28 @@ def test_hybrid_boundaries(ar, orc, M, N):
     P.assert_parity(gp, gn, rp, rn, "M=%d N=%d" % (M, N))
 
 
+@pytest.mark.parametrize("H", [8192, 4104])
+@pytest.mark.parametrize("N", [4, 12])
+@pytest.mark.parametrize("M", [300, 352])
+def test_hybrid_other_widths(ar, orc, M, N, H):
+    """The hybrid launch on rows of 1,024 and 513 vectors, whose workgroups
+    are 512 and 320 threads wide (automatic at H = 8192, forced at 4104, where
+    the automatic dispatch takes other kernels): 4- or 2-wave chunks at 300
+    tokens, half-row chunks (8 and 5 waves) at 352, against the oracle."""
+    case = case_for(("hybridw", M, N, H), lambda: W.make_case(cfg=66, M=M, H=H, N=N, add2=(N % 2 == 0)))
+    try:
+        if H == 4104:
+            ar.attnres_set_variant(3, 0)
+        plan = ar.attnres_plan(M, N, H)
+        say("hybrid widths", M, N, H, plan)
+        assert plan[0] == 3 and (M < 352 or plan[1] == 2)
+        gp, gn = P.run_gpu(case)
+    finally:
+        ar.attnres_set_variant(0, 0)
+    rp, rn = P.run_oracle(orc, case)
+    P.assert_parity(gp, gn, rp, rn, "M=%d N=%d H=%d" % (M, N, H))
+
+
 # (M, H, N): kernel W's single-group form (rows of at most 256 vectors, up to
 # 131072 threads per call) on both sides of its bound, ragged short rows, and
 # the split bounds for rows of 257..895 vectors (1-wave chunks up to 32 / 48 /
