@@ -623,9 +623,10 @@ def test_bounded_waits_give_up(ar, orc):
 
 
 # (forced variant, case): kernel S's two exchanges (1 and 7 waves per chunk),
-# its Gram form, the automatic single-token call (14 one-wave chunks), and the
-# hybrid's split part
-EXCHANGE_CASES = [((2, 1), "cfg4"), ((2, 7), "cfg4"), ((2, 2), "cfg2"), ((0, 0), "cfg4b"), ((3, 0), "hybrid21")]
+# its Gram form, the automatic single-token call (14 one-wave chunks), the
+# hybrid's split part, and the two-wave form at 40 snapshots (both record pages)
+EXCHANGE_CASES = [((2, 1), "cfg4"), ((2, 7), "cfg4"), ((2, 2), "cfg2"), ((0, 0), "cfg4b"), ((3, 0), "hybrid21"),
+                  ((0, 0), "twowave40")]
 
 
 @pytest.mark.parametrize("mode", [1, 2], ids=["device-copies", "chunks-on-other-XCDs"])
@@ -640,6 +641,8 @@ def test_exchange_copies(ar, orc, mode):
     for variant, name in EXCHANGE_CASES:
         if name == "hybrid21":
             case = case_for(name, lambda: W.make_case(cfg=68, M=21, H=7176, N=12, add2=True))
+        elif name == "twowave40":
+            case = case_for(name, lambda: W.make_case(cfg=69, M=9, N=40, add2=True))
         else:
             case = case_for(name, lambda: W.config_case(name))
         ar.attnres_set_variant(*variant)
