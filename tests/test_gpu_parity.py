@@ -496,7 +496,8 @@ def test_exchange_forms_alternate(ar, orc, variant):
 
 
 @pytest.mark.parametrize("variant", SYNC_VARIANTS, ids=SYNC_VID, indirect=True)
-@pytest.mark.parametrize("N", [8, 4])  # the split kernel's two exchanges, and its Gram form's one
+# the split kernel's two exchanges, its Gram form's one, and its two-wave form (40 snapshots)
+@pytest.mark.parametrize("N", [8, 4, 40])
 def test_graph_replay(ar, variant, N):
     """Capture one call into a HIP graph; replay it with fresh inputs copied
     in between (eager work and synchronisation between replays); every replay
