@@ -1443,6 +1443,256 @@ __global__ __launch_bounds__(128, 1) void fwd_split_long(ParamsSplitLong pl)
 }
 
 // ---------------------------------------------------------------------------
+// Kernel S's four-wave form, also for 32..MAX_SPLIT_LONG_SNAP snapshots: four
+// waves per chunk of 128 vectors (two per lane, vectors c*128 + 64i + lane),
+// wave w holding sources 16w .. 16w + 15 (source N, the folded prefix, in
+// wave N / 16, which also runs A1), so rows of up to 16384 fit in
+// SPLIT_LONG_MAX_CHUNKS chunks.  The record layout is the two-wave form's
+// (value g in page g / 64, slot g % 64); each wave publishes and gathers
+// its 32 values, lanes l and l + 32 taking value l from alternate chunks, so
+// one round of polls covers 16 chunks.  The waves' largest logits and sums
+// meet in LDS (one barrier), waves 1..3 hand their mixtures to wave 0 (a
+// second), and wave 0 runs A5 and stores.  Wider calls take this form (it
+// halves the chunks per token and their polling), small ones the two-wave
+// form (its chunks hold half the work).
+constexpr int QUAD_SOURCES = 16;
+static_assert(4 * QUAD_SOURCES == LONG_TABLE && 2 * QUAD_SOURCES <= 32, "one gather round per wave");
+
+template <bool ADD2>
+__global__ __launch_bounds__(256, 1) void fwd_split_quad(ParamsSplitLong pl)
+{
+    const Params& p = pl.p;
+    __shared__ float zs[4][2];                  // per wave: largest logit, sum of exponentials below it
+    __shared__ __align__(16) float xs[3][16][64];  // waves 1..3's mixtures, element e of lane l at [e][l]
+
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int C = p.chunks;
+    const int ib = b >> 3;
+    const int chunk = ib - (ib / C) * C;
+    const int64_t rel = (int64_t)(ib / C) * 8 + ((b + p.xcd_skew * chunk) & 7);
+    const int64_t t = p.split_base + rel;
+    const int64_t slot = p.slot_base + rel;
+    if (t >= p.M)
+        return;
+
+    unsigned* state = p.state + (size_t)slot * STATE_STRIDE;
+    const unsigned epoch = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tag1 = 2u * epoch + 1u, tag2 = 2u * epoch + 2u;
+
+    const int ns = pl.n_snap;
+    const int nv = 2 * (ns + 1);
+    const int s0 = QUAD_SOURCES * wave;
+    const int nvec = p.nvec;
+    const int64_t row = t * (int64_t)nvec;
+    bool ok[2];
+    int vc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int v = chunk * 128 + j * 64 + lane;
+        ok[j] = v < nvec;
+        vc[j] = ok[j] ? v : nvec - 1;
+    }
+    uint4 k[QUAD_SOURCES][2];
+    {
+        const uint4* ptr[QUAD_SOURCES];
+#pragma unroll
+        for (int j = 0; j < QUAD_SOURCES; ++j)
+            ptr[j] = pl.snaps[s0 + j];
+#pragma unroll
+        for (int j = 0; j < QUAD_SOURCES; ++j) {
+            const bool real = s0 + j < ns;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint4 x = load_stream(real ? ptr[j] + row + vc[i] : p.query + vc[i]);
+                k[j][i] = real ? x : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    uint4 q[2], g[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    uint4 kp[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        q[i] = p.query[vc[i]];
+    unsigned long long* rec1 = p.rec1 + (size_t)slot * MAX_CHUNKS * REC1_CHUNK;
+    const bool pre = ns / QUAD_SOURCES == wave; // this wave holds the folded prefix (source N)
+    // every load of the wave in flight at once (as in the two-wave form), then
+    // gamma (wave 0) or the prefix and addends (the prefix's wave)
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            g[i] = p.gamma[vc[i]];
+    }
+    if (pre) {
+        uint4 a[2], bb[2], c[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            a[i] = load_stream(&p.prefix[row + vc[i]]);
+            bb[i] = load_stream(&p.add[row + vc[i]]);
+            c[i] = ADD2 ? load_stream(&p.add2[row + vc[i]]) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        fold_add<ADD2, 2>(a, bb, c, kp);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            if (ok[i])
+                store_stream(&p.out_prefix[row + chunk * 128 + i * 64 + lane], kp[i]);
+        const float2 pp = source_partial<2>(kp, q, ok);
+        const float part[2] = {pp.x, pp.y};
+        const float wt = wave_totals<2>(part, lane);
+        const int wv = bfly_index<2>(lane);
+        const int gv = 2 * ns + wv;
+        if (wv >= 0)
+            publish(&rec1[(chunk + LONG_PAGE * (gv >> 6)) * REC1_CHUNK + (gv & 63)], REC_STRIDE, tag1, wt);
+    }
+    {
+        float part[2 * QUAD_SOURCES];
+        source_partials<QUAD_SOURCES, 2>(k, q, ok, part);
+        fence_sources<QUAD_SOURCES, 2>(k);
+        const float wt = wave_totals<2 * QUAD_SOURCES>(part, lane);
+        const int wv = bfly_index<2 * QUAD_SOURCES>(lane);
+        const int gv = 2 * s0 + wv;
+        if (wv >= 0 && gv < 2 * ns)
+            publish(&rec1[(chunk + LONG_PAGE * (gv >> 6)) * REC1_CHUNK + (gv & 63)], REC_STRIDE, tag1, wt);
+    }
+
+    // A3: lanes l and l + 32 take value 32w + (l & 31) from alternate chunks;
+    // lane 2j then holds sum k_s^2 and lane 2j + 1 q.k_s, s = 16w + j
+    const int hh = lane >> 5, vv = lane & 31;
+    const int mygv = 2 * s0 + vv;
+    const bool want = mygv < nv;
+    const unsigned long long* src = rec1 + (size_t)LONG_PAGE * (mygv >> 6) * REC1_CHUNK + (mygv & 63);
+    const unsigned long long ready_zero = (unsigned long long)tag1 << 32;
+    float tv = 0.f;
+    for (int c0 = 0; c0 < C; c0 += 16) {
+        unsigned long long r0[8];
+        int off = p.l2_polls ? 0 : REC_STRIDE;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cj = c0 + hh + 2 * j;
+            r0[j] = cj < C && want ? peek(&src[cj * REC1_CHUNK + off]) : ready_zero;
+        }
+        for (unsigned polls = 0;; ++polls) {
+            bool ready = true;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                ready &= tag_of(r0[j]) == tag1;
+            if (ready)
+                break;
+            if (polls >= p.spin_limit) {
+                atomicAdd(p.timeouts, 1u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (tag_of(r0[j]) != tag1)
+                        r0[j] = gave_up(tag1);
+                break;
+            }
+            if (polls >= p.l2_polls)
+                off = REC_STRIDE;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int cj = c0 + hh + 2 * j;
+                if (cj < C && want && tag_of(r0[j]) != tag1)
+                    r0[j] = peek(&src[cj * REC1_CHUNK + off]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            tv += __uint_as_float((unsigned)r0[j]);
+    }
+    tv = tv + __shfl_xor(tv, 32);
+    const float qd = dpp<0xb1>(tv);
+    const bool srcl = (lane & 1) == 0 && lane < 32 && want;
+    const float z = srcl ? rsqrtf(tv * p.inv_h + p.eps) * qd : -INFINITY;
+    const float zm = wave_max(z);
+    const float e = srcl ? __expf(z - zm) : 0.f;
+    const float den = wave_sum(e);
+    if (lane == 0) {
+        zs[wave][0] = zm;
+        zs[wave][1] = den;
+    }
+    __syncthreads();
+    const float zmax = fmaxf(fmaxf(zs[0][0], zs[1][0]), fmaxf(zs[2][0], zs[3][0]));
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        total += zs[w][1] * __expf(zs[w][0] - zmax);
+    const float al = e * (__expf(zm - zmax) / total);
+    float alpha[QUAD_SOURCES];
+#pragma unroll
+    for (int i = 0; i < QUAD_SOURCES; ++i)
+        alpha[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * i));
+
+    float x[2][8];
+    combine<QUAD_SOURCES, 2>(k, alpha, ok, x);
+    if (pre) {
+        const float an = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 2 * (ns - s0)));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t A = word(kp[i], w);
+                x[i][2 * w] = __builtin_fmaf(an, lo_f32(A), x[i][2 * w]);
+                x[i][2 * w + 1] = __builtin_fmaf(an, hi_f32(A), x[i][2 * w + 1]);
+            }
+    }
+    if (wave != 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8)
+                xs[wave - 1][8 * i + e8][lane] = x[i][e8];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    float sx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float sxi = 0.f;
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+            x[i][e8] += xs[0][8 * i + e8][lane];
+            x[i][e8] += xs[1][8 * i + e8][lane];
+            x[i][e8] += xs[2][8 * i + e8][lane];
+            sxi = __builtin_fmaf(x[i][e8], x[i][e8], sxi);
+        }
+        sx += ok[i] ? sxi : 0.f;
+    }
+    sx = wave_sum(sx);
+
+    unsigned long long* rec2 = p.rec2 + (size_t)slot * REC2_SLOT;
+    if (lane == 0)
+        publish(&rec2[chunk], MAX_CHUNKS, tag2, sx);
+    int off = p.l2_polls ? 0 : MAX_CHUNKS;
+    unsigned long long w2 = lane < C ? peek(&rec2[off + lane]) : (unsigned long long)tag2 << 32;
+    for (unsigned polls = 0; tag_of(w2) != tag2; ++polls) {
+        if (polls >= p.spin_limit) {
+            atomicAdd(p.timeouts, 1u);
+            w2 = gave_up(tag2);
+            break;
+        }
+        if (polls >= p.l2_polls)
+            off = MAX_CHUNKS;
+        __builtin_amdgcn_s_sleep(1);
+        w2 = peek(&rec2[off + lane]);
+    }
+    const float ssum = wave_sum(__uint_as_float((unsigned)w2));
+    if (chunk == 0 && lane == 0)
+        advance_epoch(p, state, epoch, slot, RecordUse{C, 64, nv - 64, true});
+    const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (ok[i]) {
+            const int64_t at = row + chunk * 128 + i * 64 + lane;
+            store_stream(&p.out_norm[at], normalise(x[i], rstd, g[i]));
+            if (p.out_mix)
+                store_stream(&p.out_mix[at], pack_scaled(x[i], 1.0f));
+        }
+}
+
+// ---------------------------------------------------------------------------
 // The standalone bf16 addition (the unfused tail): 16-byte vectors, grid-stride,
 // plus a scalar tail of n % 8 elements.
 __global__ __launch_bounds__(256) void bf16_add_kernel(const uint4* a, const uint4* b, uint4* out,
@@ -1550,9 +1800,10 @@ const std::array<Kernel, MAX_SPLIT_SNAP + 1> kSpSmall[2] = {
 // split hidden, 4-8 waves per workgroup (up to 8 chunks), two workgroups per CU
 const std::array<Kernel, MAX_SNAP + 1> kSpLarge[2] = {split_table<false, 512, 8, 4>(Seq{}),
                                                       split_table<true, 512, 8, 4>(Seq{})};
-// split hidden, two-wave form (32..MAX_SPLIT_LONG_SNAP snapshots)
+// split hidden, two- and four-wave forms (32..MAX_SPLIT_LONG_SNAP snapshots)
 using KernelSplitLong = void (*)(ParamsSplitLong);
 const KernelSplitLong kSpLong[2] = {&fwd_split_long<false>, &fwd_split_long<true>};
+const KernelSplitLong kSpQuad[2] = {&fwd_split_quad<false>, &fwd_split_quad<true>};
 // the hybrid of the two
 const std::array<Kernel, MAX_SNAP + 1> kHybrid[2] = {hybrid_table<false>(Seq{}), hybrid_table<true>(Seq{})};
 
@@ -1803,7 +2054,8 @@ int launch_fwd(const void* prefix, const void* add, const void* add2, const void
             lp.snaps[s] = static_cast<const uint4*>(snapshots[s < n_snapshots ? s : n_snapshots - 1]);
         lp.n_snap = n_snapshots;
         void* largs[] = {&lp};
-        if (hipLaunchKernel(reinterpret_cast<const void*>(kSpLong[a2]), dim3((unsigned)pl.grid), dim3(pl.threads),
+        const KernelSplitLong fl = pl.threads == 256 ? kSpQuad[a2] : kSpLong[a2];
+        if (hipLaunchKernel(reinterpret_cast<const void*>(fl), dim3((unsigned)pl.grid), dim3(pl.threads),
                             largs, 0, stream) != hipSuccess)
             return ATTNRES_EHIP;
         return ATTNRES_OK;

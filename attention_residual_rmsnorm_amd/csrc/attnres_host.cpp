@@ -77,23 +77,38 @@ bool plan_split(int64_t M, int nvec, int waves, Plan& pl)
 // 1-wave 13.60 against 4-wave 15.64 us; M = 288: 2-wave 14.55 against 16.05;
 // M = 300 and 320: 4-wave 15.98 and 17.21 against 18.0 and 19.0 for 2-wave).
 // nw is a multiple of 8 so the chunks of a token keep one workgroup id mod 8.
-// The split kernel's two-wave form for 32..MAX_SPLIT_LONG_SNAP snapshots:
-// chunks of 64 vectors, two waves each (each holding half of the sources), at
-// most SPLIT_LONG_MAX_CHUNKS per token.
-bool plan_split_long(int64_t M, int nvec, Plan& pl)
+// The split kernel's forms for 32..MAX_SPLIT_LONG_SNAP snapshots, at most
+// SPLIT_LONG_MAX_CHUNKS chunks per token: waves = 2, chunks of 64 vectors
+// with two waves each (each holding half of the sources); waves = 4, chunks
+// of 128 vectors (two per lane) with four waves each (a quarter each).
+bool plan_split_long(int64_t M, int nvec, int waves, Plan& pl)
 {
-    const int chunks = (nvec + 63) / 64;
+    if (waves != 2 && waves != 4)
+        return false;
+    const int width = waves == 2 ? 64 : 128;
+    const int chunks = (nvec + width - 1) / width;
     if (chunks > SPLIT_LONG_MAX_CHUNKS || M > MAX_SPLIT_TOKENS)
         return false;
     pl = Plan{};
     pl.variant = 2;
-    pl.vpt = 1;
-    pl.threads = 128;
+    pl.vpt = waves == 2 ? 1 : 2;
+    pl.threads = 64 * waves;
     pl.chunks = chunks;
     pl.grid = 8 * (int64_t)chunks * ((M + 7) / 8);
-    pl.split_threads = 128;
+    pl.split_threads = pl.threads;
     pl.split_slots = M;
     return true;
+}
+
+// The form of 32..MAX_SPLIT_LONG_SNAP snapshots the automatic dispatch takes
+// for M tokens, or 0 for kernel W's batches.
+int split_long_waves(int64_t M, int n, int nvec)
+{
+    if (nvec < LONG_ROW_VECTORS)
+        return M <= SPLIT_LONG_TOKENS ? 2 : 0;
+    if (M > (n >= SPLIT_LONG_WIDE_SNAP ? SPLIT_LONG_TOKENS : SPLIT_LONG_TOKENS_LONG_ROWS))
+        return 0;
+    return nvec <= VERY_LONG_ROW_VECTORS && M <= SPLIT_LONG_PAIR_TOKENS ? 2 : 4;
 }
 
 bool plan_hybrid(int64_t M, int nvec, int waves, Plan& pl)
@@ -230,8 +245,12 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
         return plan_wg(M, nvec, force_param ? force_param : wg_vpt, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
     }
     if (force_variant == 2) {
-        if (split_long && force_param <= 1)
-            return plan_split_long(M, nvec, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+        if (split_long && (force_param <= 1 || force_param == 4)) {
+            int w = force_param == 4 ? 4 : force_param == 1 ? 2 : split_long_waves(M, n, nvec);
+            if (w == 0)
+                w = nvec <= VERY_LONG_ROW_VECTORS ? 2 : 4;
+            return plan_split_long(M, nvec, w, pl) ? ATTNRES_OK : ATTNRES_EINVAL;
+        }
         if (!split_ok || (many && force_param > 2))
             return ATTNRES_EINVAL;
         return plan_split(M, nvec, many && force_param == 0 ? 2 : force_param, pl) ? ATTNRES_OK
@@ -290,14 +309,17 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     // N = 31: 16.76 against 18.34 us for 1-wave; M = 16, N = 20: 8.74
     // against 9.66; H = 12288, M = 32, N = 31: 1-wave 11.65 against 13.00;
     // one token within 0.4 us either way).
-    // 32..63 snapshots (the split's two-wave form, rows of at most 8192): up
-    // to 96 tokens, but up to 64 on rows of 7168..8192 below 52 snapshots,
-    // else W's batches (H = 7168, M = 1, N = 32 / 63: 8.72 / 9.06 against
-    // 19.49 / 34.90 us; M = 64, N = 32: 16.86 against 19.91; M = 80, N = 32:
-    // W 19.93 against 22.32; M = 96, N = 52: 29.41 against 30.55, N = 44: W
-    // 26.52 against 28.00; H = 8192, M = 64, N = 32: 20.68 against 20.88;
-    // H = 3584, M = 96, N = 63: 16.76 against 28.14; H = 896, M = 96, N =
-    // 32: 8.73 against 12.76).
+    // 32..63 snapshots (split_long_waves): rows of 7168 and more take the
+    // split's two-wave form up to 16 tokens (rows of at most 8192) and its
+    // four-wave form beyond, up to 64 tokens and up to 96 from 40 snapshots
+    // on, else W's batches; shorter rows the two-wave form up to 96 (H =
+    // 7168, M = 1, N = 32 / 63: 8.72 / 9.06 against 19.49 / 34.90 us for W
+    // and 9.26 / 9.43 in four waves; M = 24, N = 32: four-wave 10.80 against
+    // 13.53 two-wave and 19.49 W; M = 96, N = 40: 23.57 against W's 24.36,
+    // N = 32: W 20.39 against 22.69; H = 16384, M = 1, N = 63: 9.67 against
+    // W's 61.28; M = 64, N = 32: 28.85 against 35.75; M = 96, N = 32: W
+    // 37.67 against 40.94; H = 896: two-wave 7.9..9.4 against four-wave
+    // 8.6..9.8 up to 96 tokens).
     // Shorter rows (H = 896 ... 4096, N <= 12): a token's rows fit in flight
     // on one CU, and the exchange of a split costs more than it spreads.
     //  * H <= 2048: one workgroup per token everywhere (H = 896, N = 12: 3.88
@@ -312,8 +334,8 @@ int make_plan(int64_t M, int n, int64_t H, int force_variant, int force_param, P
     //    4.09).
     const bool long_rows = nvec >= LONG_ROW_VECTORS;
     if (split_long) {
-        const int most = !long_rows || n >= SPLIT_LONG_WIDE_SNAP ? SPLIT_LONG_TOKENS : SPLIT_LONG_TOKENS_LONG_ROWS;
-        if (M <= most && plan_split_long(M, nvec, pl))
+        const int w = split_long_waves(M, n, nvec);
+        if (w && plan_split_long(M, nvec, w, pl))
             return ATTNRES_OK;
     } else if (many) {
         const bool mid_m = M > SPLIT_SMALL_TOKENS && M <= SPLIT_SMALL_TOKENS_WIDE; // 17..32

@@ -14,19 +14,23 @@ constexpr int MAX_SPLIT_SNAP = 31;       // split hidden, 1-2 waves per workgrou
 constexpr int MAX_HIDDEN = 16384;        // == ATTNRES_MAX_HIDDEN
 constexpr int MAX_SPLIT_TOKENS = 512;    // token slots of the split-hidden scratch
 constexpr int MAX_CHUNKS = 32;           // workgroups per token in the split-hidden kernel
-// The split kernel's two-wave form (32..MAX_SPLIT_LONG_SNAP snapshots):
-// chunks of 64 vectors with two waves each, wave w holding sources 32w ..
-// 32w + 31, at most SPLIT_LONG_MAX_CHUNKS chunks per token (rows of up to
-// 8192), so that each chunk's 2 (N + 1) first-exchange values fit in two
-// pages of 64 records (its own chunk index and that index +
-// SPLIT_LONG_MAX_CHUNKS); automatic up to SPLIT_LONG_TOKENS tokens, except
-// up to SPLIT_LONG_TOKENS_LONG_ROWS for rows of LONG_ROW_VECTORS and more
-// with fewer than SPLIT_LONG_WIDE_SNAP snapshots.
+// The split kernel's two- and four-wave forms (32..MAX_SPLIT_LONG_SNAP
+// snapshots): chunks of 64 vectors with two waves each (wave w holding
+// sources 32w .. 32w + 31) or of 128 vectors with four (16 sources each), at
+// most SPLIT_LONG_MAX_CHUNKS chunks per token, so that each chunk's 2 (N + 1)
+// first-exchange values fit in two pages of 64 records (its own chunk index
+// and that index + SPLIT_LONG_MAX_CHUNKS).  Automatic (split_long_waves):
+// rows shorter than LONG_ROW_VECTORS the two-wave form up to
+// SPLIT_LONG_TOKENS tokens; longer rows the two-wave form up to
+// SPLIT_LONG_PAIR_TOKENS tokens (rows of at most VERY_LONG_ROW_VECTORS) and
+// the four-wave form beyond, up to SPLIT_LONG_TOKENS_LONG_ROWS tokens, or up
+// to SPLIT_LONG_TOKENS from SPLIT_LONG_WIDE_SNAP snapshots on.
 constexpr int MAX_SPLIT_LONG_SNAP = 63;
 constexpr int SPLIT_LONG_MAX_CHUNKS = MAX_CHUNKS / 2;
 constexpr int SPLIT_LONG_TOKENS = 96;
 constexpr int SPLIT_LONG_TOKENS_LONG_ROWS = 64;
-constexpr int SPLIT_LONG_WIDE_SNAP = 52;
+constexpr int SPLIT_LONG_WIDE_SNAP = 40;
+constexpr int SPLIT_LONG_PAIR_TOKENS = 16;
 // automatic dispatch (see make_plan) at H >= 7168, one pass of sources:
 // N >= GRAM_MAX_SOURCES (two exchanges): 1-wave split chunks up to
 // SPLIT_ONE_WAVE_TOKENS tokens, and up to SPLIT_MID_TOKENS with at most

@@ -79,8 +79,8 @@ extern "C" {
                                     running softmax over batches of 12 snapshots; the
                                     split-hidden kernel, used for a few tokens, holds
                                     up to 31 at once in one wave per chunk and up to 63
-                                    in two), so the page's N > 12 fallback is not
-                                    needed below 65 */
+                                    in two or four), so the page's N > 12 fallback is
+                                    not needed below 65 */
 #define ATTNRES_MAX_HIDDEN 16384
 #define ATTNRES_NOALLOC_MAX_SPLIT_TOKENS 96 /* token slots of the no-allocation scratch */
 

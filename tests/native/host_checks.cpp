@@ -86,8 +86,11 @@ int main()
                                 if (n > MAX_SNAP)
                                     EXPECT((pl.variant == 1 && (pl.vpt == 2 || pl.vpt == 4)) ||
                                            (pl.variant == 2 && n <= MAX_SPLIT_SNAP && pl.threads <= 128) ||
-                                           (pl.variant == 2 && n <= MAX_SPLIT_LONG_SNAP && pl.threads == 128 &&
-                                            pl.chunks <= SPLIT_LONG_MAX_CHUNKS));
+                                           (pl.variant == 2 && n > MAX_SPLIT_SNAP && n <= MAX_SPLIT_LONG_SNAP &&
+                                            ((pl.threads == 128 && pl.vpt == 1) ||
+                                             (pl.threads == 256 && pl.vpt == 2)) &&
+                                            pl.chunks <= SPLIT_LONG_MAX_CHUNKS &&
+                                            (int64_t)pl.chunks * (pl.threads / 2) * 8 >= h));
                                 // the single-group table is built for at most SHORT_WG_THREADS
                                 if (pl.single_group)
                                     EXPECT(pl.variant == 1 && pl.vpt == 1 && pl.threads <= SHORT_WG_THREADS &&
@@ -97,7 +100,8 @@ int main()
                                            pl.grid == 8 * pl.chunks * ((m + 7) / 8) &&
                                            pl.threads <= 512 && pl.split_slots == m &&
                                            pl.split_threads == pl.threads &&
-                                           pl.chunks <= (pl.threads <= 128 ? MAX_CHUNKS : 8));
+                                           pl.chunks <= (n > MAX_SPLIT_SNAP ? SPLIT_LONG_MAX_CHUNKS
+                                                         : pl.threads <= 128 ? MAX_CHUNKS : 8));
                                 // the hybrid: W on [0, split_base), one workgroup per token, 1-, 2- or
                                 // 4-wave chunks on the rest (one pass of sources), chunks of a token on
                                 // one workgroup id mod 8

@@ -234,12 +234,16 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(96, 31, 7168) == (2, 7, 128)
     assert ar.attnres_plan(97, 13, 7168) == (1, 1, 448)
     assert ar.attnres_plan(1, 32, 7168) == (2, 14, 128)    # 32..63 snapshots: the split's two-wave
-    assert ar.attnres_plan(64, 51, 7168) == (2, 14, 128)   # form up to 64 tokens on long rows,
-    assert ar.attnres_plan(65, 51, 8192) == (1, 1, 512)
-    assert ar.attnres_plan(65, 52, 7168) == (2, 14, 128)   # up to 96 from 52 snapshots on,
-    assert ar.attnres_plan(96, 63, 7168) == (2, 14, 128)
-    assert ar.attnres_plan(96, 32, 896) == (2, 2, 128)     # and on shorter rows;
-    assert ar.attnres_plan(1, 40, 8192) == (2, 16, 128)    # at most 16 chunks per token
+    assert ar.attnres_plan(16, 63, 8192) == (2, 16, 128)   # form up to 16 tokens,
+    assert ar.attnres_plan(17, 32, 7168) == (2, 7, 256)    # its four-wave form beyond,
+    assert ar.attnres_plan(64, 39, 7168) == (2, 7, 256)    # up to 64 tokens,
+    assert ar.attnres_plan(65, 39, 7168) == (1, 1, 448)
+    assert ar.attnres_plan(65, 40, 8192) == (2, 8, 256)    # up to 96 from 40 snapshots on;
+    assert ar.attnres_plan(96, 63, 7168) == (2, 7, 256)
+    assert ar.attnres_plan(1, 40, 16384) == (2, 16, 256)   # rows past 8192: four waves at every M
+    assert ar.attnres_plan(96, 40, 12288) == (2, 12, 256)
+    assert ar.attnres_plan(65, 39, 16384) == (1, 1, 512)
+    assert ar.attnres_plan(96, 32, 896) == (2, 2, 128)     # shorter rows: two waves up to 96
     assert ar.attnres_plan(5, 36, 1000) == (2, 2, 128)
     assert ar.attnres_plan(97, 52, 7168) == (1, 1, 448)    # then W's batches,
     assert ar.attnres_plan(1, 64, 7168) == (1, 1, 448)     # and W alone at 64 snapshots
@@ -247,7 +251,7 @@ def test_plan_is_pure_and_sane():
     assert ar.attnres_plan(96, 31, 896) == (2, 2, 64)
     assert ar.attnres_plan(97, 13, 896)[0] == 1
     assert ar.attnres_plan(256, 64, 7168) == (1, 1, 448)
-    assert ar.attnres_plan(3, 40, 16384) == (1, 1, 512)
+    assert ar.attnres_plan(3, 40, 16384) == (2, 16, 256)
     # rows longer than 8192, one pass: the split at every N up to 96 tokens
     assert ar.attnres_plan(1, 0, 16384) == (2, 16, 128)    # 2-wave chunks up to 16 tokens,
     assert ar.attnres_plan(16, 12, 12288) == (2, 12, 128)
@@ -303,7 +307,7 @@ def test_set_variant_validation():
         ar.attnres_set_variant(2, 1)
         assert ar.attnres_plan(3, 4, 7168) == (2, 14, 64)
         assert ar.attnres_plan(200, 63, 7168) == (2, 14, 128)  # the two-wave form, forced past 96 tokens
-        with pytest.raises(ar.AttnResError):  # more than 16 chunks per token
+        with pytest.raises(ar.AttnResError):  # more than 16 chunks of 64 vectors per token
             ar.attnres_plan(1, 40, 16384)
         with pytest.raises(ar.AttnResError):  # two record pages hold at most 63 snapshots
             ar.attnres_plan(1, 64, 7168)
@@ -313,11 +317,13 @@ def test_set_variant_validation():
             ar.attnres_plan(1, 13, 7168)
         ar.attnres_set_variant(2, 2)
         assert ar.attnres_plan(1, 31, 7168) == (2, 7, 128)
-        with pytest.raises(ar.AttnResError):  # 32..63: only the two-wave form
+        with pytest.raises(ar.AttnResError):  # 32..63: only the two- and four-wave forms
             ar.attnres_plan(1, 32, 7168)
         ar.attnres_set_variant(2, 4)
         with pytest.raises(ar.AttnResError):  # more than 12 only in the 1-2-wave family
             ar.attnres_plan(1, 13, 7168)
+        assert ar.attnres_plan(1, 32, 7168) == (2, 7, 256)  # 32..63: the four-wave form
+        assert ar.attnres_plan(1, 40, 16384) == (2, 16, 256)
         ar.attnres_set_variant(3, 0)
         assert ar.attnres_plan(20, 12, 7168) == (3, 14, 448)  # the hybrid, forced at a small M
         with pytest.raises(ar.AttnResError):  # its split part: one pass of sources

@@ -110,7 +110,7 @@ def check(ar, orc, case, what):
 KERNELS = [((1, 0), 4, "W"), ((1, 0), 12, "W"), ((1, 0), 20, "W batched"), ((1, 4), 12, "W 4 vectors"),
            ((2, 1), 12, "S1w"), ((2, 2), 12, "S2w"), ((2, 7), 12, "S7w"), ((2, 2), 4, "S2w Gram"),
            ((2, 1), 5, "S1w Gram"), ((2, 7), 4, "S7w Gram"), ((3, 0), 12, "hybrid"), ((3, 0), 4, "hybrid Gram"), ((2, 1), 8, "S1w N=8"),
-           ((3, 4), 12, "hybrid 4w"), ((2, 1), 40, "S two-wave"),
+           ((3, 4), 12, "hybrid 4w"), ((2, 1), 40, "S two-wave"), ((2, 4), 40, "S four-wave"),
            ((0, 0), 1, "auto")]
 
 

@@ -84,14 +84,16 @@ def test_many_sources_dispatch_bounds(ar, orc, M, N, H):
     P.assert_parity(gp, gn, rp, rn, "M=%d H=%d N=%d" % (M, H, N))
 
 
-@pytest.mark.parametrize("H", [7168, 8192, 896])
-@pytest.mark.parametrize("N", [32, 51, 52, 63])
-@pytest.mark.parametrize("M", [1, 8, 9, 64, 65, 96, 97])
+@pytest.mark.parametrize("H", [7168, 8192, 896, 16384])
+@pytest.mark.parametrize("N", [32, 39, 40, 63])
+@pytest.mark.parametrize("M", [1, 16, 17, 64, 65, 96, 97])
 def test_split_long_dispatch_bounds(ar, orc, M, N, H):
     """The automatic dispatch from 32 to 63 snapshots on both sides of its
-    bounds (the split kernel's two-wave form up to 96 tokens, up to 64 on
-    rows of 7168..8192 below 52 snapshots; then kernel W's batches), with
-    the pre-norm mixture output."""
+    bounds (rows of 7168 and more: the split kernel's two-wave form up to 16
+    tokens where rows are at most 8192, its four-wave form beyond, up to 64
+    tokens below 40 snapshots and 96 from 40 on; shorter rows the two-wave
+    form up to 96; then kernel W's batches), with the pre-norm mixture
+    output."""
     case = W.make_case(cfg=87, M=M, H=H, N=N, add2=(M % 2 == 0))
     say("two-wave split, auto", M, H, N, ar.attnres_plan(M, N, case.H))
     gp, gn, gm = P.run_gpu_mix(case)

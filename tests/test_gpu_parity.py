@@ -625,9 +625,10 @@ def test_bounded_waits_give_up(ar, orc):
 
 # (forced variant, case): kernel S's two exchanges (1 and 7 waves per chunk),
 # its Gram form, the automatic single-token call (14 one-wave chunks), the
-# hybrid's split part, and the two-wave form at 40 snapshots (both record pages)
+# hybrid's split part, and the two- and four-wave forms at 40 snapshots (both
+# record pages)
 EXCHANGE_CASES = [((2, 1), "cfg4"), ((2, 7), "cfg4"), ((2, 2), "cfg2"), ((0, 0), "cfg4b"), ((3, 0), "hybrid21"),
-                  ((0, 0), "twowave40")]
+                  ((0, 0), "twowave40"), ((2, 4), "twowave40")]
 
 
 @pytest.mark.parametrize("mode", [1, 2], ids=["device-copies", "chunks-on-other-XCDs"])
@@ -734,13 +735,15 @@ def test_epoch_wrap_value_slots(ar, orc):
         ar.attnres_debug_reset_scratch()
 
 
-def test_epoch_wrap_two_wave(ar, orc):
-    """The same across the wrap for the split kernel's two-wave form (32..63
-    snapshots), whose second record page sits at chunk indices 16..29: a
-    two-wave call at epoch 5 leaves records there, one-wave 14-chunk calls
-    run across the wrap (the wrapping call clears indices 14..31), and a
-    two-wave call on other inputs at epoch 5 again expects the tags the old
-    page-1 records carry, and must still be exact."""
+@pytest.mark.parametrize("variant,shape", [((0, 0), (2, 14, 128)), ((2, 4), (2, 7, 256))],
+                         ids=["two-wave", "four-wave"])
+def test_epoch_wrap_two_wave(ar, orc, variant, shape):
+    """The same across the wrap for the split kernel's two- and four-wave
+    forms (32..63 snapshots), whose second record page sits at chunk indices
+    16 and on: such a call at epoch 5 leaves records there, one-wave 14-chunk
+    calls run across the wrap (the wrapping call clears indices 14..31), and
+    a call of the same form on other inputs at epoch 5 again expects the tags
+    the old page-1 records carry, and must still be exact."""
     a = case_for(("wrap2", 0), lambda: W.make_case(cfg=82, M=8, N=40, add2=True))
     b = case_for(("wrap2", 1), lambda: W.make_case(cfg=83, M=8, N=40, add2=False))
     c = case_for(("wrap2", 2), lambda: W.make_case(cfg=84, M=8, N=8, add2=True))
@@ -748,7 +751,8 @@ def test_epoch_wrap_two_wave(ar, orc):
     try:
         ar.attnres_debug_reset_scratch()
         ar.attnres_debug_set_slot_rotation(False)  # every call on token slots 0..7
-        assert ar.attnres_plan(8, 40, 7168) == (2, 14, 128)
+        ar.attnres_set_variant(*variant)
+        assert ar.attnres_plan(8, 40, 7168) == shape
         ar.attnres_debug_set_epoch(5)
         P.assert_parity(*P.run_gpu(a), *ra, "two-wave call at epoch 5")
         ar.attnres_set_variant(2, 1)
@@ -757,7 +761,7 @@ def test_epoch_wrap_two_wave(ar, orc):
         for i in range(4):  # epochs 2^31 - 3 .. 2^31 - 2, then 0 and 1
             say("wrap: one-wave call", i)
             P.assert_parity(*P.run_gpu(c), *rc, "14 one-wave chunks, call %d across the wrap" % i)
-        ar.attnres_set_variant(0, 0)
+        ar.attnres_set_variant(*variant)
         ar.attnres_debug_set_epoch(5)
         P.assert_parity(*P.run_gpu(b), *rb, "two-wave call at epoch 5 after the wrap")
         assert ar.attnres_debug_timeouts() == 0
