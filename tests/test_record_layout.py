@@ -8,7 +8,10 @@ their device-scope copies at 64..127).  A call with C chunks writes and reads:
   0 .. NV - 1 (NV = 2(N + 1), or N + 1 + (N + 1)(N + 2) / 2 in the Gram form);
 * the two-wave form (32..63 snapshots, C <= 16): wave 0 area c, values
   0..63; wave 1 area c + 16, values 0 .. 2N - 63 (its snapshots, then the
-  folded prefix's two values).
+  folded prefix's two values);
+* the four-wave form (the same values, four writers per chunk): wave w
+  values 32w .. 32w + 31, the prefix's wave also 2N and 2N + 1, so the same
+  records as the two-wave form.
 
 Checked for every chunk count and source count each form takes: every
 record a reader polls is written by exactly one chunk of the call (its own
@@ -56,6 +59,27 @@ def two_wave_form(n, C):
     return writes, reads, (C, 64, nv - 64)
 
 
+def four_wave_form(n, C):
+    """Wave w of chunk c publishes value 32w + l of its snapshots (lane l's
+    butterfly total) when below 2N, the prefix's wave (N // 16) values 2N and
+    2N + 1; value g sits in area c + 16 (g // 64), slot g % 64; wave w gathers
+    values 32w .. 32w + 31 below 2(N + 1)."""
+    nv = 2 * (n + 1)
+    writes = {}
+    for c in range(C):
+        for wave in range(4):
+            vals = [32 * wave + l for l in range(32) if 32 * wave + l < 2 * n]
+            if wave == n // 16:
+                vals += [2 * n, 2 * n + 1]
+            for g in vals:
+                key = (c + PAGE * (g // 64), g % 64)
+                assert key not in writes
+                writes[key] = c
+    reads = {(c + PAGE * (g // 64), g % 64) for wave in range(4) for g in range(32 * wave, 32 * wave + 32)
+             if g < nv for c in range(C)}
+    return writes, reads, (C, 64, nv - 64)
+
+
 def cleared(use):
     C, nv0, nv1 = use
     out = set()
@@ -89,6 +113,15 @@ def test_one_wave_forms(n, C):
 @pytest.mark.parametrize("n", range(32, 64))
 def test_two_wave_form(n, C):
     check(*two_wave_form(n, C))
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 8, 12, 16])
+@pytest.mark.parametrize("n", range(32, 64))
+def test_four_wave_form(n, C):
+    w2, r2, u2 = two_wave_form(n, C)
+    w4, r4, u4 = four_wave_form(n, C)
+    assert set(w4) == set(w2) and r4 == r2 and u4 == u2, "the two forms share one record layout"
+    check(w4, r4, u4)
 
 
 def test_two_wave_form_stops_at_63():
