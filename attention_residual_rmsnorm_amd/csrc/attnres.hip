@@ -1433,7 +1433,7 @@ __global__ __launch_bounds__(128, 1) void fwd_split_long(ParamsSplitLong pl)
     }
     const float ssum = wave_sum(__uint_as_float((unsigned)w2));
     if (chunk == 0 && lane == 0) // every chunk has published its second record: all have read the epoch
-        advance_epoch(p, state, epoch, slot, RecordUse{C, 64, nv - 64, true});
+        advance_epoch(p, state, epoch, slot, RecordUse{C, nv < 64 ? nv : 64, nv > 64 ? nv - 64 : 0, true});
     const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
     if (ok[0]) {
         store_stream(&p.out_norm[row + v], normalise(x[0], rstd, g));
@@ -1680,7 +1680,7 @@ __global__ __launch_bounds__(256, 1) void fwd_split_quad(ParamsSplitLong pl)
     }
     const float ssum = wave_sum(__uint_as_float((unsigned)w2));
     if (chunk == 0 && lane == 0)
-        advance_epoch(p, state, epoch, slot, RecordUse{C, 64, nv - 64, true});
+        advance_epoch(p, state, epoch, slot, RecordUse{C, nv < 64 ? nv : 64, nv > 64 ? nv - 64 : 0, true});
     const float rstd = rsqrtf(ssum * p.inv_h + p.eps);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
