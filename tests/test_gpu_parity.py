@@ -705,6 +705,44 @@ def test_epoch_wrap(ar, orc):
         ar.attnres_debug_reset_scratch()
 
 
+def test_bounded_waits_give_up_four_wave(ar, orc):
+    """The same for the split kernel's four-wave form (40 snapshots, both
+    record pages): with the spin limit forced down to one re-poll, every
+    call finishes, the give-ups are counted, out_prefix stays exact and every
+    out_norm element is exact or NaN; after a reset, exact again."""
+    import torch
+
+    case = W.make_case(cfg=88, M=3, N=40, add2=True)
+    rp, rn = P.run_oracle(orc, case)
+    forced = 0
+    ar.attnres_set_variant(2, 4)
+    try:
+        assert ar.attnres_plan(case.M, case.N, case.H) == (2, 7, 256)
+        for rep in range(4):
+            ar.attnres_debug_reset_scratch()
+            ar.attnres_debug_set_spin_limit(1)
+            try:
+                gp, gn = P.run_gpu(case)
+                torch.cuda.synchronize()
+            finally:
+                ar.attnres_debug_set_spin_limit(0)
+            forced += ar.attnres_debug_timeouts()
+            assert np.array_equal(gp, rp), "out_prefix depends on no exchange"
+            nan = P.is_nan16(gn)
+            bad = P.norm_mismatches(gn, rn) & ~nan
+            assert not bad.any(), "call %d: %d elements neither exact nor NaN" % (rep, int(bad.sum()))
+        ar.attnres_debug_reset_scratch()
+        assert forced > 0
+        assert ar.attnres_debug_timeouts() == 0
+        gp, gn = P.run_gpu(case)
+        P.assert_parity(gp, gn, rp, rn, "after the reset")
+        assert ar.attnres_debug_timeouts() == 0
+    finally:
+        ar.attnres_debug_set_spin_limit(0)
+        ar.attnres_debug_reset_scratch()
+        ar.attnres_set_variant(0, 0)
+
+
 def test_epoch_wrap_value_slots(ar, orc):
     """Across the wrap with the same chunk count but fewer first-exchange
     values: a 31-snapshot call at epoch 5 fills all 64 value slots of chunk
