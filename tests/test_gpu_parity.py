@@ -812,20 +812,20 @@ def test_epoch_wrap_two_wave(ar, orc, variant, shape):
 def test_concurrent_streams(ar, orc):
     """Split-kernel calls enqueued on two streams with no ordering between
     them (two exchanges and the Gram form's one, 1- and 2-wave chunks, the
-    hybrid launch's 1- and 2-wave chunks, and the two-wave form's two record
-    pages at 40 snapshots): each call takes its own token
+    hybrid launch's 1- and 2-wave chunks, and the two- and four-wave forms'
+    two record pages at 40 snapshots): each call takes its own token
     slots of the scratch, so calls that run at the same time do not share
     records.  Every output against the oracle, and no wait given up."""
     import torch
 
     cases = [W.make_case(cfg=90 + i, M=32, N=(12, 4, 8)[i % 3], add2=True) for i in range(6)]
     cases += [W.make_case(cfg=96, M=264, N=12, add2=True), W.make_case(cfg=97, M=288, N=4, add2=True),
-              W.make_case(cfg=98, M=16, N=40, add2=True)]
+              W.make_case(cfg=98, M=16, N=40, add2=True), W.make_case(cfg=99, M=4, H=16384, N=40, add2=True)]
     refs = [P.run_oracle(orc, c) for c in cases]
     d = P.dev
     ins = [(d(c.prefix), d(c.add), d(c.add2), [d(s) for s in c.snapshots], d(c.query), d(c.gamma)) for c in cases]
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    ar.attnres_debug_reset_scratch()  # slots from 0: the 18 calls take 496 of the 512
+    ar.attnres_debug_reset_scratch()  # slots from 0: the 20 calls take 504 of the 512
     outs = []
     for rep in range(2):
         for i, c in enumerate(cases):
