@@ -236,7 +236,9 @@ int attnres_plan(int64_t M, int n_snapshots, int64_t H, int* variant, int* chunk
  * attnres_set_variant -- process-wide dispatch override for tests and
  * benchmarks: variant 0 = automatic (param 0); 1 = workgroup per token, param =
  * 16-byte vectors per thread (0 automatic, or 1, 2, 4); 2 = split hidden, param
- * = waves per workgroup (0 automatic, or 1, 2, 4..8); 3 = hybrid, param =
+ * = waves per workgroup (0 automatic, or 1, 2, 4..8; with 32..63 snapshots only 0,
+ * 1 for the two-wave form on 64-vector chunks, or 4 for the four-wave form on
+ * 128-vector chunks); 3 = hybrid, param =
  * waves per split chunk (0 automatic, or 1, 2, 4, or 8 for half rows, the
  * workgroup-per-token width; rows of 4104..8192 elements, at most 12
  * snapshots; below 257 tokens the workgroup-per-token part takes about half
